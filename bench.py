@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MXFP4 MoE FFN hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+resident in HBM: per-32 int8 activation quantisation, top-k routing + expert
+grouping, gate/up projection + SwiGLU + requant, down projection, weighted
+combine.  Layer weight sets are rotated per step so the MALL (256 MB) cannot
+hold them.  Prints one JSON line.
+
+Workloads (--workload):
+  decode        DS-V4 layer (256 experts, top-6 + shared, D 4096, F 2048),
+                1 token per step, 8 layer sets (27.5 GB)            [default]
+  decode-batch  same layer, --rows 2/4/8/16 tokens per step (--hot: +2.0 logit
+                bias on 16 experts)
+  prefill       same layer, --rows 512 or 4096 tokens per step, 2 layer sets
+  matvec        MXFP4 matvec 14336x4096, --rows K resident rows, 16 copies
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-FFN tokens/s + achieved HBM GB/s (decode 1-16 rows), TFLOP/s (prefill)"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+I8_MFMA_PEAK_TOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "decode-batch", "prefill", "matvec"])
+    ap.add_argument("--rows", type=int, default=None)
+    ap.add_argument("--hot", action="store_true")
+    ap.add_argument("--sets", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None)
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the routed-expert path here has no "
+              "multi-GPU execution (no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_routed_expert_e2m1_amd as m
+    import synth
+
+    m.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    wl = args.workload
+    if wl == "matvec":
+        return bench_matvec(args, m, synth, np, torch, dev)
+
+    L = synth.DSV4_LAYER
+    if wl == "decode":
+        T, seed, sets = 1, synth.DECODE["seed"], 8
+    elif wl == "decode-batch":
+        T, seed, sets = (args.rows or 16), synth.DECODE_BATCH["seed"], 8
+    else:
+        T, seed, sets = (args.rows or 4096), synth.PREFILL["seed"], 2
+    sets = args.sets or sets
+    prefill = wl == "prefill"
+    steps = args.steps or (200 if prefill else 1000)
+    warmup = args.warmup if args.warmup is not None else (20 if prefill else 50)
+    n_inputs = 4 if prefill else 16
+    hot = 2.0 if args.hot else 0.0
+
+    t0 = time.time()
+    layers = []
+    for s in range(sets):
+        fn = lambda e, s=s: synth.expert_weights(seed, s, e, L.d_model, L.d_ff, device=dev)
+        layers.append(m.pack_layer(L.d_model, L.d_ff, L.n_experts, L.top_k, fn, True, dev))
+    torch.cuda.synchronize()
+    print(f"[bench] packed {sets} layer sets in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+
+    xs = [torch.from_numpy(synth.activations(seed, i, T, L.d_model)).to(dev)
+          for i in range(n_inputs)]
+    lgs = [torch.from_numpy(synth.router_logits(seed, i, T, L.n_experts, hot_bias=hot)).to(dev)
+           for i in range(n_inputs)]
+    q = torch.empty((T, L.d_model), dtype=torch.int8, device=dev)
+    qs = torch.empty((T, L.d_model // 32), dtype=torch.float32, device=dev)
+    route_out = (torch.empty((T, L.top_k), dtype=torch.int32, device=dev),
+                 torch.empty((T, L.top_k), dtype=torch.float32, device=dev),
+                 torch.empty(L.n_experts, dtype=torch.int32, device=dev),
+                 torch.empty(L.n_experts + 1, dtype=torch.int32, device=dev),
+                 torch.empty(T * L.top_k, dtype=torch.int32, device=dev))
+    y = torch.empty((T, L.d_model), dtype=torch.float32, device=dev)
+    ws = torch.empty(m.moe_ffn_workspace_bytes(layers[0], T), dtype=torch.uint8, device=dev)
+    ffn = m.moe_ffn_prefill if prefill else m.moe_ffn_decode
+
+    def step(i):
+        m.moe_quant_act_q8(xs[i % n_inputs], q=q, scales=qs)
+        ids, w, counts, offsets, srt = m.moe_route_group(lgs[i % n_inputs], L.top_k,
+                                                         out=route_out)
+        ffn(layers[i % sets], q, qs, ids, w, offsets, srt, y=y, ws=ws)
+
+    # touched experts per input (bytes are counted from the actual routes)
+    touched = []
+    for i in range(n_inputs):
+        m.moe_route_group(lgs[i], L.top_k, out=route_out)
+        counts = route_out[2].cpu().numpy()
+        touched.append(int(np.count_nonzero(counts)) + 1)  # + shared expert
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / steps
+    tok_s = T * steps / (ms_total / 1e3)
+
+    gu_bytes = 2 * L.d_ff * L.d_model // 2 + 2 * L.d_ff * L.d_model // 32
+    dn_bytes = L.d_model * L.d_ff // 2 + L.d_model * L.d_ff // 32
+    A = T * L.top_k + T
+    act_bytes = T * (L.d_model * 4 + L.d_model + L.d_model // 8)  # x read, q + scales written
+    mean_touched = float(np.mean([touched[i % n_inputs] for i in range(steps)]))
+    step_bytes = mean_touched * (gu_bytes + dn_bytes) + act_bytes + T * L.d_model * 4
+
+    # dominant kernel: the gate/up stage, timed alone over the rotated sets
+    n_k = max(50, min(steps, 400))
+    for i in range(n_inputs):  # make every workspace valid for the stage-only runs
+        step(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(n_k):
+        ids, w, counts, offsets, srt = route_out
+        m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP, q, qs, ids, w,
+                         offsets, srt, y, ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    k_us = ev0.elapsed_time(ev1) * 1e3 / n_k
+    # routes in route_out now belong to the last input evaluated
+    last_touched = touched[(n_inputs - 1) % n_inputs]
+    hidden_bytes = A * (L.d_ff + L.d_ff // 32 * 4)
+    k_bytes = last_touched * gu_bytes + T * (L.d_model + L.d_model // 8) + hidden_bytes
+    if prefill:
+        k_flops = 2.0 * A * (2 * L.d_ff) * L.d_model
+        achieved = k_flops / (k_us * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                    traffic=None, kernel="proj_kernel<gate/up>", avg_us=round(k_us, 3),
+                    i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
+                    hbm_gbs=round(k_bytes / (k_us * 1e-6) / 1e9, 1))
+    else:
+        achieved = k_bytes / (k_us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="proj_kernel<gate/up>", avg_us=round(k_us, 3),
+                    bytes_per_launch=int(k_bytes))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill)
+
+    line = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4(e2m1+e8m0) x int8 -> exact block dots, f32 accumulate",
+        "data": "synthetic (seeded counter-hash weights, N(0,1) activations/logits)",
+        "config": {"workload": f"{wl}: E256 top-6 + shared, d_model 4096, d_ff 2048, "
+                               f"{T} token(s)/step, {sets} rotated layer sets"
+                               + (", hot-16 +2.0 bias" if hot else ""),
+                   "rows": T, "layer_sets": sets, "seed": seed},
+        "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_bytes": int(step_bytes),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    emit(line, args)
+
+
+def cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+
+    S = args.cpu_sample or (8 if prefill else 32)
+    threads = min(16, len(os.sched_getaffinity(0)))
+    x = np.concatenate([synth.activations(seed, i, T, L.d_model) for i in range(4)])[:S]
+    lg = np.concatenate([synth.router_logits(seed, i, T, L.n_experts,
+                                             hot_bias=2.0 if args.hot else 0.0)
+                         for i in range(4)])[:S]
+    S = x.shape[0]
+    q, qs = oracle.quant_q8(x)
+    ids, w = oracle.route(lg, L.top_k)
+    need = set(int(e) for e in ids.reshape(-1)) | {L.n_experts}
+    ex = {e: {k: v.cpu().numpy() for k, v in
+              synth.expert_weights(seed, 0, e, L.d_model, L.d_ff, device=dev).items()}
+          for e in sorted(need)}
+    oracle.set_threads(threads)
+    t0 = time.perf_counter()
+    qo, qso = oracle.quant_q8(x)
+    ido, wo = oracle.route(lg, L.top_k)
+    oracle.group(ido, L.n_experts)
+    oracle.ffn(ex, L.n_experts, L.top_k, True, qo, qso, ido, wo)
+    dt = time.perf_counter() - t0
+    return {"value": round(S / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{S} tokens of the same workload (layer set 0): quant, route, group, "
+                      f"FFN in fp64; {dt:.1f}s wall on {threads} threads"}
+
+
+def bench_matvec(args, m, synth, np, torch, dev):
+    c = synth.MATVEC
+    N, D, K = c["n_out"], c["d_in"], (args.rows or 4)
+    copies = args.sets or c["copies"]
+    steps = args.steps or 2000
+    warmup = args.warmup if args.warmup is not None else 100
+    packs = []
+    for i in range(copies):
+        codes, scales = synth.matrix_weights(c["seed"], i, N, D, dev)
+        packs.append(m.moe_pack_mxfp4(codes, scales, 0))
+        del codes, scales
+    x = torch.from_numpy(synth.activations(c["seed"], 0, K, D)).to(dev)
+    q, qs = m.moe_quant_act_q8(x)
+    y = torch.empty((K, N), device=dev)
+    for i in range(warmup):
+        m.moe_matvec_mxfp4(packs[i % copies], N, D, q, qs, y=y)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        m.moe_matvec_mxfp4(packs[i % copies], N, D, q, qs, y=y)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    nbytes = packs[0].numel() + K * (D + D // 8) + K * N * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(16, len(os.sched_getaffinity(0)))
+        codes, scales = synth.matrix_weights(c["seed"], 0, N, D, dev)
+        cn, sn = codes.cpu().numpy(), scales.cpu().numpy()
+        xn = x.cpu().numpy()
+        oracle.set_threads(threads)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 5.0:
+            qo, qso = oracle.quant_q8(xn)
+            oracle.matvec(cn, sn, qo, qso)
+            reps += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(reps * K / dt, 4), "unit": "rows/s", "cores": threads,
+               "kind": "oracle", "sample": f"{reps} full matvecs of {K} rows, {dt:.1f}s wall"}
+    line = {
+        "metric": METRIC, "value": round(K / (us * 1e-6), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4(e2m1+e8m0) x int8 -> exact block dots, f32 accumulate",
+        "data": "synthetic", "config": {"workload": f"matvec {N}x{D}, {K} rows, {copies} copies",
+                                        "rows": K},
+        "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                         kernel="proj_kernel<matvec>", avg_us=round(us, 3)),
+        "cpu_baseline": cpu,
+    }
+    emit(line, args)
+
+
+def emit(line, args):
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

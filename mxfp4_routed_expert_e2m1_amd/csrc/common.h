@@ -1,0 +1,167 @@
+// common.h -- internal helpers shared by the gfx950 kernels of libmoe_mxfp4.
+//
+// Packed MXFP4 layout (written by moe_pack_mxfp4, read by every projection).
+// A matrix W[N][K] (N % 16 == 0, K % 128 == 0) is cut into 16-row groups
+// ("row groups", RG = N/16) and 128-element K chunks (KC = K/128 = four
+// 32-element blocks).  The unit of one wave load is a (row group, K chunk)
+// tile of 1 KiB nibbles: lane l (l = 16*g + r) holds 16 bytes = for each of
+// the chunk's 4 blocks j, the 4 code bytes of row r, elements 8g..8g+7 of
+// block j.  That is exactly the A-operand fragment of one 16x16x32 matrix
+// core instruction per block, so every wave load is one contiguous 1 KiB
+// burst and every nibble lands in the lane that consumes it.
+//   nibbles: [RG][KC][64 lanes][16 B]
+//   scales : [RG][SC][16 rows][16 B]   SC = ceil(K/512); byte i of row r in
+//            super-chunk s is the E8M0 byte of block 16*s + i (0-padded).
+// Gate/up matrices interleave row groups: packed group 2j = gate group j,
+// 2j+1 = up group j, so a workgroup holding 4 consecutive packed groups holds
+// gate and up of the same 32 features.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_mxfp4.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ types
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowsPerGroup = 16;
+constexpr int kChunkK = 128;     // elements per K chunk (4 blocks)
+constexpr int kBlock = 32;       // elements per scale block
+constexpr int kSuperBlocks = 16; // blocks per scale super-chunk
+
+// ----------------------------------------------------------- layout sizes
+struct PackedDims {
+  int64_t rg, kc, sc;
+  int64_t nib_bytes, scale_bytes;
+  __host__ __device__ PackedDims(int n_out, int d_in) {
+    rg = n_out / kRowsPerGroup;
+    kc = d_in / kChunkK;
+    sc = (d_in / kBlock + kSuperBlocks - 1) / kSuperBlocks;
+    nib_bytes = rg * kc * 1024;
+    scale_bytes = rg * sc * 256;
+  }
+  __host__ __device__ int64_t total() const { return nib_bytes + scale_bytes; }
+};
+
+// packed row group -> first canonical row
+__host__ __device__ inline int packed_group_src_row(int pr, int n_out, int interleave) {
+  if (!interleave) return pr * kRowsPerGroup;
+  const int f = n_out / 2;
+  return (pr & 1) ? f + (pr >> 1) * kRowsPerGroup : (pr >> 1) * kRowsPerGroup;
+}
+
+// ------------------------------------------------------ device primitives
+// E8M0 byte -> fp32 2^(u-127) (exact for u in 1..254).
+__device__ inline float e8m0_to_f32(uint32_t u) { return __uint_as_float(u << 23); }
+
+// One A fragment: the 8 E2M1 codes of a dword (element 2i in the low nibble of
+// byte i/2) -> 8 bf16 values value*scale, via the gfx950 FP4 converter.
+// Exact: E2M1 values have 2 significant bits and scale is a power of two.
+__device__ inline bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+// 8 int8 codes -> 8 bf16 (exact: |q| <= 127 needs 7 significant bits).
+__device__ inline bf16x8 i8x8_to_bf16x8(u32x2 v) {
+  uint32_t out[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t word = (p < 2) ? v[0] : v[1];
+    const int sh = (p & 1) * 16;
+    const float lo = (float)(int32_t)(int8_t)((word >> sh) & 0xFF);
+    const float hi = (float)(int32_t)(int8_t)((word >> (sh + 8)) & 0xFF);
+    out[p] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  u32x4 r = {out[0], out[1], out[2], out[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// D[16][16] = A[16][32] * B[32][16] on the matrix core, fp32 result, zero C.
+// Lane l supplies A row l%16 / B column l%16, K elements 8*(l/16)..+7, and
+// receives D rows 4*(l/16)+i (i = 0..3) of column l%16.  With A holding
+// value*2^(u-127) and B integer codes every product and partial sum is a
+// multiple of 2^(u-128) below 2^16 units, so the result is exact.
+__device__ inline f32x4 mfma_block(bf16x8 a, bf16x8 b) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero, 0, 0, 0);
+}
+
+__device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// inclusive prefix sum over a wave64
+__device__ inline int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------- tiles
+// A "tile" is up to 16 token columns of one expert that share one weight
+// pass.  Tiles run over routed experts in expert order (ceil(count/16)
+// tiles each), then over the shared expert (ceil(rows/16) tiles).
+struct Tile {
+  int expert;  // 0..E-1, or E for the shared expert; -1 if beyond the last
+  int start;   // first sorted position (routed) or first token (shared)
+  int count;   // 1..16 columns
+};
+
+// Every lane of the calling wave gets the same answer.
+__device__ inline Tile find_tile(const int32_t* __restrict__ offsets, int n_experts,
+                                 int has_shared, int rows, int tile) {
+  Tile t{-1, 0, 0};
+  int base = 0;
+  for (int e0 = 0; e0 < n_experts; e0 += 64) {
+    const int e = e0 + lane_id();
+    const int c = (e < n_experts) ? offsets[e + 1] - offsets[e] : 0;
+    const int nt = (c + 15) >> 4;
+    const int incl = wave_incl_scan(nt);
+    const int total = __shfl(incl, 63, 64);
+    if (tile < base + total) {
+      const uint64_t m = __ballot(incl > tile - base);
+      const int L = __ffsll((unsigned long long)m) - 1;
+      const int excl = __shfl(incl - nt, L, 64);
+      const int ce = __shfl(c, L, 64);
+      const int chunk = tile - base - excl;
+      t.expert = e0 + L;
+      t.start = __shfl(e < n_experts ? offsets[e] : 0, L, 64) + chunk * 16;
+      t.count = min(16, ce - chunk * 16);
+      return t;
+    }
+    base += total;
+  }
+  if (has_shared) {
+    const int st = tile - base;
+    if (st < (rows + 15) / 16) {
+      t.expert = n_experts;
+      t.start = st * 16;
+      t.count = min(16, rows - st * 16);
+    }
+  }
+  return t;
+}
+
+// ------------------------------------------------------------ host side
+bool device_is_gfx950();  // cached per device
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

@@ -1,0 +1,184 @@
+// route.hip -- top-k routing and bit-exact stable expert grouping.
+//
+// Routing: gfx90a report §3.2 (256 routed experts, top-6 per token) and §5.3
+// (membership ties broken by logical id, selected positions in a fixed
+// order).  One wave per token: k rounds of a wave-wide arg-max over
+// (logit desc, index asc); weights are fp32 sigmoid scores renormalised over
+// the k picks.
+//
+// Grouping: gfx90a report §7.1 item 8 (the expert sorter groups assignments
+// so each expert scans its packed weights once).  One workgroup: an LDS
+// histogram (order-free), an exclusive scan, then a chunked stable scatter in
+// which a lane's destination is the expert's running base + the counts of
+// earlier waves in the chunk + its rank among earlier lanes of its wave with
+// the same expert (from ballots).  Atomics only add counts; no atomic decides
+// an order, so the permutation is unique and bit-exact.
+#include <float.h>
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;  // keeps the grouping LDS under 64 KiB
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / 64;
+
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int64_t ld_l, int rows, int n_experts,
+                                                         int top_k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+  const int row = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  if (row >= rows) return;  // whole wave exits together
+  const int lane = lane_id();
+  const float* l = logits + (int64_t)row * ld_l;
+  float v[PER_LANE];
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = (e < n_experts) ? l[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  float my_sig = 0.f;
+  int my_id = 0;
+  float sum = 0.f;
+  for (int s = 0; s < top_k; ++s) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+      const int e = lane + 64 * j;
+      const bool ok = e < n_experts && !((taken >> j) & 1u);
+      if (ok && (v[j] > bv || (v[j] == bv && e < be))) {
+        bv = v[j];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    const float sg = 1.0f / (1.0f + expf(-bv));
+    sum += sg;
+    if (lane == s) {
+      my_sig = sg;
+      my_id = be;
+    }
+  }
+  if (lane < top_k) {
+    ids[(int64_t)row * top_k + lane] = my_id;
+    w[(int64_t)row * top_k + lane] = my_sig / sum;
+  }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids,
+                                                              int n_assign, int n_experts,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted) {
+  __shared__ int hist[kMaxExperts];
+  __shared__ int running[kMaxExperts];
+  __shared__ int wave_tot[kGroupWaves];
+  extern __shared__ int wcnt[];  // [kGroupWaves][n_experts]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int e = tid; e < n_experts; e += kGroupThreads) hist[e] = 0;
+  for (int e = tid; e < kGroupWaves * n_experts; e += kGroupThreads) wcnt[e] = 0;
+  __syncthreads();
+  for (int a = tid; a < n_assign; a += kGroupThreads) {
+    const int e = ids[a];
+    if (e >= 0) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+
+  // exclusive scan of hist (n_experts <= kGroupThreads: one entry per thread)
+  const int c = tid < n_experts ? hist[tid] : 0;
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w2 = 0; w2 < wave; ++w2) base += wave_tot[w2];
+  const int excl = base + incl - c;
+  if (tid < n_experts) {
+    counts[tid] = c;
+    offsets[tid] = excl;
+    running[tid] = excl;
+  }
+  int n_valid = 0;
+  for (int w2 = 0; w2 < kGroupWaves; ++w2) n_valid += wave_tot[w2];
+  if (tid == 0) offsets[n_experts] = n_valid;
+  __syncthreads();
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int nbits = 0;
+  while ((1 << nbits) < n_experts) ++nbits;
+  for (int chunk = 0; chunk < n_assign; chunk += kGroupThreads) {
+    const int a = chunk + tid;
+    const int e = (a < n_assign) ? ids[a] : -1;
+    const bool valid = e >= 0;
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool b = valid && ((e >> bit) & 1);
+      const uint64_t m = __ballot(b);
+      same &= ((e >> bit) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int cnt = __popcll(same);
+    const bool leader = valid && rank == 0;
+    if (leader) wcnt[wave * n_experts + e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int pos = running[e] + rank;
+      for (int w2 = 0; w2 < wave; ++w2) pos += wcnt[w2 * n_experts + e];
+      sorted[pos] = a;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&running[e], cnt);
+      wcnt[wave * n_experts + e] = 0;
+    }
+    __syncthreads();
+  }
+  for (int p = n_valid + tid; p < n_assign; p += kGroupThreads) sorted[p] = -1;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int n_experts,
+                               int top_k, int32_t* ids, float* w, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted, void* stream) {
+  if (rows < 0) return MOE_ERR_INVALID_ARG;
+  if (n_experts < 1 || n_experts > kMaxExperts) return MOE_ERR_SHAPE;
+  if (top_k < 1 || top_k > n_experts || top_k > MOE_MAX_TOP_K) return MOE_ERR_SHAPE;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!logits || !ids || !w || !sorted)) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)rows * top_k > (1 << 24)) return MOE_ERR_SHAPE;
+  if (rows > 0 && ld_l < n_experts) return MOE_ERR_STRIDE;
+  if (!aligned(counts, 4) || !aligned(offsets, 4) || (rows > 0 && (!aligned(logits, 4) ||
+      !aligned(ids, 4) || !aligned(w, 4) || !aligned(sorted, 4))))
+    return MOE_ERR_ALIGNMENT;
+  if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
+  hipStream_t s = (hipStream_t)stream;
+  if (rows > 0) {
+    const int per_lane = (n_experts + 63) / 64;
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (per_lane <= 4)
+      hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, ld_l, rows, n_experts,
+                         top_k, ids, w);
+    else
+      hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, ld_l, rows,
+                         n_experts, top_k, ids, w);
+  }
+  const size_t lds = sizeof(int) * (size_t)kGroupWaves * (size_t)n_experts;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds, s, ids, rows * top_k,
+                     n_experts, counts, offsets, sorted);
+  return launch_status();
+}

@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (CPU only: every call here fails validation,
+so nothing is enqueued and no device is needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import mxfp4_routed_expert_e2m1_amd as m
+
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+OK, INVALID, SHAPE, STRIDE, WORKSPACE, ALIGN = 0, -1, -2, -3, -4, -5
+A = C.c_void_p(0x100000)        # 1 MiB-aligned fake device address, never dereferenced
+MIS = C.c_void_p(0x100002)      # misaligned
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+[\s\*]+(moe_\w+)\s*\(", txt, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert len(names) >= 12
+    L = m.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(m.EXPORTS) == names
+
+
+def test_status_strings():
+    assert m.moe_status_string(0) == "ok"
+    assert "workspace" in m.moe_status_string(WORKSPACE)
+    assert m.moe_status_string(12345) == "unknown status"
+
+
+def test_packed_bytes_and_workspace_queries():
+    assert m.moe_packed_bytes(16, 128) == 1024 + 256
+    # 14336 x 4096: exactly the canonical byte count (codes + one byte per 32)
+    assert m.moe_packed_bytes(14336, 4096) == 14336 * 2048 + 14336 * 128
+    assert m.moe_packed_bytes(15, 128) == 0 and m.moe_packed_bytes(16, 96) == 0
+    lay = m.moe_layer_t(4096, 2048, 256, 6, 1, 0x100000, 8912896, 0x200000, 4456448, 0x300000,
+                        0x400000)
+    L = m.lib()
+    # 7 hidden rows: bf16 codes, f32 scales, f32 partials, each 256-aligned
+    assert L.moe_ffn_workspace_bytes(C.byref(lay), 1) == 7 * 2048 * 2 + 7 * 64 * 4 + 7 * 4096 * 4
+    a, b, c = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    assert L.moe_ffn_workspace_layout(C.byref(lay), 1, C.byref(a), C.byref(b), C.byref(c)) == 0
+    assert (a.value, b.value, c.value) == (0, 28672, 28672 + 1792)
+
+
+def test_pack_validation():
+    L = m.lib()
+    f = L.moe_pack_mxfp4
+    assert f(None, 64, A, 4, 16, 128, 0, A, 1 << 20, None) == INVALID
+    assert f(A, 64, A, 4, 15, 128, 0, A, 1 << 20, None) == SHAPE
+    assert f(A, 64, A, 4, 16, 96, 0, A, 1 << 20, None) == SHAPE
+    assert f(A, 64, A, 4, 16, 128, 2, A, 1 << 20, None) == INVALID
+    assert f(A, 64, A, 4, 16, 128, 1, A, 1 << 20, None) == SHAPE   # 16 rows: no gate/up pair
+    assert f(A, 32, A, 4, 16, 128, 0, A, 1 << 20, None) == STRIDE
+    assert f(A, 64, A, 3, 16, 128, 0, A, 1 << 20, None) == STRIDE
+    assert f(MIS, 64, A, 4, 16, 128, 0, A, 1 << 20, None) == ALIGN
+    assert f(A, 66, A, 4, 16, 128, 0, A, 1 << 20, None) == ALIGN
+    assert f(A, 64, A, 4, 16, 128, 0, MIS, 1 << 20, None) == ALIGN
+    assert f(A, 64, A, 4, 16, 128, 0, A, 1279, None) == WORKSPACE
+
+
+def test_quant_validation():
+    f = m.lib().moe_quant_act_q8
+    assert f(A, 64, 0, 64, A, 64, A, 2, None) == OK          # rows == 0: no-op
+    assert f(A, 64, -1, 64, A, 64, A, 2, None) == INVALID
+    assert f(A, 64, 2, 48, A, 64, A, 2, None) == SHAPE
+    assert f(None, 64, 2, 64, A, 64, A, 2, None) == INVALID
+    assert f(A, 32, 2, 64, A, 64, A, 2, None) == STRIDE
+    assert f(A, 64, 2, 64, A, 64, A, 1, None) == STRIDE
+    assert f(MIS, 64, 2, 64, A, 64, A, 2, None) == ALIGN
+    assert f(A, 66, 2, 64, A, 64, A, 2, None) == ALIGN
+    assert f(A, 64, 2, 64, A, 68, A, 2, None) == ALIGN
+
+
+def test_route_validation():
+    f = m.lib().moe_route_group
+    args = lambda rows, E, k, ld=256, counts=A: (A, ld, rows, E, k, A, A, counts, A, A, None)
+    assert f(*args(4, 256, 0)) == SHAPE
+    assert f(*args(4, 256, 17)) == SHAPE
+    assert f(*args(4, 8, 9)) == SHAPE
+    assert f(*args(4, 513, 6, 513)) == SHAPE
+    assert f(*args(4, 256, 6, 255)) == STRIDE
+    assert f(*args(4, 256, 6, counts=None)) == INVALID
+    assert f(*args(-1, 256, 6)) == INVALID
+    assert f(*args(1 << 22, 256, 6)) == SHAPE
+
+
+def _layer(**kw):
+    d = dict(d_model=4096, d_ff=2048, n_experts=256, top_k=6, has_shared=1,
+             gate_up=0x1000000, gate_up_stride=8912896, down=0x2000000, down_stride=4456448,
+             shared_gate_up=0x3000000, shared_down=0x4000000)
+    d.update(kw)
+    return m.moe_layer_t(*[d[k] for k, _ in m.moe_layer_t._fields_])
+
+
+def _ffn(fn, lay, rows=1, q=A, ldq=4096, qs=A, ldqs=128, y=A, ldy=4096, ws=A, wsb=1 << 30):
+    return fn(C.byref(lay) if lay is not None else None, q, ldq, qs, ldqs, rows, A, A, A, A,
+              y, ldy, ws, wsb, None)
+
+
+@pytest.mark.parametrize("name", ["moe_ffn_decode", "moe_ffn_prefill"])
+def test_ffn_validation(name):
+    f = getattr(m.lib(), name)
+    assert _ffn(f, None) == INVALID
+    assert _ffn(f, _layer(d_model=4000)) == SHAPE
+    assert _ffn(f, _layer(d_ff=2000)) == SHAPE
+    assert _ffn(f, _layer(top_k=0)) == SHAPE
+    assert _ffn(f, _layer(top_k=17, n_experts=256)) == SHAPE
+    assert _ffn(f, _layer(n_experts=600)) == SHAPE
+    assert _ffn(f, _layer(has_shared=2)) == INVALID
+    assert _ffn(f, _layer(shared_down=0)) == INVALID
+    assert _ffn(f, _layer(gate_up_stride=8912896 - 256)) == STRIDE
+    assert _ffn(f, _layer(down_stride=4456448 + 16)) == ALIGN
+    assert _ffn(f, _layer(gate_up=0x1000010)) == ALIGN
+    assert _ffn(f, _layer(), rows=0) == SHAPE
+    assert _ffn(f, _layer(), q=None) == INVALID
+    assert _ffn(f, _layer(), ldq=4000) == STRIDE
+    assert _ffn(f, _layer(), ldy=4092) == STRIDE
+    assert _ffn(f, _layer(), ldq=4100) == ALIGN
+    assert _ffn(f, _layer(), qs=MIS) == ALIGN
+    assert _ffn(f, _layer(), ws=MIS) == ALIGN
+    assert _ffn(f, _layer(), wsb=1000) == WORKSPACE
+    if name == "moe_ffn_decode":
+        assert _ffn(f, _layer(), rows=17) == SHAPE
+
+
+def test_matvec_and_debug_validation():
+    L = m.lib()
+    assert L.moe_matvec_mxfp4(A, 14336, 4096, A, 4096, A, 128, 0, A, 14336, None) == SHAPE
+    assert L.moe_matvec_mxfp4(A, 14336, 4096, A, 4096, A, 128, 17, A, 14336, None) == SHAPE
+    assert L.moe_matvec_mxfp4(A, 14330, 4096, A, 4096, A, 128, 1, A, 14336, None) == SHAPE
+    assert L.moe_matvec_mxfp4(MIS, 14336, 4096, A, 4096, A, 128, 1, A, 14336, None) == ALIGN
+    assert L.moe_matvec_mxfp4(A, 14336, 4096, A, 4096, A, 128, 1, A, 100, None) == STRIDE
+    assert L.moe_debug_block_dots(None, 16, 128, A, 128, 1, A, None) == INVALID
+    assert L.moe_debug_block_dots(A, 16, 128, A, 100, 1, A, None) == STRIDE

@@ -1,0 +1,191 @@
+"""GPU parity of the whole routed-expert layer (decode and prefill) through the
+C ABI, stage by stage, against the oracle, at the workloads' real shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (assert_rows_close, check_hidden, down_col_absmax, flip_bound)
+
+pytestmark = pytest.mark.gpu
+
+m = pytest.importorskip("mxfp4_routed_expert_e2m1_amd")
+DEV = "cuda"
+
+_CACHE = {}
+
+
+def layer_for(L: synth.Layer, seed: int, set_idx: int = 0):
+    """Packed layer on the GPU (one cached at a time: a DS-V4 layer is 3.4 GB)."""
+    key = (L, seed, set_idx)
+    if key not in _CACHE:
+        _CACHE.clear()
+        torch.cuda.empty_cache()
+        fn = lambda e: synth.expert_weights(seed, set_idx, e, L.d_model, L.d_ff, device=DEV)
+        _CACHE[key] = m.pack_layer(L.d_model, L.d_ff, L.n_experts, L.top_k, fn,
+                                   has_shared=L.has_shared, device=DEV)
+        torch.cuda.synchronize()
+    return _CACHE[key]
+
+
+def canonical_experts(L, seed, set_idx, experts):
+    return {e: {k: v.cpu().numpy() for k, v in
+                synth.expert_weights(seed, set_idx, e, L.d_model, L.d_ff, device=DEV).items()}
+            for e in sorted(experts)}
+
+
+def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
+             ids_override=None, pads=(0, 0, 0)):
+    """Run the GPU layer and check it against the oracle on rows `sample`."""
+    T = x.shape[0]
+    layer = layer_for(L, seed, set_idx)
+    pad_x, pad_q, pad_y = pads
+    xw = torch.zeros((T, L.d_model + pad_x), device=DEV)
+    xw[:, : L.d_model] = torch.from_numpy(x).to(DEV)
+    qw = torch.zeros((T, L.d_model + pad_q), dtype=torch.int8, device=DEV)
+    sw = torch.zeros((T, L.d_model // 32 + pad_q // 8), dtype=torch.float32, device=DEV)
+    q, qs = m.moe_quant_act_q8(xw[:, : L.d_model], q=qw[:, : L.d_model],
+                               scales=sw[:, : L.d_model // 32])
+    ids, w, counts, offsets, srt = m.moe_route_group(torch.from_numpy(logits).to(DEV), L.top_k)
+    # oracle side: its own quantiser, router and grouping on the same inputs
+    q_o, qs_o = oracle.quant_q8(x)
+    ids_o, w_o = oracle.route(logits, L.top_k)
+    c_o, off_o, srt_o = oracle.group(ids_o, L.n_experts)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+    np.testing.assert_array_equal(qs.cpu().numpy(), qs_o)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_o)
+    np.testing.assert_array_equal(srt.cpu().numpy()[: srt_o.size], srt_o)
+    if ids_override is not None:  # sentinel-edited routes, regrouped by the oracle
+        ids_o = ids_override
+        c_o, off_o, srt_o = oracle.group(ids_o, L.n_experts)
+        ids = torch.from_numpy(ids_o).to(DEV)
+        w = torch.from_numpy(w_o).to(DEV)
+        offsets = torch.from_numpy(off_o).to(DEV)
+        srt = torch.from_numpy(srt_o).to(DEV)
+    yw = torch.full((T, L.d_model + pad_y), 3.0, device=DEV)
+    ws = torch.empty(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
+    y = getattr(m, entry)(layer, q, qs, ids, w, offsets, srt, y=yw[:, : L.d_model], ws=ws)
+    torch.cuda.synchronize()
+    if pad_y:
+        assert torch.all(yw[:, L.d_model:] == 3.0)
+
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    need = set(int(e) for e in ids_o[rows].reshape(-1) if e >= 0)
+    if L.has_shared:
+        need.add(L.n_experts)
+    ex = canonical_experts(L, seed, set_idx, need)
+    k, slots = L.top_k, L.top_k + 1
+    y_o, mid = oracle.ffn(ex, L.n_experts, k, L.has_shared, q_o[rows], qs_o[rows], ids_o[rows],
+                          w_o[rows], want_intermediates=True)
+
+    # stage 3: requantised intermediate read back from the documented workspace
+    off_h, off_hs, _ = m.moe_ffn_workspace_layout(layer, T)
+    A = T * k
+    n_h = A + (T if L.has_shared else 0)
+    hb = ws[off_h: off_h + n_h * L.d_ff * 2].view(torch.bfloat16).view(n_h, L.d_ff)
+    hs = ws[off_hs: off_hs + n_h * (L.d_ff // 32) * 4].view(torch.float32).view(n_h, L.d_ff // 32)
+    hb, hs = hb.float().cpu().numpy(), hs.cpu().numpy()
+    pos = np.empty(A, np.int64)
+    valid = srt_o[: off_o[-1]]
+    pos[valid] = np.arange(valid.size)
+    gpu_rows, o_rows, wts = [], [], []
+    for j, t in enumerate(rows):
+        for i in range(slots):
+            if i < k and ids_o[t, i] < 0:
+                continue
+            if i == k and not L.has_shared:
+                continue
+            gpu_rows.append(pos[t * k + i] if i < k else A + t)
+            o_rows.append(j * slots + i)
+            wts.append(w_o[t, i] if i < k else 1.0)
+    gpu_rows, o_rows = np.array(gpu_rows), np.array(o_rows)
+    flips = np.zeros((len(rows) * slots, L.d_ff), bool)
+    flips[o_rows] = check_hidden(hb[gpu_rows], hs[gpu_rows], mid["hq"][o_rows],
+                                 mid["hs"][o_rows], mid["h"][o_rows])
+    weight = np.zeros(len(rows) * slots)
+    weight[o_rows] = wts
+    col_max = {}
+
+    def colmax(r):
+        j, i = divmod(r, slots)
+        e = L.n_experts if i == k else int(ids_o[rows[j], i])
+        if e not in col_max:
+            col_max[e] = down_col_absmax(ex[e]["down_codes"], ex[e]["down_scales"])
+        return col_max[e]
+
+    extra_slot = flip_bound(flips, weight, mid["hs"], colmax)
+    extra = extra_slot.reshape(len(rows), slots).sum(axis=1)
+    worst = assert_rows_close(y.cpu().numpy()[rows], y_o, extra=extra, what=entry)
+    return dict(worst=worst, flips=int(flips.sum()), y=y)
+
+
+TINY = synth.TINY["layer"]
+DSV4 = synth.DSV4_LAYER
+
+
+def test_tiny_layer_all_rows():
+    c = synth.TINY
+    x = synth.activations(c["seed"], 0, c["rows"], TINY.d_model)
+    lg = synth.router_logits(c["seed"], 0, c["rows"], TINY.n_experts)
+    r = run_case(TINY, c["seed"], x, lg)
+    assert r["flips"] == 0
+
+
+def test_tiny_layer_prefill_entry_matches_decode():
+    c = synth.TINY
+    x = synth.activations(c["seed"], 1, 40, TINY.d_model)
+    lg = synth.router_logits(c["seed"], 1, 40, TINY.n_experts)
+    run_case(TINY, c["seed"], x, lg, entry="moe_ffn_prefill")
+
+
+def test_decode_one_token():
+    c = synth.DECODE
+    x = synth.activations(c["seed"], 0, 1, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 0, 1, DSV4.n_experts)
+    run_case(DSV4, c["seed"], x, lg)
+
+
+@pytest.mark.parametrize("rows", [2, 4, 8, 16])
+@pytest.mark.parametrize("hot", [0.0, 2.0])
+def test_decode_batch(rows, hot):
+    c = synth.DECODE_BATCH
+    x = synth.activations(c["seed"], rows, rows, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], rows, rows, DSV4.n_experts, hot_bias=hot)
+    run_case(DSV4, c["seed"], x, lg)
+
+
+def test_decode_deterministic_and_padded():
+    c = synth.DECODE_BATCH
+    x = synth.activations(c["seed"], 99, 5, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 99, 5, DSV4.n_experts)
+    r1 = run_case(DSV4, c["seed"], x, lg, pads=(64, 128, 36))
+    r2 = run_case(DSV4, c["seed"], x, lg)
+    assert torch.equal(r1["y"], r2["y"])
+
+
+def test_decode_sentinel_routes():
+    c = synth.DECODE_BATCH
+    T = 6
+    x = synth.activations(c["seed"], 7, T, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 7, T, DSV4.n_experts)
+    ids_o, _ = oracle.route(lg, DSV4.top_k)
+    ids_s = ids_o.copy()
+    ids_s[0, 1] = -1
+    ids_s[3, :] = -1          # a token owned by no local expert: shared expert only
+    ids_s[5, 5] = -1
+    run_case(DSV4, c["seed"], x, lg, ids_override=ids_s)
+
+
+@pytest.mark.parametrize("rows", [512, 4096])
+def test_prefill_sampled(rows):
+    c = synth.PREFILL
+    x = synth.activations(c["seed"], rows, rows, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], rows, rows, DSV4.n_experts)
+    rng = np.random.default_rng(rows)
+    sample = np.sort(rng.choice(rows, 24, replace=False))
+    sample[-1] = rows - 1    # the ragged tail
+    r = run_case(DSV4, c["seed"], x, lg, sample=sample, entry="moe_ffn_prefill")
+    print(f"prefill {rows}: worst err/tol {r['worst']:.3f}, flips {r['flips']}")
