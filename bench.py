@@ -122,15 +122,38 @@ def main():
         counts = route_out[2].cpu().numpy()
         touched.append(int(np.count_nonzero(counts)) + 1)  # + shared expert
 
-    for i in range(warmup):
+    # eager warmup; eager reference of the last timed step
+    cycle = int(np.lcm(sets, n_inputs))
+    reps, rem = divmod(steps, cycle)
+    last = (steps - 1) % cycle
+    for i in range(max(warmup, cycle)):
         step(i)
+    torch.cuda.synchronize()
+    t_e = time.perf_counter()
+    for i in range(cycle):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t_e) * 1e3 / cycle
+    step(last)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+
+    # HIP graphs: one holds a whole rotation cycle of steps, one the remainder,
+    # so exactly `steps` steps run with no host work between them
+    g_step = capture(torch, lambda: [step(i) for i in range(cycle)])
+    g_rem = capture(torch, lambda: [step(i) for i in range(rem)]) if rem else None
+    g_step.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for i in range(steps):
-        step(i)
+    for _ in range(reps):
+        g_step.replay()
+    if g_rem is not None:
+        g_rem.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
+    if not torch.equal(y, y_eager):
+        raise SystemExit("graph replay differs from the eager step")
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / steps
     tok_s = T * steps / (ms_total / 1e3)
@@ -139,24 +162,25 @@ def main():
     dn_bytes = L.d_model * L.d_ff // 2 + L.d_model * L.d_ff // 32
     A = T * L.top_k + T
     act_bytes = T * (L.d_model * 4 + L.d_model + L.d_model // 8)  # x read, q + scales written
-    mean_touched = float(np.mean([touched[i % n_inputs] for i in range(steps)]))
+    mean_touched = float(np.mean(touched))
     step_bytes = mean_touched * (gu_bytes + dn_bytes) + act_bytes + T * L.d_model * 4
 
-    # dominant kernel: the gate/up stage, timed alone over the rotated sets
-    n_k = max(50, min(steps, 400))
-    for i in range(n_inputs):  # make every workspace valid for the stage-only runs
-        step(i)
+    # dominant kernel: the gate/up stage alone over the rotated sets, in a graph
+    ids, w, counts, offsets, srt = route_out   # routes of input `last`
+    n_k = sets * max(1, 64 // sets)
+    g_k = capture(torch, lambda: [m.moe_ffn_stages(layers[i % sets], int(prefill),
+                                                   m.MOE_STAGE_GATE_UP, q, qs, ids, w,
+                                                   offsets, srt, y, ws) for i in range(n_k)])
+    g_k.replay()
     torch.cuda.synchronize()
+    kreps = max(2, (200 if prefill else 2000) // n_k)
     ev0.record(stream)
-    for i in range(n_k):
-        ids, w, counts, offsets, srt = route_out
-        m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP, q, qs, ids, w,
-                         offsets, srt, y, ws)
+    for _ in range(kreps):
+        g_k.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
-    k_us = ev0.elapsed_time(ev1) * 1e3 / n_k
-    # routes in route_out now belong to the last input evaluated
-    last_touched = touched[(n_inputs - 1) % n_inputs]
+    k_us = ev0.elapsed_time(ev1) * 1e3 / (kreps * n_k)
+    last_touched = touched[last % n_inputs]
     hidden_bytes = A * (L.d_ff + L.d_ff // 32 * 4)
     k_bytes = last_touched * gu_bytes + T * (L.d_model + L.d_model // 8) + hidden_bytes
     if prefill:
@@ -189,11 +213,26 @@ def main():
                                + (", hot-16 +2.0 bias" if hot else ""),
                    "rows": T, "layer_sets": sets, "seed": seed},
         "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "eager_ms_per_step": round(eager_ms, 4),
         "step_bytes": int(step_bytes),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     emit(line, args)
+
+
+def capture(torch, fn):
+    """Capture fn's launches (on torch's current stream) into a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
 
 
 def cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill):
@@ -239,13 +278,22 @@ def bench_matvec(args, m, synth, np, torch, dev):
     x = torch.from_numpy(synth.activations(c["seed"], 0, K, D)).to(dev)
     q, qs = m.moe_quant_act_q8(x)
     y = torch.empty((K, N), device=dev)
-    for i in range(warmup):
+    for i in range(max(warmup, copies)):
         m.moe_matvec_mxfp4(packs[i % copies], N, D, q, qs, y=y)
+    torch.cuda.synchronize()
+    reps, rem = divmod(steps, copies)
+    g = capture(torch, lambda: [m.moe_matvec_mxfp4(packs[i], N, D, q, qs, y=y)
+                                for i in range(copies)])
+    g_rem = capture(torch, lambda: [m.moe_matvec_mxfp4(packs[i], N, D, q, qs, y=y)
+                                    for i in range(rem)]) if rem else None
+    g.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for i in range(steps):
-        m.moe_matvec_mxfp4(packs[i % copies], N, D, q, qs, y=y)
+    for _ in range(reps):
+        g.replay()
+    if g_rem is not None:
+        g_rem.replay()
     ev1.record()
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / steps

@@ -189,3 +189,53 @@ def test_prefill_sampled(rows):
     sample[-1] = rows - 1    # the ragged tail
     r = run_case(DSV4, c["seed"], x, lg, sample=sample, entry="moe_ffn_prefill")
     print(f"prefill {rows}: worst err/tol {r['worst']:.3f}, flips {r['flips']}")
+
+
+def test_decode_graph_replays_match_eager():
+    # quant + route/group + FFN captured in one HIP graph; every replay, with
+    # other eager work and synchronisations in between, equals the eager result
+    c = synth.DECODE_BATCH
+    layer = layer_for(DSV4, c["seed"])
+    T = 4
+    x = torch.from_numpy(synth.activations(c["seed"], 50, T, DSV4.d_model)).to(DEV)
+    lg = torch.from_numpy(synth.router_logits(c["seed"], 50, T, DSV4.n_experts)).to(DEV)
+    q = torch.empty((T, DSV4.d_model), dtype=torch.int8, device=DEV)
+    qs = torch.empty((T, DSV4.d_model // 32), dtype=torch.float32, device=DEV)
+    rt = (torch.empty((T, 6), dtype=torch.int32, device=DEV),
+          torch.empty((T, 6), dtype=torch.float32, device=DEV),
+          torch.empty(256, dtype=torch.int32, device=DEV),
+          torch.empty(257, dtype=torch.int32, device=DEV),
+          torch.empty(T * 6, dtype=torch.int32, device=DEV))
+    y = torch.empty((T, DSV4.d_model), device=DEV)
+    ws = torch.empty(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
+
+    def step():
+        m.moe_quant_act_q8(x, q=q, scales=qs)
+        ids, w, counts, offsets, srt = m.moe_route_group(lg, 6, out=rt)
+        m.moe_ffn_decode(layer, q, qs, ids, w, offsets, srt, y=y, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    x2 = torch.from_numpy(synth.activations(c["seed"], 51, T, DSV4.d_model)).to(DEV)
+    for r in range(4):
+        y.zero_()
+        ws.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r}"
+        # unrelated eager work between replays
+        q2, qs2 = m.moe_quant_act_q8(x2)
+        other = m.moe_ffn_decode(layer, q2, qs2, *m.moe_route_group(lg, 6)[:2],
+                                 *m.moe_route_group(lg, 6)[3:])
+        torch.cuda.synchronize()
+        assert torch.isfinite(other).all()
