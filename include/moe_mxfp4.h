@@ -170,6 +170,9 @@ typedef struct moe_layer {
  *                                      codes stored as exact bf16 values
  *   hidden scales f32  [A'][d_ff/32]
  *   partials      f32  [A'][d_model]  per-slot down projections
+ *   activations   bf16 [A'][d_model]  prefill: activation codes gathered per
+ *                                      hidden row, stored as exact bf16 values
+ *   act scales    f32  [A'][d_model/32]
  * Hidden row of routed assignment at sorted position p is p; the shared
  * expert's row for token t is rows*top_k + t.  Partials row of routed
  * assignment a is a; shared: rows*top_k + t.  The byte offsets are returned
@@ -202,21 +205,21 @@ int moe_ffn_prefill(const moe_layer_t* L, const int8_t* q, int64_t ld_q,
                     const float* w, const int32_t* offsets, const int32_t* sorted,
                     float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream);
 
-/* The three stages of moe_ffn_decode / moe_ffn_prefill, selectable:
+/* The two stages of moe_ffn_decode / moe_ffn_prefill, selectable:
  *   MOE_STAGE_GATE_UP  gate/up projection + SwiGLU + group-32 requant
  *                      (writes the workspace's hidden codes and scales)
- *   MOE_STAGE_DOWN     down projection of the hidden codes (writes partials)
- *   MOE_STAGE_COMBINE  fixed-order weighted combine of the partials into y
+ *   MOE_STAGE_DOWN     down projection of the hidden codes into fp32 per-slot
+ *                      partials and their fixed-order weighted combine into y
  * Stages communicate only through the workspace, so running them in separate
  * calls (in order, same arguments) gives the same y as one full call; a stage
- * may be re-run on its own, e.g. to time it.  `prefill` = 0 selects the
- * decode limits (rows <= MOE_MAX_DECODE_ROWS), 1 the prefill ones.  Other
- * arguments and errors as moe_ffn_decode; stage_mask must be non-zero and
- * within MOE_STAGE_ALL. */
+ * may be re-run on its own, e.g. to time it, once the workspace has seen a
+ * GATE_UP stage of the same rows.  `prefill` = 0 selects the decode limits and
+ * kernels (rows <= MOE_MAX_DECODE_ROWS), 1 the prefill ones.  Other arguments
+ * and errors as moe_ffn_decode; stage_mask must be non-zero and within
+ * MOE_STAGE_ALL. */
 #define MOE_STAGE_GATE_UP 1
 #define MOE_STAGE_DOWN 2
-#define MOE_STAGE_COMBINE 4
-#define MOE_STAGE_ALL 7
+#define MOE_STAGE_ALL 3
 int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask, const int8_t* q,
                    int64_t ld_q, const float* qs, int64_t ld_qs, int rows,
                    const int32_t* ids, const float* w, const int32_t* offsets,

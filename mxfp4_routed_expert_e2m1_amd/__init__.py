@@ -26,7 +26,7 @@ EXPORTS = [
     "moe_debug_block_dots", "moe_status_string",
 ]
 
-MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE, MOE_STAGE_ALL = 1, 2, 4, 7
+MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_ALL = 1, 2, 3
 
 
 class MoeError(RuntimeError):

@@ -117,40 +117,60 @@ __device__ inline int wave_incl_scan(int v) {
 struct Tile {
   int expert;  // 0..E-1, or E for the shared expert; -1 if beyond the last
   int start;   // first sorted position (routed) or first token (shared)
-  int count;   // 1..16 columns
+  int count;   // 1..TM columns
 };
 
-// Every lane of the calling wave gets the same answer.
+// Every lane of the calling wave gets the same answer.  One memory round trip:
+// each lane loads the offsets of its (up to 8) experts at once, then a wave
+// scan of per-lane tile counts locates the tile.  *n_tiles receives the total
+// number of tiles of the call (routed + shared).  Tiles hold up to TM columns.
+template <int TM = 16>
 __device__ inline Tile find_tile(const int32_t* __restrict__ offsets, int n_experts,
-                                 int has_shared, int rows, int tile) {
-  Tile t{-1, 0, 0};
-  int base = 0;
-  for (int e0 = 0; e0 < n_experts; e0 += 64) {
-    const int e = e0 + lane_id();
-    const int c = (e < n_experts) ? offsets[e + 1] - offsets[e] : 0;
-    const int nt = (c + 15) >> 4;
-    const int incl = wave_incl_scan(nt);
-    const int total = __shfl(incl, 63, 64);
-    if (tile < base + total) {
-      const uint64_t m = __ballot(incl > tile - base);
-      const int L = __ffsll((unsigned long long)m) - 1;
-      const int excl = __shfl(incl - nt, L, 64);
-      const int ce = __shfl(c, L, 64);
-      const int chunk = tile - base - excl;
-      t.expert = e0 + L;
-      t.start = __shfl(e < n_experts ? offsets[e] : 0, L, 64) + chunk * 16;
-      t.count = min(16, ce - chunk * 16);
-      return t;
-    }
-    base += total;
+                                 int has_shared, int rows, int tile, int* n_tiles) {
+  const int lane = lane_id();
+  const int per = (n_experts + 63) >> 6;  // <= 8 (n_experts <= 512)
+  const int e0 = lane * per;
+  int o[9];
+#pragma unroll
+  for (int i = 0; i <= 8; ++i) o[i] = (i <= per && e0 + i <= n_experts) ? offsets[e0 + i] : 0;
+  int nt[8];
+  int lsum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = (i < per && e0 + i < n_experts) ? o[i + 1] - o[i] : 0;
+    nt[i] = (c + TM - 1) / TM;
+    lsum += nt[i];
   }
-  if (has_shared) {
-    const int st = tile - base;
-    if (st < (rows + 15) / 16) {
-      t.expert = n_experts;
-      t.start = st * 16;
-      t.count = min(16, rows - st * 16);
+  const int incl = wave_incl_scan(lsum);
+  const int routed = __shfl(incl, 63, 64);
+  const int shared_tiles = has_shared ? (rows + TM - 1) / TM : 0;
+  *n_tiles = routed + shared_tiles;
+  Tile t{-1, 0, 0};
+  if (tile < routed) {
+    int rem = tile - (incl - lsum);
+    int se = -1, ss = 0, sc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (se < 0) {
+        if (rem < nt[i]) {
+          se = e0 + i;
+          ss = o[i] + rem * TM;
+          sc = min(TM, o[i + 1] - o[i] - rem * TM);
+        } else {
+          rem -= nt[i];
+        }
+      }
     }
+    const uint64_t m = __ballot(incl > tile);
+    const int L = __ffsll((unsigned long long)m) - 1;
+    t.expert = __shfl(se, L, 64);
+    t.start = __shfl(ss, L, 64);
+    t.count = __shfl(sc, L, 64);
+  } else if (tile - routed < shared_tiles) {
+    const int st = tile - routed;
+    t.expert = n_experts;
+    t.start = st * TM;
+    t.count = min(TM, rows - st * TM);
   }
   return t;
 }

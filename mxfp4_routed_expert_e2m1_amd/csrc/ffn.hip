@@ -23,7 +23,7 @@
 // last (gfx90a report §8.2 and Table 4: fp32 partials, fixed reduction).
 #include <algorithm>
 
-#include "common.h"
+#include "ffn_internal.h"
 
 namespace moe {
 
@@ -54,8 +54,118 @@ struct ProjArgs {
   int64_t ld_h, ld_hs;
 };
 
-template <int PASS, int W, int RGW>
-__global__ __launch_bounds__(W * 64) void proj_kernel(ProjArgs p) {
+// One wave's share of a projection: RGW row groups x K chunks [kc0, kc0 + n),
+// accumulated into acc.  KPW > 0: exactly KPW chunks, every weight load issued
+// up front (kc0 % 4 == 0 when KPW == 4, so one 16-byte load per row group
+// holds the scales of all its blocks); KPW == 0: runtime chunk count with a
+// one-chunk prefetch.  B/activation-scale loads run one chunk ahead.
+template <int PASS, int RGW, int KPW>
+__device__ inline void wave_project(const ProjArgs& p, const uint8_t* blob, int pr0, int kc0,
+                                    int n_kc, int brow, f32x4 (&acc)[RGW]) {
+  const int lane = lane_id();
+  const int g8 = 8 * (lane >> 4);
+  const u32x4* nib = (const u32x4*)blob;
+  const uint8_t* scl = blob + p.nib_bytes;
+
+  auto load_b = [&](int kc, u32x4* b, f32x4& d) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t k = (int64_t)kc * kChunkK + j * kBlock + g8;
+      if (PASS == PASS_DOWN) {
+        b[j] = *(const u32x4*)((const uint16_t*)p.b + (int64_t)brow * p.ld_b + k);
+      } else {
+        const u32x2 v = *(const u32x2*)((const int8_t*)p.b + (int64_t)brow * p.ld_b + k);
+        b[j] = u32x4{v[0], v[1], 0u, 0u};
+      }
+    }
+    d = *(const f32x4*)(p.bs + (int64_t)brow * p.ld_bs + (int64_t)kc * 4);
+  };
+  auto compute = [&](const u32x4* a, const uint32_t* s, const u32x4* b, f32x4 d) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 bb;
+      if (PASS == PASS_DOWN) bb = __builtin_bit_cast(bf16x8, b[j]);
+      else bb = i8x8_to_bf16x8(u32x2{b[j][0], b[j][1]});
+#pragma unroll
+      for (int g = 0; g < RGW; ++g) {
+        const float sc = e8m0_to_f32((s[g] >> (8 * j)) & 0xFFu);
+        const f32x4 r = mfma_block(fp4x8_to_bf16x8(a[g][j], sc), bb);
+        acc[g] += r * d[j];
+      }
+    }
+  };
+
+  if constexpr (KPW > 0) {
+    u32x4 a[KPW][RGW];
+#pragma unroll
+    for (int kk = 0; kk < KPW; ++kk)
+#pragma unroll
+      for (int g = 0; g < RGW; ++g)
+        a[kk][g] = nib[((int64_t)(pr0 + g) * p.kc_total + kc0 + kk) * 64 + lane];
+    uint32_t s[KPW][RGW];
+    if constexpr (KPW == 4) {
+#pragma unroll
+      for (int g = 0; g < RGW; ++g) {
+        const u32x4 sv = *(const u32x4*)(scl + (((int64_t)(pr0 + g) * p.sc_total + (kc0 >> 2)) * 16 +
+                                                (lane & 15)) * 16);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) s[kk][g] = sv[kk];
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KPW; ++kk)
+#pragma unroll
+        for (int g = 0; g < RGW; ++g) {
+          const int kc = kc0 + kk;
+          s[kk][g] = *(const uint32_t*)(scl + (((int64_t)(pr0 + g) * p.sc_total + (kc >> 2)) * 16 +
+                                               (lane & 15)) * 16 + (kc & 3) * 4);
+        }
+    }
+    u32x4 b[2][4];
+    f32x4 d[2];
+    load_b(kc0, b[0], d[0]);
+#pragma unroll
+    for (int kk = 0; kk < KPW; ++kk) {
+      if (kk + 1 < KPW) load_b(kc0 + kk + 1, b[(kk + 1) & 1], d[(kk + 1) & 1]);
+      compute(a[kk], s[kk], b[kk & 1], d[kk & 1]);
+    }
+  } else {
+    u32x4 a_cur[RGW], a_nxt[RGW], b_cur[4], b_nxt[4];
+    uint32_t s_cur[RGW], s_nxt[RGW];
+    f32x4 d_cur, d_nxt;
+    auto load_a = [&](int kc, u32x4* a, uint32_t* s) {
+#pragma unroll
+      for (int g = 0; g < RGW; ++g) {
+        a[g] = nib[((int64_t)(pr0 + g) * p.kc_total + kc) * 64 + lane];
+        s[g] = *(const uint32_t*)(scl + (((int64_t)(pr0 + g) * p.sc_total + (kc >> 2)) * 16 +
+                                         (lane & 15)) * 16 + (kc & 3) * 4);
+      }
+    };
+    if (n_kc > 0) {
+      load_a(kc0, a_cur, s_cur);
+      load_b(kc0, b_cur, d_cur);
+    }
+    for (int kc = kc0; kc < kc0 + n_kc; ++kc) {
+      if (kc + 1 < kc0 + n_kc) {
+        load_a(kc + 1, a_nxt, s_nxt);
+        load_b(kc + 1, b_nxt, d_nxt);
+      }
+      compute(a_cur, s_cur, b_cur, d_cur);
+#pragma unroll
+      for (int g = 0; g < RGW; ++g) {
+        a_cur[g] = a_nxt[g];
+        s_cur[g] = s_nxt[g];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b_cur[j] = b_nxt[j];
+      d_cur = d_nxt;
+    }
+  }
+}
+
+// 4 waves per SIMD (<= 128 VGPRs) keeps two 8-wave workgroups resident per CU.
+template <int PASS, int W, int RGW, int KPW>
+__global__ __launch_bounds__(W * 64, 4) void proj_kernel(ProjArgs p) {
   static_assert(PASS != PASS_GATEUP || RGW == 4, "gate/up needs 2 gate/up pairs = 32 features");
   __shared__ float red[W][RGW * 4][64];
   const int wave = threadIdx.x >> 6;
@@ -65,12 +175,13 @@ __global__ __launch_bounds__(W * 64) void proj_kernel(ProjArgs p) {
   const int tile_idx = blockIdx.x / n_rb;
 
   Tile t;
+  int n_tiles = 1;
   if (PASS == PASS_MATVEC) {
     t.expert = 0;
     t.start = 0;
     t.count = p.rows;
   } else {
-    t = find_tile(p.offsets, p.n_experts, p.has_shared, p.rows, tile_idx);
+    t = find_tile(p.offsets, p.n_experts, p.has_shared, p.rows, tile_idx, &n_tiles);
   }
   if (t.expert < 0) return;  // the same for every wave of the workgroup
   const bool shared = (PASS != PASS_MATVEC) && t.expert == p.n_experts;
@@ -87,66 +198,16 @@ __global__ __launch_bounds__(W * 64) void proj_kernel(ProjArgs p) {
   else if (PASS == PASS_GATEUP) brow = shared ? t.start + ccol : p.sorted[t.start + ccol] / p.top_k;
   else brow = shared ? n_tok_assign + t.start + ccol : t.start + ccol;
 
-  const int kc0 = wave * p.kc_total / W;
-  const int kc1 = (wave + 1) * p.kc_total / W;
   const int pr0 = rb * RGW;
-  const u32x4* nib = (const u32x4*)blob;
-  const uint8_t* scl = blob + p.nib_bytes;
-  const int g8 = 8 * (lane >> 4);
-
   f32x4 acc[RGW];
 #pragma unroll
   for (int g = 0; g < RGW; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // register double buffer over K chunks
-  u32x4 a_cur[RGW], a_nxt[RGW];
-  uint32_t s_cur[RGW], s_nxt[RGW];
-  u32x4 b_cur[4], b_nxt[4];  // int8: .xy used; bf16: all four dwords
-  f32x4 d_cur, d_nxt;
-
-  auto load = [&](int kc, u32x4* a, uint32_t* s, u32x4* b, f32x4& d) {
-#pragma unroll
-    for (int g = 0; g < RGW; ++g) {
-      a[g] = nib[((int64_t)(pr0 + g) * p.kc_total + kc) * 64 + lane];
-      s[g] = *(const uint32_t*)(scl + (((int64_t)(pr0 + g) * p.sc_total + (kc >> 2)) * 16 +
-                                       (lane & 15)) * 16 + (kc & 3) * 4);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t k = (int64_t)kc * kChunkK + j * kBlock + g8;
-      if (PASS == PASS_DOWN) {
-        b[j] = *(const u32x4*)((const uint16_t*)p.b + (int64_t)brow * p.ld_b + k);
-      } else {
-        const u32x2 v = *(const u32x2*)((const int8_t*)p.b + (int64_t)brow * p.ld_b + k);
-        b[j] = u32x4{v[0], v[1], 0u, 0u};
-      }
-    }
-    d = *(const f32x4*)(p.bs + (int64_t)brow * p.ld_bs + (int64_t)kc * 4);
-  };
-
-  if (kc0 < kc1) load(kc0, a_cur, s_cur, b_cur, d_cur);
-  for (int kc = kc0; kc < kc1; ++kc) {
-    if (kc + 1 < kc1) load(kc + 1, a_nxt, s_nxt, b_nxt, d_nxt);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 bb;
-      if (PASS == PASS_DOWN) bb = __builtin_bit_cast(bf16x8, b_cur[j]);
-      else bb = i8x8_to_bf16x8(u32x2{b_cur[j][0], b_cur[j][1]});
-#pragma unroll
-      for (int g = 0; g < RGW; ++g) {
-        const float sc = e8m0_to_f32((s_cur[g] >> (8 * j)) & 0xFFu);
-        const f32x4 r = mfma_block(fp4x8_to_bf16x8(a_cur[g][j], sc), bb);
-        acc[g] += r * d_cur[j];
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < RGW; ++g) {
-      a_cur[g] = a_nxt[g];
-      s_cur[g] = s_nxt[g];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b_cur[j] = b_nxt[j];
-    d_cur = d_nxt;
+  if constexpr (KPW > 0) {
+    wave_project<PASS, RGW, KPW>(p, blob, pr0, wave * KPW, KPW, brow, acc);
+  } else {
+    const int kc0 = wave * p.kc_total / W;
+    const int kc1 = (wave + 1) * p.kc_total / W;
+    wave_project<PASS, RGW, 0>(p, blob, pr0, kc0, kc1 - kc0, brow, acc);
   }
 
   // cross-wave reduction, fixed wave order
@@ -251,15 +312,30 @@ __global__ __launch_bounds__(64) void block_dots_kernel(const uint8_t* __restric
 }
 
 // ------------------------------------------------------------------ host
+// K split: KPW = 4 chunks per wave when K/128 is 8, 16 or 32 (W = 2..8 waves),
+// otherwise a runtime split over W = min(8, K/128) waves.
 template <int PASS, int RGW>
 static void launch_proj(const ProjArgs& a, int tiles, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)tiles * (a.rg_total / RGW));
+  switch (a.kc_total) {
+    case 32:
+      hipLaunchKernelGGL((proj_kernel<PASS, 8, RGW, 4>), dim3(grid), dim3(512), 0, s, a);
+      return;
+    case 16:
+      hipLaunchKernelGGL((proj_kernel<PASS, 4, RGW, 4>), dim3(grid), dim3(256), 0, s, a);
+      return;
+    case 8:
+      hipLaunchKernelGGL((proj_kernel<PASS, 2, RGW, 4>), dim3(grid), dim3(128), 0, s, a);
+      return;
+    default:
+      break;
+  }
   if (a.kc_total >= 8)
-    hipLaunchKernelGGL((proj_kernel<PASS, 8, RGW>), dim3(grid), dim3(8 * 64), 0, s, a);
+    hipLaunchKernelGGL((proj_kernel<PASS, 8, RGW, 0>), dim3(grid), dim3(512), 0, s, a);
   else if (a.kc_total >= 4)
-    hipLaunchKernelGGL((proj_kernel<PASS, 4, RGW>), dim3(grid), dim3(4 * 64), 0, s, a);
+    hipLaunchKernelGGL((proj_kernel<PASS, 4, RGW, 0>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((proj_kernel<PASS, 2, RGW>), dim3(grid), dim3(2 * 64), 0, s, a);
+    hipLaunchKernelGGL((proj_kernel<PASS, 2, RGW, 0>), dim3(grid), dim3(128), 0, s, a);
 }
 
 static int check_layer(const moe_layer_t* L) {
@@ -281,22 +357,6 @@ static int check_layer(const moe_layer_t* L) {
   return MOE_OK;
 }
 
-struct WsLayout {
-  size_t hidden, hidden_scales, partials, total;
-};
-
-static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-static WsLayout ws_layout(const moe_layer_t* L, int rows) {
-  const size_t hrows = (size_t)rows * L->top_k + (L->has_shared ? (size_t)rows : 0);
-  WsLayout w;
-  w.hidden = 0;
-  w.hidden_scales = round256(hrows * L->d_ff * 2);
-  w.partials = w.hidden_scales + round256(hrows * (L->d_ff / kBlock) * 4);
-  w.total = w.partials + round256(hrows * L->d_model * 4);
-  return w;
-}
-
 static int check_acts(const int8_t* q, int64_t ld_q, const float* qs, int64_t ld_qs, int cols,
                       float* y, int64_t ld_y, int ycols) {
   if (!q || !qs || !y) return MOE_ERR_INVALID_ARG;
@@ -307,8 +367,15 @@ static int check_acts(const int8_t* q, int64_t ld_q, const float* qs, int64_t ld
   return MOE_OK;
 }
 
-static int ffn_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
-                   const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
+void launch_combine(const float* P, const int32_t* ids, const float* w, int rows, int top_k,
+                    int has_shared, int d_model, float* y, int64_t ld_y, hipStream_t s) {
+  const int64_t threads = (int64_t)rows * (d_model / 4);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, P,
+                     ids, w, rows, top_k, has_shared, d_model, y, ld_y);
+}
+
+static int ffn_run(const moe_layer_t* L, int stages, const int8_t* q,
+                   int64_t ld_q, const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                    const float* w, const int32_t* offsets, const int32_t* sorted, float* y,
                    int64_t ld_y, void* ws, hipStream_t s) {
   const WsLayout lay = ws_layout(L, rows);
@@ -346,7 +413,7 @@ static int ffn_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld
     g.ld_hs = L->d_ff / kBlock;
     launch_proj<PASS_GATEUP, 4>(g, tiles, s);
   }
-  // down projection -> per-slot partials
+  // down projection -> per-slot partials -> fixed-order combine into y
   if (stages & MOE_STAGE_DOWN) {
     const PackedDims pd(L->d_model, L->d_ff);
     ProjArgs d = a;
@@ -364,20 +431,17 @@ static int ffn_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld
     d.y = (float*)(base + lay.partials);
     d.ld_y = L->d_model;
     launch_proj<PASS_DOWN, 4>(d, tiles, s);
-  }
-  if (stages & MOE_STAGE_COMBINE) {
-    const int64_t threads = (int64_t)rows * (L->d_model / 4);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       (const float*)(base + lay.partials), ids, w, rows, L->top_k,
-                       L->has_shared, L->d_model, y, ld_y);
+    launch_combine((const float*)(base + lay.partials), ids, w, rows, L->top_k, L->has_shared,
+                   L->d_model, y, ld_y, s);
   }
   return launch_status();
 }
 
-static int ffn_entry(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
-                     const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
+static int ffn_entry(const moe_layer_t* L, bool decode, int stages, const int8_t* q,
+                     int64_t ld_q, const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                      const float* w, const int32_t* offsets, const int32_t* sorted, float* y,
-                     int64_t ld_y, void* ws, size_t ws_bytes, void* stream, int max_rows) {
+                     int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
+  const int max_rows = decode ? MOE_MAX_DECODE_ROWS : kMaxPrefillRows;
   if (stages <= 0 || stages > MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
   int rc = check_layer(L);
   if (rc != MOE_OK) return rc;
@@ -389,6 +453,10 @@ static int ffn_entry(const moe_layer_t* L, int stages, const int8_t* q, int64_t 
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
   if (ws_bytes < ws_layout(L, rows).total) return MOE_ERR_WORKSPACE;
   if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
+  // the prefill GEMM works in 256-row weight blocks; other shapes use the tiles
+  if (!decode && L->d_model % 256 == 0 && (2 * L->d_ff) % 256 == 0)
+    return prefill_run(L, stages, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y, ws,
+                       (hipStream_t)stream);
   return ffn_run(L, stages, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y, ws,
                  (hipStream_t)stream);
 }
@@ -418,8 +486,8 @@ extern "C" int moe_ffn_decode(const moe_layer_t* L, const int8_t* q, int64_t ld_
                               const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                               const float* w, const int32_t* offsets, const int32_t* sorted,
                               float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
-  return ffn_entry(L, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y,
-                   ld_y, ws, ws_bytes, stream, MOE_MAX_DECODE_ROWS);
+  return ffn_entry(L, true, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y,
+                   ld_y, ws, ws_bytes, stream);
 }
 
 extern "C" int moe_matvec_mxfp4(const void* w_packed, int n_out, int d_in, const int8_t* q,
@@ -449,8 +517,7 @@ extern "C" int moe_matvec_mxfp4(const void* w_packed, int n_out, int d_in, const
   a.ld_y = ld_y;
   hipStream_t s = (hipStream_t)stream;
   if (pd.rg % 2 == 0) launch_proj<PASS_MATVEC, 2>(a, 1, s);
-  else hipLaunchKernelGGL((proj_kernel<PASS_MATVEC, 8, 1>), dim3((unsigned)pd.rg), dim3(512), 0,
-                          s, a);
+  else launch_proj<PASS_MATVEC, 1>(a, 1, s);
   return launch_status();
 }
 
@@ -470,14 +537,13 @@ extern "C" int moe_debug_block_dots(const void* w_packed, int n_out, int d_in, c
   return launch_status();
 }
 
-// Prefill shares the tile machinery with decode; tiles of 16 columns walk
-// each expert's token list.
+// Prefill runs the grouped matrix-core GEMM (prefill.hip).
 extern "C" int moe_ffn_prefill(const moe_layer_t* L, const int8_t* q, int64_t ld_q,
                                const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                                const float* w, const int32_t* offsets, const int32_t* sorted,
                                float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
-  return ffn_entry(L, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y,
-                   ld_y, ws, ws_bytes, stream, kMaxPrefillRows);
+  return ffn_entry(L, false, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted,
+                   y, ld_y, ws, ws_bytes, stream);
 }
 
 extern "C" int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask,
@@ -486,6 +552,6 @@ extern "C" int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask,
                               const int32_t* offsets, const int32_t* sorted, float* y,
                               int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
   if (prefill != 0 && prefill != 1) return MOE_ERR_INVALID_ARG;
-  return ffn_entry(L, stage_mask, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y,
-                   ws, ws_bytes, stream, prefill ? kMaxPrefillRows : MOE_MAX_DECODE_ROWS);
+  return ffn_entry(L, prefill == 0, stage_mask, q, ld_q, qs, ld_qs, rows, ids, w, offsets,
+                   sorted, y, ld_y, ws, ws_bytes, stream);
 }

@@ -1,0 +1,45 @@
+// ffn_internal.h -- workspace layout and the prefill entry shared by ffn.hip and
+// prefill.hip.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Workspace regions (each 256-byte aligned), for A' = rows*top_k (+ rows when
+// a shared expert is present) hidden rows:
+//   hidden        bf16 [A'][d_ff]      requantised intermediate codes
+//   hidden_scales f32  [A'][d_ff/32]
+//   partials      f32  [A'][d_model]   per-slot down projections
+//   act           bf16 [A'][d_model]   prefill: activation codes gathered per
+//                                      hidden row (tile order), exact in bf16
+//   act_scales    f32  [A'][d_model/32]
+struct WsLayout {
+  size_t hidden, hidden_scales, partials, act, act_scales, total;
+};
+
+inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(const moe_layer_t* L, int rows) {
+  const size_t hrows = (size_t)rows * L->top_k + (L->has_shared ? (size_t)rows : 0);
+  WsLayout w;
+  w.hidden = 0;
+  w.hidden_scales = round256(hrows * L->d_ff * 2);
+  w.partials = w.hidden_scales + round256(hrows * (L->d_ff / kBlock) * 4);
+  w.act = w.partials + round256(hrows * L->d_model * 4);
+  w.act_scales = w.act + round256(hrows * L->d_model * 2);
+  w.total = w.act_scales + round256(hrows * (L->d_model / kBlock) * 4);
+  return w;
+}
+
+// y = weighted combine of the partials (slot order, shared expert last)
+void launch_combine(const float* P, const int32_t* ids, const float* w, int rows, int top_k,
+                    int has_shared, int d_model, float* y, int64_t ld_y, hipStream_t s);
+
+// Prefill stages on the grouped matrix-core GEMM (validated arguments).
+int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
+                const float* qs, int64_t ld_qs, int rows, const int32_t* ids, const float* w,
+                const int32_t* offsets, const int32_t* sorted, float* y, int64_t ld_y,
+                void* ws, hipStream_t s);
+
+}  // namespace moe

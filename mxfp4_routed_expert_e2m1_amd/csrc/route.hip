@@ -23,15 +23,11 @@ constexpr int kMaxExperts = 512;  // keeps the grouping LDS under 64 KiB
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 
+// One wave: top_k picks of one row; lane s < top_k receives slot s.
 template <int PER_LANE>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
-                                                         int64_t ld_l, int rows, int n_experts,
-                                                         int top_k, int32_t* __restrict__ ids,
-                                                         float* __restrict__ w) {
-  const int row = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6);
-  if (row >= rows) return;  // whole wave exits together
+__device__ inline void topk_row(const float* __restrict__ l, int n_experts, int top_k,
+                                int* my_id, float* my_w) {
   const int lane = lane_id();
-  const float* l = logits + (int64_t)row * ld_l;
   float v[PER_LANE];
 #pragma unroll
   for (int j = 0; j < PER_LANE; ++j) {
@@ -40,8 +36,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
   uint32_t taken = 0;
   float my_sig = 0.f;
-  int my_id = 0;
   float sum = 0.f;
+  *my_id = 0;
   for (int s = 0; s < top_k; ++s) {
     float bv = -INFINITY;
     int be = 0x7fffffff;
@@ -68,31 +64,64 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     sum += sg;
     if (lane == s) {
       my_sig = sg;
-      my_id = be;
+      *my_id = be;
     }
   }
+  *my_w = my_sig / sum;
+}
+
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int64_t ld_l, int rows, int n_experts,
+                                                         int top_k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+  const int row = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  if (row >= rows) return;  // whole wave exits together
+  int id;
+  float wt;
+  topk_row<PER_LANE>(logits + (int64_t)row * ld_l, n_experts, top_k, &id, &wt);
+  const int lane = lane_id();
   if (lane < top_k) {
-    ids[(int64_t)row * top_k + lane] = my_id;
-    w[(int64_t)row * top_k + lane] = my_sig / sum;
+    ids[(int64_t)row * top_k + lane] = id;
+    w[(int64_t)row * top_k + lane] = wt;
   }
 }
 
-__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids,
-                                                              int n_assign, int n_experts,
-                                                              int32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ sorted) {
+// Grouping of ids (global, or LDS when FUSED: then the first `rows` waves
+// first compute the top-k of one row each, for rows <= kGroupWaves).
+constexpr int kFusedMaxAssign = kGroupWaves * MOE_MAX_TOP_K;
+
+template <bool FUSED, int PER_LANE>
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(
+    const float* __restrict__ logits, int64_t ld_l, int rows, int top_k,
+    int32_t* __restrict__ ids_g, float* __restrict__ w_g, int n_assign, int n_experts,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
   __shared__ int hist[kMaxExperts];
   __shared__ int running[kMaxExperts];
   __shared__ int wave_tot[kGroupWaves];
+  __shared__ int ids_l[FUSED ? kFusedMaxAssign : 1];
   extern __shared__ int wcnt[];  // [kGroupWaves][n_experts]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (FUSED) {
+    if (wave < rows) {
+      int id;
+      float wt;
+      topk_row<PER_LANE>(logits + (int64_t)wave * ld_l, n_experts, top_k, &id, &wt);
+      if (lane < top_k) {
+        ids_g[wave * top_k + lane] = id;
+        w_g[wave * top_k + lane] = wt;
+        ids_l[wave * top_k + lane] = id;
+      }
+    }
+    __syncthreads();
+  }
+  auto id_at = [&](int a) -> int { return FUSED ? ids_l[a] : ids_g[a]; };
 
   for (int e = tid; e < n_experts; e += kGroupThreads) hist[e] = 0;
   for (int e = tid; e < kGroupWaves * n_experts; e += kGroupThreads) wcnt[e] = 0;
   __syncthreads();
   for (int a = tid; a < n_assign; a += kGroupThreads) {
-    const int e = ids[a];
+    const int e = id_at(a);
     if (e >= 0) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
@@ -120,7 +149,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
   while ((1 << nbits) < n_experts) ++nbits;
   for (int chunk = 0; chunk < n_assign; chunk += kGroupThreads) {
     const int a = chunk + tid;
-    const int e = (a < n_assign) ? ids[a] : -1;
+    const int e = (a < n_assign) ? id_at(a) : -1;
     const bool valid = e >= 0;
     uint64_t same = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -167,8 +196,20 @@ extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int 
     return MOE_ERR_ALIGNMENT;
   if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
   hipStream_t s = (hipStream_t)stream;
+  const int per_lane = (n_experts + 63) / 64;
+  const size_t lds = sizeof(int) * (size_t)kGroupWaves * (size_t)n_experts;
+  const int n_assign = rows * top_k;
+  if (rows > 0 && rows <= kGroupWaves) {
+    // decode-sized: top-k and grouping in one workgroup, one launch
+    if (per_lane <= 4)
+      hipLaunchKernelGGL((group_kernel<true, 4>), dim3(1), dim3(kGroupThreads), lds, s, logits,
+                         ld_l, rows, top_k, ids, w, n_assign, n_experts, counts, offsets, sorted);
+    else
+      hipLaunchKernelGGL((group_kernel<true, 8>), dim3(1), dim3(kGroupThreads), lds, s, logits,
+                         ld_l, rows, top_k, ids, w, n_assign, n_experts, counts, offsets, sorted);
+    return launch_status();
+  }
   if (rows > 0) {
-    const int per_lane = (n_experts + 63) / 64;
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     if (per_lane <= 4)
       hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, ld_l, rows, n_experts,
@@ -177,8 +218,7 @@ extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int 
       hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, ld_l, rows,
                          n_experts, top_k, ids, w);
   }
-  const size_t lds = sizeof(int) * (size_t)kGroupWaves * (size_t)n_experts;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds, s, ids, rows * top_k,
-                     n_experts, counts, offsets, sorted);
+  hipLaunchKernelGGL((group_kernel<false, 4>), dim3(1), dim3(kGroupThreads), lds, s, logits,
+                     ld_l, rows, top_k, ids, w, n_assign, n_experts, counts, offsets, sorted);
   return launch_status();
 }
