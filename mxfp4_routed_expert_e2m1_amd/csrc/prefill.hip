@@ -5,21 +5,23 @@
 // and (§7.1 item 8) sorts assignments into per-expert row blocks so an expert
 // with ~48 rows scans its packed weights once.  Here a workgroup owns one
 // tile of up to 128 token rows of one expert (rows grouped by
-// moe_route_group) and 128 weight rows, so each expert's weights are streamed
+// moe_route_group) and 256 weight rows, so each expert's weights are streamed
 // once per 128 tokens.  The contraction runs on the bf16 matrix core with the
 // same exact per-block scheme as decode (E2M1 x E8M0 folded into bf16 by the
 // FP4 converter, int8 codes exact in bf16, one 16x16x32 op per 32-element
 // block, fp32 FMA with the activation scale).
 //
 //   * A prep kernel gathers every hidden row's activation codes once into
-//     bf16 rows in tile order (so the GEMM's token tiles are contiguous).
-//   * Four waves: 2 (row halves of 64) x 2 (token halves, token groups
-//     interleaved for balance); wave tile = 4 row groups x 4 token groups.
-//   * Token tiles are double-buffered in LDS (128 x 128 bf16 per K chunk,
-//     rows padded by 16 bytes against bank conflicts); weights stream from
-//     HBM straight into the A fragments with one chunk of register prefetch.
-//   * Block ids are remapped so the 2F/128 (or D/128) workgroups that share a
-//     token tile run on the same XCD and share its L2.
+//     bf16 rows in tile order (so a tile's token rows are contiguous).
+//   * A workgroup owns 128 token rows x 256 weight rows; 8 waves = 4 row
+//     quarters x 2 token halves (token groups interleaved for balance); wave
+//     tile = 4 row groups x up to 4 token groups, the live count being a
+//     template parameter so the inner loop is branch-free.
+//   * Weights, scales, token fragments and activation scales stream through
+//     a 3-stage LDS ring filled by direct global->LDS loads (no registers),
+//     each piece in the lane order its reader uses.
+//   * Block ids are remapped so the workgroups that share a token tile run on
+//     the same XCD and share its L2.
 //   * Gate/up epilogue: SwiGLU + group-32 requant in registers (a wave holds
 //     gate and up of the same 32 features); down epilogue: fp32 partials.
 #include "ffn_internal.h"
@@ -266,12 +268,15 @@ template <int PASS>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs p) {
   __shared__ Stage ring[kStages];
 
+  // Block b runs on XCD b % 8 (round-robin dispatch).  XCD x walks tiles
+  // x, x+8, x+16, ... and all weight-row blocks of a tile back to back, so the
+  // workgroups sharing a token tile share that XCD's L2, and the live tiles
+  // (the low ids) spread over all eight XCDs.
   const int n_nb = p.rg_total / kBNGroups;
-  const int per_xcd = (int)((gridDim.x + 7) / 8);
-  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (logical >= p.n_items) return;
-  const int tile_idx = logical / n_nb;
-  const int nb = logical % n_nb;
+  const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
+  const int tile_idx = (slot / n_nb) * 8 + xcd;
+  const int nb = slot % n_nb;
+  if (tile_idx * n_nb >= p.n_items) return;
   int n_tiles;
   GemmCtx c;
   c.t = find_tile<kBM>(p.offsets, p.n_experts, p.has_shared, p.rows, tile_idx, &n_tiles);
@@ -342,7 +347,7 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     g.ld_h = L->d_ff;
     g.ld_hs = L->d_ff / kBlock;
     g.n_items = tiles * (g.rg_total / kBNGroups);
-    const unsigned grid = (unsigned)((g.n_items + 7) / 8 * 8);
+    const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
     hipLaunchKernelGGL(gemm_kernel<GEMM_GATEUP>, dim3(grid), dim3(kGemmThreads), 0, s, g);
   }
   if (stages & MOE_STAGE_DOWN) {
@@ -362,7 +367,7 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     d.y = (float*)(base + lay.partials);
     d.ld_y = L->d_model;
     d.n_items = tiles * (d.rg_total / kBNGroups);
-    const unsigned grid = (unsigned)((d.n_items + 7) / 8 * 8);
+    const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (d.rg_total / kBNGroups));
     hipLaunchKernelGGL(gemm_kernel<GEMM_DOWN>, dim3(grid), dim3(kGemmThreads), 0, s, d);
     launch_combine((const float*)(base + lay.partials), ids, w, rows, L->top_k, L->has_shared,
                    L->d_model, y, ld_y, s);
