@@ -106,7 +106,7 @@ def main():
                  torch.empty(L.n_experts + 1, dtype=torch.int32, device=dev),
                  torch.empty(T * L.top_k, dtype=torch.int32, device=dev))
     y = torch.empty((T, L.d_model), dtype=torch.float32, device=dev)
-    ws = torch.empty(m.moe_ffn_workspace_bytes(layers[0], T), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(m.moe_ffn_workspace_bytes(layers[0], T), dtype=torch.uint8, device=dev)
     ffn = m.moe_ffn_prefill if prefill else m.moe_ffn_decode
 
     def step(i):
@@ -165,12 +165,19 @@ def main():
     mean_touched = float(np.mean(touched))
     step_bytes = mean_touched * (gu_bytes + dn_bytes) + act_bytes + T * L.d_model * 4
 
-    # dominant kernel: the gate/up stage alone over the rotated sets, in a graph
+    # dominant kernel, alone over the rotated sets in a graph: decode = the
+    # single-launch layer kernel when moe_ffn_decode uses it (8+ rows), else
+    # the gate/up projection kernel; prefill = the gate/up GEMM stage
     ids, w, counts, offsets, srt = route_out   # routes of input `last`
     n_k = sets * max(1, 64 // sets)
-    g_k = capture(torch, lambda: [m.moe_ffn_stages(layers[i % sets], int(prefill),
-                                                   m.MOE_STAGE_GATE_UP, q, qs, ids, w,
-                                                   offsets, srt, y, ws) for i in range(n_k)])
+    single = (not prefill) and m.moe_ffn_decode_single_launch(layers[0], T)
+    if single:
+        kcall = lambda i: m.moe_ffn_decode(layers[i % sets], q, qs, ids, w, offsets, srt, y=y,
+                                           ws=ws)
+    else:
+        kcall = lambda i: m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
+                                           q, qs, ids, w, offsets, srt, y, ws)
+    g_k = capture(torch, lambda: [kcall(i) for i in range(n_k)])
     g_k.replay()
     torch.cuda.synchronize()
     kreps = max(2, (200 if prefill else 2000) // n_k)
@@ -181,22 +188,33 @@ def main():
     torch.cuda.synchronize()
     k_us = ev0.elapsed_time(ev1) * 1e3 / (kreps * n_k)
     last_touched = touched[last % n_inputs]
-    hidden_bytes = A * (L.d_ff + L.d_ff // 32 * 4)
-    k_bytes = last_touched * gu_bytes + T * (L.d_model + L.d_model // 8) + hidden_bytes
     if prefill:
         k_flops = 2.0 * A * (2 * L.d_ff) * L.d_model
         achieved = k_flops / (k_us * 1e-6) / 1e12
+        hidden_bytes = A * (L.d_ff + L.d_ff // 32 * 4)
+        k_bytes = last_touched * gu_bytes + T * (L.d_model + L.d_model // 8) + hidden_bytes
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                    traffic=None, kernel="proj_kernel<gate/up>", avg_us=round(k_us, 3),
+                    traffic=None, kernel="gemm_kernel<gate/up>", avg_us=round(k_us, 3),
                     i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
                     hbm_gbs=round(k_bytes / (k_us * 1e-6) / 1e9, 1))
     else:
+        if single:
+            # algorithmic bytes: every touched expert's gate/up + down once, the
+            # activation codes and scales read, y written
+            k_bytes = (last_touched * (gu_bytes + dn_bytes) + T * (L.d_model + L.d_model // 8)
+                       + T * L.d_model * 4)
+            kname = "fused_decode_kernel"
+        else:
+            # gate/up weights of the touched experts, activations, hidden codes out
+            k_bytes = (last_touched * gu_bytes + T * (L.d_model + L.d_model // 8)
+                       + A * (L.d_ff + L.d_ff // 32 * 4))
+            kname = "proj_kernel<gate/up>"
         achieved = k_bytes / (k_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="proj_kernel<gate/up>", avg_us=round(k_us, 3),
-                    bytes_per_launch=int(k_bytes))
+                    kernel=kname, avg_us=round(k_us, 3),
+                    bytes_per_launch=int(k_bytes), experts_touched=last_touched)
 
     cpu = None
     if not args.no_cpu_baseline:

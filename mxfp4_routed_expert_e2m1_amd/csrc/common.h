@@ -120,59 +120,83 @@ struct Tile {
   int count;   // 1..TM columns
 };
 
-// Every lane of the calling wave gets the same answer.  One memory round trip:
-// each lane loads the offsets of its (up to 8) experts at once, then a wave
-// scan of per-lane tile counts locates the tile.  *n_tiles receives the total
-// number of tiles of the call (routed + shared).  Tiles hold up to TM columns.
+// The offsets of the call, spread over the lanes of a wave: each lane holds
+// the offsets of its (up to 8) experts and a wave scan of per-lane tile
+// counts.  Loading it is the only memory round trip; lookups are register and
+// shuffle work, so a persistent workgroup loads it once.  Tiles hold up to TM
+// columns.
+template <int TM = 16>
+struct TileMap {
+  int o[9];    // offsets[e0 .. e0+8] of this lane's experts
+  int nt[8];   // tiles of each of them
+  int e0;      // first expert of this lane
+  int lsum;    // tiles of this lane
+  int incl;    // inclusive scan of lsum over the wave
+  int routed;  // routed tiles in total
+  int shared_tiles;
+
+  __device__ inline void load(const int32_t* __restrict__ offsets, int n_experts, int has_shared,
+                              int rows) {
+    const int per = (n_experts + 63) >> 6;  // <= 8 (n_experts <= 512)
+    e0 = lane_id() * per;
+#pragma unroll
+    for (int i = 0; i <= 8; ++i) o[i] = (i <= per && e0 + i <= n_experts) ? offsets[e0 + i] : 0;
+    lsum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = (i < per && e0 + i < n_experts) ? o[i + 1] - o[i] : 0;
+      nt[i] = (c + TM - 1) / TM;
+      lsum += nt[i];
+    }
+    incl = wave_incl_scan(lsum);
+    routed = __shfl(incl, 63, 64);
+    shared_tiles = has_shared ? (rows + TM - 1) / TM : 0;
+  }
+
+  __device__ inline int n_tiles() const { return routed + shared_tiles; }
+
+  // Every lane of the calling wave gets the same answer.
+  __device__ inline Tile lookup(int n_experts, int rows, int tile) const {
+    Tile t{-1, 0, 0};
+    if (tile < routed) {
+      int rem = tile - (incl - lsum);
+      int se = -1, ss = 0, sc = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (se < 0) {
+          if (rem < nt[i]) {
+            se = e0 + i;
+            ss = o[i] + rem * TM;
+            sc = min(TM, o[i + 1] - o[i] - rem * TM);
+          } else {
+            rem -= nt[i];
+          }
+        }
+      }
+      const uint64_t m = __ballot(incl > tile);
+      const int L = __ffsll((unsigned long long)m) - 1;
+      t.expert = __shfl(se, L, 64);
+      t.start = __shfl(ss, L, 64);
+      t.count = __shfl(sc, L, 64);
+    } else if (tile - routed < shared_tiles) {
+      const int st = tile - routed;
+      t.expert = n_experts;
+      t.start = st * TM;
+      t.count = min(TM, rows - st * TM);
+    }
+    return t;
+  }
+};
+
+// One-shot lookup; *n_tiles receives the total number of tiles of the call
+// (routed + shared).
 template <int TM = 16>
 __device__ inline Tile find_tile(const int32_t* __restrict__ offsets, int n_experts,
                                  int has_shared, int rows, int tile, int* n_tiles) {
-  const int lane = lane_id();
-  const int per = (n_experts + 63) >> 6;  // <= 8 (n_experts <= 512)
-  const int e0 = lane * per;
-  int o[9];
-#pragma unroll
-  for (int i = 0; i <= 8; ++i) o[i] = (i <= per && e0 + i <= n_experts) ? offsets[e0 + i] : 0;
-  int nt[8];
-  int lsum = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = (i < per && e0 + i < n_experts) ? o[i + 1] - o[i] : 0;
-    nt[i] = (c + TM - 1) / TM;
-    lsum += nt[i];
-  }
-  const int incl = wave_incl_scan(lsum);
-  const int routed = __shfl(incl, 63, 64);
-  const int shared_tiles = has_shared ? (rows + TM - 1) / TM : 0;
-  *n_tiles = routed + shared_tiles;
-  Tile t{-1, 0, 0};
-  if (tile < routed) {
-    int rem = tile - (incl - lsum);
-    int se = -1, ss = 0, sc = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (se < 0) {
-        if (rem < nt[i]) {
-          se = e0 + i;
-          ss = o[i] + rem * TM;
-          sc = min(TM, o[i + 1] - o[i] - rem * TM);
-        } else {
-          rem -= nt[i];
-        }
-      }
-    }
-    const uint64_t m = __ballot(incl > tile);
-    const int L = __ffsll((unsigned long long)m) - 1;
-    t.expert = __shfl(se, L, 64);
-    t.start = __shfl(ss, L, 64);
-    t.count = __shfl(sc, L, 64);
-  } else if (tile - routed < shared_tiles) {
-    const int st = tile - routed;
-    t.expert = n_experts;
-    t.start = st * TM;
-    t.count = min(TM, rows - st * TM);
-  }
-  return t;
+  TileMap<TM> m;
+  m.load(offsets, n_experts, has_shared, rows);
+  *n_tiles = m.n_tiles();
+  return m.lookup(n_experts, rows, tile);
 }
 
 // ------------------------------------------------------------ host side

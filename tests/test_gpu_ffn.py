@@ -66,11 +66,18 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
         offsets = torch.from_numpy(off_o).to(DEV)
         srt = torch.from_numpy(srt_o).to(DEV)
     yw = torch.full((T, L.d_model + pad_y), 3.0, device=DEV)
-    ws = torch.empty(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
-    y = getattr(m, entry)(layer, q, qs, ids, w, offsets, srt, y=yw[:, : L.d_model], ws=ws)
+    ws = torch.zeros(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
+    if entry == "stages":  # decode through the separate gate/up, down, combine kernels
+        y = m.moe_ffn_stages(layer, 0, m.MOE_STAGE_ALL, q, qs, ids, w, offsets, srt,
+                             yw[:, : L.d_model], ws)
+    else:
+        y = getattr(m, entry)(layer, q, qs, ids, w, offsets, srt, y=yw[:, : L.d_model], ws=ws)
     torch.cuda.synchronize()
     if pad_y:
         assert torch.all(yw[:, L.d_model:] == 3.0)
+    off_h, off_hs, _ = m.moe_ffn_workspace_layout(layer, T)
+    # the decode kernel's queue/counter words are back to zero, no wait expired
+    assert not torch.any(ws[:off_h]), "workspace counters not reset"
 
     rows = np.arange(T) if sample is None else np.asarray(sample)
     need = set(int(e) for e in ids_o[rows].reshape(-1) if e >= 0)
@@ -82,7 +89,6 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
                           w_o[rows], want_intermediates=True)
 
     # stage 3: requantised intermediate read back from the documented workspace
-    off_h, off_hs, _ = m.moe_ffn_workspace_layout(layer, T)
     A = T * k
     n_h = A + (T if L.has_shared else 0)
     hb = ws[off_h: off_h + n_h * L.d_ff * 2].view(torch.bfloat16).view(n_h, L.d_ff)
@@ -166,9 +172,9 @@ def test_decode_deterministic_and_padded():
     assert torch.equal(r1["y"], r2["y"])
 
 
-def test_decode_sentinel_routes():
+@pytest.mark.parametrize("T", [6, 12])
+def test_decode_sentinel_routes(T):
     c = synth.DECODE_BATCH
-    T = 6
     x = synth.activations(c["seed"], 7, T, DSV4.d_model)
     lg = synth.router_logits(c["seed"], 7, T, DSV4.n_experts)
     ids_o, _ = oracle.route(lg, DSV4.top_k)
@@ -191,12 +197,13 @@ def test_prefill_sampled(rows):
     print(f"prefill {rows}: worst err/tol {r['worst']:.3f}, flips {r['flips']}")
 
 
-def test_decode_graph_replays_match_eager():
+@pytest.mark.parametrize("T", [4, 12])
+def test_decode_graph_replays_match_eager(T):
     # quant + route/group + FFN captured in one HIP graph; every replay, with
     # other eager work and synchronisations in between, equals the eager result
+    # (4 rows: three kernels; 12 rows: the single-launch kernel)
     c = synth.DECODE_BATCH
     layer = layer_for(DSV4, c["seed"])
-    T = 4
     x = torch.from_numpy(synth.activations(c["seed"], 50, T, DSV4.d_model)).to(DEV)
     lg = torch.from_numpy(synth.router_logits(c["seed"], 50, T, DSV4.n_experts)).to(DEV)
     q = torch.empty((T, DSV4.d_model), dtype=torch.int8, device=DEV)
@@ -207,7 +214,7 @@ def test_decode_graph_replays_match_eager():
           torch.empty(257, dtype=torch.int32, device=DEV),
           torch.empty(T * 6, dtype=torch.int32, device=DEV))
     y = torch.empty((T, DSV4.d_model), device=DEV)
-    ws = torch.empty(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
 
     def step():
         m.moe_quant_act_q8(x, q=q, scales=qs)
@@ -239,3 +246,66 @@ def test_decode_graph_replays_match_eager():
                                  *m.moe_route_group(lg, 6)[3:])
         torch.cuda.synchronize()
         assert torch.isfinite(other).all()
+
+
+# Shapes that take the single-launch decode kernel with other K splits than
+# the DS-V4 layer (gate/up chunks per wave x down chunks per wave: 2x2, 2x4,
+# 8x2), against the oracle and against the separate-kernel path; the last one
+# (d_ff 1024) takes the separate kernels in both calls.
+FUSED_SHAPES = [
+    synth.Layer(n_experts=16, top_k=4, d_model=2048, d_ff=2048, has_shared=True),
+    synth.Layer(n_experts=32, top_k=8, d_model=2048, d_ff=4096, has_shared=False),
+    synth.Layer(n_experts=8, top_k=2, d_model=8192, d_ff=2048, has_shared=True),
+    synth.Layer(n_experts=16, top_k=4, d_model=1024, d_ff=1024, has_shared=True),
+]
+
+
+@pytest.mark.parametrize("shape", range(len(FUSED_SHAPES)))
+@pytest.mark.parametrize("rows", [8, 11, 16])
+def test_decode_single_launch_shapes(shape, rows):
+    L = FUSED_SHAPES[shape]
+    seed = 11 + shape
+    x = synth.activations(seed, rows, rows, L.d_model)
+    lg = synth.router_logits(seed, rows, rows, L.n_experts, hot_bias=1.0, n_hot=4)
+    r1 = run_case(L, seed, x, lg)
+    r2 = run_case(L, seed, x, lg, entry="stages")
+    print(f"shape {shape} rows {rows}: worst {r1['worst']:.3f} / {r2['worst']:.3f}")
+
+
+def test_decode_single_launch_all_sentinels_gives_zero():
+    # no shared expert and every slot a sentinel: nothing to do, y = 0
+    L = FUSED_SHAPES[1]
+    layer = layer_for(L, 12)
+    T = 9
+    q = torch.ones((T, L.d_model), dtype=torch.int8, device=DEV)
+    qs = torch.ones((T, L.d_model // 32), dtype=torch.float32, device=DEV)
+    ids = torch.full((T, L.top_k), -1, dtype=torch.int32, device=DEV)
+    w = torch.zeros((T, L.top_k), dtype=torch.float32, device=DEV)
+    offsets = torch.zeros(L.n_experts + 1, dtype=torch.int32, device=DEV)
+    srt = torch.full((T * L.top_k,), -1, dtype=torch.int32, device=DEV)
+    y = torch.full((T, L.d_model), 5.0, device=DEV)
+    ws = torch.zeros(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
+    m.moe_ffn_decode(layer, q, qs, ids, w, offsets, srt, y=y, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+    off_h, _, _ = m.moe_ffn_workspace_layout(layer, T)
+    assert not torch.any(ws[:off_h])
+
+
+def test_decode_workspace_reuse_across_row_counts():
+    # one zero-filled workspace serves calls of different row counts in a
+    # row: every result equals that of a fresh workspace, bit for bit
+    c = synth.DECODE_BATCH
+    layer = layer_for(DSV4, c["seed"])
+    ws = torch.zeros(m.moe_ffn_workspace_bytes(layer, 16), dtype=torch.uint8, device=DEV)
+    for j, T in enumerate([16, 3, 9, 1, 16]):
+        x = torch.from_numpy(synth.activations(c["seed"], 300 + j, T, DSV4.d_model)).to(DEV)
+        lg = torch.from_numpy(synth.router_logits(c["seed"], 300 + j, T, DSV4.n_experts)).to(DEV)
+        q, qs = m.moe_quant_act_q8(x)
+        ids, w, counts, offsets, srt = m.moe_route_group(lg, DSV4.top_k)
+        y1 = m.moe_ffn_decode(layer, q, qs, ids, w, offsets, srt, ws=ws)
+        y2 = m.moe_ffn_decode(layer, q, qs, ids, w, offsets, srt)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), f"call {j} (rows {T})"
+    off_h, _, _ = m.moe_ffn_workspace_layout(layer, 16)
+    assert not torch.any(ws[:off_h])
