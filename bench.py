@@ -14,6 +14,8 @@ Workloads (--workload):
                 bias on 16 experts)
   prefill       same layer, --rows 512 or 4096 tokens per step, 2 layer sets
   matvec        MXFP4 matvec 14336x4096, --rows K resident rows, 16 copies
+  copy          calibration only: a plain 1 GiB device-to-device copy (torch),
+                the known-size reference for HBM byte counters
 """
 from __future__ import annotations
 
@@ -38,18 +40,24 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode-batch", "prefill", "matvec"])
+                    choices=["decode", "decode-batch", "prefill", "matvec", "copy"])
     ap.add_argument("--rows", type=int, default=None)
     ap.add_argument("--hot", action="store_true")
     ap.add_argument("--sets", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None)
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step eagerly instead of replaying HIP graphs (for "
+                         "counter profilers that cannot follow graph launches); the timings "
+                         "then include host launch gaps")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    global EAGER
+    EAGER = args.eager
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the routed-expert path here has no "
@@ -70,6 +78,8 @@ def main():
     wl = args.workload
     if wl == "matvec":
         return bench_matvec(args, m, synth, np, torch, dev)
+    if wl == "copy":
+        return bench_copy(args, torch, dev)
 
     L = synth.DSV4_LAYER
     if wl == "decode":
@@ -239,8 +249,23 @@ def main():
     emit(line, args)
 
 
+EAGER = False
+
+
+class _EagerReplay:
+    def __init__(self, fn):
+        self.fn = fn
+
+    def replay(self):
+        self.fn()
+
+
 def capture(torch, fn):
-    """Capture fn's launches (on torch's current stream) into a HIP graph."""
+    """Capture fn's launches (on torch's current stream) into a HIP graph
+    (with --eager: an object whose replay() simply runs fn again)."""
+    if EAGER:
+        fn()
+        return _EagerReplay(fn)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -254,16 +279,15 @@ def capture(torch, fn):
 
 
 def cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload: S
+    fresh rows with the workload's distributions (about 10-15 s of CPU work
+    on 16 threads), quantised, routed, grouped and run through the FFN."""
     import oracle
 
-    S = args.cpu_sample or (8 if prefill else 32)
+    S = args.cpu_sample or 256
     threads = min(16, len(os.sched_getaffinity(0)))
-    x = np.concatenate([synth.activations(seed, i, T, L.d_model) for i in range(4)])[:S]
-    lg = np.concatenate([synth.router_logits(seed, i, T, L.n_experts,
-                                             hot_bias=2.0 if args.hot else 0.0)
-                         for i in range(4)])[:S]
-    S = x.shape[0]
+    x = synth.activations(seed, 1000 + T, S, L.d_model)
+    lg = synth.router_logits(seed, 1000 + T, S, L.n_experts, hot_bias=2.0 if args.hot else 0.0)
     q, qs = oracle.quant_q8(x)
     ids, w = oracle.route(lg, L.top_k)
     need = set(int(e) for e in ids.reshape(-1)) | {L.n_experts}
@@ -278,8 +302,8 @@ def cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill):
     oracle.ffn(ex, L.n_experts, L.top_k, True, qo, qso, ido, wo)
     dt = time.perf_counter() - t0
     return {"value": round(S / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{S} tokens of the same workload (layer set 0): quant, route, group, "
-                      f"FFN in fp64; {dt:.1f}s wall on {threads} threads"}
+            "sample": f"{S} rows drawn like the workload's (layer set 0, {len(need)} experts): "
+                      f"quant, route, group, FFN in fp64; {dt:.1f}s wall on {threads} threads"}
 
 
 def bench_matvec(args, m, synth, np, torch, dev):
@@ -344,6 +368,35 @@ def bench_matvec(args, m, synth, np, torch, dev):
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
                          kernel="proj_kernel<matvec>", avg_us=round(us, 3)),
         "cpu_baseline": cpu,
+    }
+    emit(line, args)
+
+
+def bench_copy(args, torch, dev):
+    """Plain device copy of a known size (1 GiB read + 1 GiB written per launch),
+    rotated over 4 source buffers so no launch reads what the MALL holds."""
+    n = 1 << 30
+    srcs = [torch.full((n // 4,), float(i), dtype=torch.float32, device=dev) for i in range(4)]
+    dst = torch.empty(n // 4, dtype=torch.float32, device=dev)
+    steps = args.steps or 40
+    warmup = args.warmup if args.warmup is not None else 4
+    for i in range(warmup):
+        dst.copy_(srcs[i % 4])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        dst.copy_(srcs[i % 4])
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    line = {
+        "metric": "calibration: device copy", "value": round(2 * n / (us * 1e-6) / 1e9, 1),
+        "unit": "GB/s (read + write)", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "copy 1 GiB -> 1 GiB, 4 rotated sources"},
+        "bytes_read_per_launch": n, "bytes_written_per_launch": n,
     }
     emit(line, args)
 
