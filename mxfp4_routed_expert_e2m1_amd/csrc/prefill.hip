@@ -83,7 +83,7 @@ __device__ inline void load_to_lds(const void* src, void* lds_base, int bytes) {
 // order), then all waves meet at s_barrier; every LDS read of the previous
 // chunk has returned (its data was consumed) before a wave reaches it.  The
 // empty asm statements keep the compiler from moving memory accesses across.
-__device__ inline void lds_barrier() {
+__device__ inline void ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -176,7 +176,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
     } else {
       WAIT_VMCNT(0);
     }
-    lds_barrier();  // every wave's loads of chunk kc have landed; chunk kc-1 is consumed
+    ring_barrier();  // every wave's loads of chunk kc have landed; chunk kc-1 is consumed
     if (kc + 2 < KC) gemm_issue(p, c, ring[(kc + 2) % kStages], kc + 2, wave, lane, b_live);
     if constexpr (NQ > 0) {
       const Stage& S = ring[kc % kStages];
