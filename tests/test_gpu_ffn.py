@@ -309,3 +309,59 @@ def test_decode_workspace_reuse_across_row_counts():
         assert torch.equal(y1, y2), f"call {j} (rows {T})"
     off_h, _, _ = m.moe_ffn_workspace_layout(layer, 16)
     assert not torch.any(ws[:off_h])
+
+
+# Prefill shapes off the DS-V4 path: d_model 384 is not a multiple of 256, so
+# moe_ffn_prefill walks the 16-column decode tiles instead of the grouped GEMM;
+# 1 and 17 rows take the GEMM with nearly empty tiles.
+ODD = synth.Layer(n_experts=16, top_k=4, d_model=384, d_ff=640, has_shared=True)
+
+
+@pytest.mark.parametrize("rows", [1, 17, 100])
+def test_prefill_tile_fallback_shape(rows):
+    seed = 21
+    x = synth.activations(seed, rows, rows, ODD.d_model)
+    lg = synth.router_logits(seed, rows, rows, ODD.n_experts, hot_bias=1.0, n_hot=3)
+    run_case(ODD, seed, x, lg, entry="moe_ffn_prefill")
+
+
+@pytest.mark.parametrize("rows", [1, 17])
+def test_prefill_gemm_small_rows(rows):
+    c = synth.PREFILL
+    x = synth.activations(c["seed"], 7000 + rows, rows, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 7000 + rows, rows, DSV4.n_experts)
+    run_case(DSV4, c["seed"], x, lg, entry="moe_ffn_prefill")
+
+
+def test_prefill_sentinel_routes_sampled():
+    # a prefill chunk whose routes are partly owned elsewhere (-1 sentinels):
+    # whole tokens and single slots dropped, regrouped by the oracle
+    c = synth.PREFILL
+    T = 600
+    x = synth.activations(c["seed"], 600, T, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 600, T, DSV4.n_experts)
+    ids_o, _ = oracle.route(lg, DSV4.top_k)
+    ids_s = ids_o.copy()
+    rng = np.random.default_rng(600)
+    ids_s[rng.random(ids_s.shape) < 0.3] = -1
+    ids_s[5, :] = -1
+    sample = np.array([0, 5, 17, 256, 411, T - 1])
+    run_case(DSV4, c["seed"], x, lg, sample=sample, entry="moe_ffn_prefill", ids_override=ids_s)
+
+
+def test_prefill_stages_match_full_call():
+    # gate/up and down as two moe_ffn_stages calls give the full call's y, bit for bit
+    c = synth.PREFILL
+    layer = layer_for(DSV4, c["seed"])
+    T = 300
+    x = torch.from_numpy(synth.activations(c["seed"], 300, T, DSV4.d_model)).to(DEV)
+    lg = torch.from_numpy(synth.router_logits(c["seed"], 300, T, DSV4.n_experts)).to(DEV)
+    q, qs = m.moe_quant_act_q8(x)
+    ids, w, counts, offsets, srt = m.moe_route_group(lg, DSV4.top_k)
+    y1 = m.moe_ffn_prefill(layer, q, qs, ids, w, offsets, srt)
+    ws = torch.zeros(m.moe_ffn_workspace_bytes(layer, T), dtype=torch.uint8, device=DEV)
+    y2 = torch.empty_like(y1)
+    m.moe_ffn_stages(layer, 1, m.MOE_STAGE_GATE_UP, q, qs, ids, w, offsets, srt, y2, ws)
+    m.moe_ffn_stages(layer, 1, m.MOE_STAGE_DOWN, q, qs, ids, w, offsets, srt, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
