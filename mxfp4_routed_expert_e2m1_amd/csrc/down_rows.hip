@@ -1,0 +1,251 @@
+// down_rows.hip -- down projection + fixed-order combine for one-row decode
+// steps, organised by output rows.
+//
+// One row touches 7 experts (six routed + the shared one) and the down
+// projection's cost is latency: a per-expert kernel has to store fp32
+// partials, and a combine kernel has to read them back.
+// Here a workgroup owns 16 output rows (one packed row group) of every tile.
+// It first copies every hidden row of the step (codes and scales, 4.3 KB per
+// row at d_ff 2048) into LDS with one round of loads; then wave w streams row
+// group `blockIdx.x` of tiles w, w+8, ... (16 K chunks at a time in flight,
+// the first tile's before the copy) against the LDS copy, keeps the 16x16 partial tile in LDS, and when
+// all tiles are done the workgroup adds, for every token and row, the
+// partials of the token's slots in slot order, shared expert last (gfx90a
+// report §8.2: fp32 partials, fixed reduction order) and writes y.  No partials leave the
+// chip and no combine kernel runs.  Same exact block dots as every other
+// projection here (FP4 converter with the E8M0 scale folded in, one 16x16x32
+// bf16 matrix-core op per 32-element block, fp32 FMA with the hidden scale).
+#include "ffn_internal.h"
+
+namespace moe {
+
+constexpr int kDRWaves = 8;
+constexpr int kDRThreads = kDRWaves * 64;
+constexpr int kDRGroup = 16;  // K chunks of a wave in flight at once (16 KiB)
+
+struct DownRowsArgs {
+  const uint8_t* dn;  // routed expert 0 blob
+  int64_t dn_stride;
+  const uint8_t* dn_shared;
+  int64_t nib_bytes;
+  int kc_total, sc_total;
+  const int32_t* offsets;
+  const int32_t* sorted;
+  const int32_t* ids;
+  const float* w;
+  int n_experts, top_k, has_shared, rows;
+  const uint16_t* h;  // hidden codes (bf16 bits) and scales
+  const float* hs;
+  int64_t ld_h, ld_hs;
+  float* y;
+  int64_t ld_y;
+};
+
+// Dynamic LDS: partials [n_tiles][16 columns][16 rows] f32, then the hidden
+// rows of the step [R][d_ff] bf16 and their scales [R][d_ff/32] f32, R =
+// valid routed assignments + shared rows (row r < n_valid is sorted position
+// r, row n_valid + t the shared expert's row of token t).
+__global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p, int tiles_cap) {
+  extern __shared__ __align__(16) float dyn[];
+  float* part = dyn;
+  __shared__ int4 s_tiles[kMaxDecodeTiles];  // expert, start, count
+  __shared__ int s_pos[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // assignment -> sorted position
+  __shared__ int s_ptile[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // sorted position -> tile
+  __shared__ int s_ntiles, s_routed;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  if (wave == 0) {
+    TileMap<16> tm;
+    tm.load(p.offsets, p.n_experts, p.has_shared, p.rows);
+    int idx = tm.incl - tm.lsum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      for (int r = 0; r < tm.nt[i] && idx < kMaxDecodeTiles; ++r, ++idx) {
+        const int start = tm.o[i] + 16 * r;
+        const int cnt = min(16, tm.o[i + 1] - tm.o[i] - 16 * r);
+        s_tiles[idx] = int4{tm.e0 + i, start, cnt, 0};
+        for (int c = 0; c < cnt; ++c) s_ptile[start + c] = idx;
+      }
+    const int st = tm.routed + lane;
+    if (lane < tm.shared_tiles && st < kMaxDecodeTiles)
+      s_tiles[st] = int4{p.n_experts, 16 * lane, min(16, p.rows - 16 * lane), 0};
+    if (lane == 0) {
+      s_ntiles = min(tm.n_tiles(), kMaxDecodeTiles);
+      s_routed = tm.routed;
+    }
+  }
+  const int n_valid = p.offsets[p.n_experts];
+  for (int i = tid; i < n_valid; i += kDRThreads) s_pos[p.sorted[i]] = i;
+  __syncthreads();
+  const int n_tiles = s_ntiles;
+  const int F = p.kc_total * kChunkK;
+  const int rg = blockIdx.x;  // 16 output rows 16*rg .. 16*rg+15
+  const int col = lane & 15, g8 = 8 * (lane >> 4);
+
+  // this wave's weight stream: row group rg of tile ti, K chunks kg..kg+15
+  u32x4 a[kDRGroup];
+  uint32_t s[kDRGroup];
+  auto issue = [&](int ti, int kg) {
+    const int4 te = s_tiles[ti];
+    const uint8_t* blob = te.x == p.n_experts ? p.dn_shared : p.dn + (int64_t)te.x * p.dn_stride;
+    const u32x4* nib = (const u32x4*)blob;
+    const uint8_t* scl = blob + p.nib_bytes;
+    const int n_in = min(kDRGroup, p.kc_total - kg);
+#pragma unroll
+    for (int kk = 0; kk < kDRGroup; ++kk) {
+      if (kk < n_in) {
+        const int kc = kg + kk;
+        a[kk] = nib[((int64_t)rg * p.kc_total + kc) * 64 + lane];
+        s[kk] = *(const uint32_t*)(scl + (((int64_t)rg * p.sc_total + (kc >> 2)) * 16 + col) * 16 +
+                                   (kc & 3) * 4);
+      }
+    }
+  };
+  // the first tile's weights go out before the hidden rows are copied, so
+  // both arrive in one round trip
+  if (wave < n_tiles) issue(wave, 0);
+
+  // hidden rows -> LDS (16-byte pieces)
+  const int R = n_valid + (p.has_shared ? p.rows : 0);
+  uint16_t* hl = (uint16_t*)(part + (size_t)tiles_cap * 256);
+  float* hsl = (float*)(hl + (size_t)R * F);
+  {
+    const int per_row = F / 8;  // 16-byte pieces of codes per row
+    for (int e = tid; e < R * per_row; e += kDRThreads) {
+      const int r = e / per_row, c = e % per_row;
+      const int64_t src = r < n_valid ? r : (int64_t)p.rows * p.top_k + (r - n_valid);
+      *(u32x4*)(hl + (size_t)r * F + c * 8) = *(const u32x4*)(p.h + src * p.ld_h + c * 8);
+    }
+    const int per_row_s = F / kBlock / 4;  // 16-byte pieces of scales per row
+    for (int e = tid; e < R * per_row_s; e += kDRThreads) {
+      const int r = e / per_row_s, c = e % per_row_s;
+      const int64_t src = r < n_valid ? r : (int64_t)p.rows * p.top_k + (r - n_valid);
+      *(f32x4*)(hsl + (size_t)r * (F / kBlock) + c * 4) =
+          *(const f32x4*)(p.hs + src * p.ld_hs + c * 4);
+    }
+  }
+  __syncthreads();
+
+  for (int ti = wave; ti < n_tiles; ti += kDRWaves) {
+    const int4 te = s_tiles[ti];
+    const bool shared = te.x == p.n_experts;
+    const int ccol = col < te.z ? col : 0;  // columns past the tile repeat column 0
+    const int lrow = shared ? n_valid + te.y + ccol : te.y + ccol;  // row of the LDS copy
+    auto load_h = [&](int kc, u32x4 (&b)[4], f32x4& d) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *(const u32x4*)(hl + (size_t)lrow * F + kc * kChunkK + j * kBlock + g8);
+      d = *(const f32x4*)(hsl + (size_t)lrow * (F / kBlock) + kc * 4);
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kg = 0; kg < p.kc_total; kg += kDRGroup) {
+      if (kg > 0) issue(ti, kg);  // the group at kg = 0 is already in flight
+      const int n_in = min(kDRGroup, p.kc_total - kg);
+      u32x4 b[2][4];
+      f32x4 d[2];
+      load_h(kg, b[0], d[0]);
+#pragma unroll
+      for (int kk = 0; kk < kDRGroup; ++kk) {
+        if (kk < n_in) {
+          if (kk + 1 < n_in) load_h(kg + kk + 1, b[(kk + 1) & 1], d[(kk + 1) & 1]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float sc = e8m0_to_f32((s[kk] >> (8 * j)) & 0xFFu);
+            acc += mfma_block(fp4x8_to_bf16x8(a[kk][j], sc),
+                              __builtin_bit_cast(bf16x8, b[kk & 1][j])) *
+                   d[kk & 1][j];
+          }
+        }
+      }
+    }
+    // lane l holds rows 4*(l/16) + i of column l % 16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[(ti * 16 + col) * 16 + 4 * (lane >> 4) + i] = acc[i];
+    if (ti + kDRWaves < n_tiles) issue(ti + kDRWaves, 0);
+  }
+  __syncthreads();
+
+  // y[t][16 rg + r] = sum over the token's slots in slot order, shared last
+  for (int e = tid; e < p.rows * 16; e += kDRThreads) {
+    const int t = e >> 4, r = e & 15;
+    float v = 0.f;
+    for (int s2 = 0; s2 < p.top_k; ++s2) {
+      const int a2 = t * p.top_k + s2;
+      if (p.ids[a2] < 0) continue;
+      const int pos = s_pos[a2];
+      const int ti = s_ptile[pos];
+      v += p.w[a2] * part[(ti * 16 + (pos - s_tiles[ti].y)) * 16 + r];
+    }
+    if (p.has_shared) {
+      const int ti = s_routed + (t >> 4);
+      v += part[(ti * 16 + (t & 15)) * 16 + r];
+    }
+    p.y[(int64_t)t * p.ld_y + 16 * rg + r] = v;
+  }
+}
+
+// Tiles of a decode step with `rows` rows: at most min(E, A) + ceil(A/16)
+// routed plus ceil(rows/16) shared.
+static int tiles_bound(const moe_layer_t* L, int rows) {
+  const int A = rows * L->top_k;
+  return std::min(L->n_experts, A) + (A + 15) / 16 + (L->has_shared ? (rows + 15) / 16 : 0);
+}
+
+// LDS of one workgroup: partials + every hidden row (codes and scales)
+static size_t down_rows_lds(const moe_layer_t* L, int rows) {
+  const size_t R = (size_t)rows * L->top_k + (L->has_shared ? rows : 0);
+  return (size_t)tiles_bound(L, rows) * 1024 + R * (size_t)L->d_ff * 2 +
+         R * (size_t)(L->d_ff / kBlock) * 4;
+}
+
+// Measured on MI355X (DS-V4 layer, FFN of one step): 1 row 35.5 vs 38.1 us
+// for the per-expert kernels + combine; 2 rows 61.0 vs 56.8, 3 rows 79.6 vs
+// 74.7 -- so one row only.
+bool down_rows_supported(const moe_layer_t* L, int rows) {
+  return rows == 1 && down_rows_lds(L, rows) <= kDownRowsMaxLds;
+}
+
+int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const float* w,
+                  const int32_t* offsets, const int32_t* sorted, const uint16_t* h,
+                  const float* hs, float* y, int64_t ld_y, hipStream_t s) {
+  const PackedDims pd(L->d_model, L->d_ff);
+  DownRowsArgs a{};
+  a.dn = (const uint8_t*)L->down;
+  a.dn_stride = L->down_stride;
+  a.dn_shared = (const uint8_t*)L->shared_down;
+  a.nib_bytes = pd.nib_bytes;
+  a.kc_total = (int)pd.kc;
+  a.sc_total = (int)pd.sc;
+  a.offsets = offsets;
+  a.sorted = sorted;
+  a.ids = ids;
+  a.w = w;
+  a.n_experts = L->n_experts;
+  a.top_k = L->top_k;
+  a.has_shared = L->has_shared;
+  a.rows = rows;
+  a.h = h;
+  a.hs = hs;
+  a.ld_h = L->d_ff;
+  a.ld_hs = L->d_ff / kBlock;
+  a.y = y;
+  a.ld_y = ld_y;
+  const size_t lds = down_rows_lds(L, rows);
+  if (lds > (size_t)kDownRowsMaxLds) return MOE_ERR_SHAPE;
+  // allow more than 64 KiB of dynamic LDS: once per device
+  static bool lds_raised[64] = {false};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  if (!lds_raised[dev]) {
+    if (hipFuncSetAttribute((const void*)down_rows_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kDownRowsMaxLds) != hipSuccess)
+      return MOE_ERR_HIP;
+    lds_raised[dev] = true;
+  }
+  hipLaunchKernelGGL(down_rows_kernel, dim3((unsigned)pd.rg), dim3(kDRThreads), lds, s, a,
+                     tiles_bound(L, rows));
+  return launch_status();
+}
+
+}  // namespace moe

@@ -374,7 +374,7 @@ void launch_combine(const float* P, const int32_t* ids, const float* w, int rows
                      ids, w, rows, top_k, has_shared, d_model, y, ld_y);
 }
 
-static int ffn_run(const moe_layer_t* L, int stages, const int8_t* q,
+static int ffn_run(const moe_layer_t* L, bool decode, int stages, const int8_t* q,
                    int64_t ld_q, const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                    const float* w, const int32_t* offsets, const int32_t* sorted, float* y,
                    int64_t ld_y, void* ws, hipStream_t s) {
@@ -414,7 +414,12 @@ static int ffn_run(const moe_layer_t* L, int stages, const int8_t* q,
     launch_proj<PASS_GATEUP, 4>(g, tiles, s);
   }
   // down projection -> per-slot partials -> fixed-order combine into y
-  if (stages & MOE_STAGE_DOWN) {
+  if ((stages & MOE_STAGE_DOWN) && decode && down_rows_supported(L, rows)) {
+    const int rc = down_rows_run(L, rows, ids, w, offsets, sorted,
+                                 (const uint16_t*)(base + lay.hidden),
+                                 (const float*)(base + lay.hidden_scales), y, ld_y, s);
+    if (rc != MOE_OK) return rc;
+  } else if (stages & MOE_STAGE_DOWN) {
     const PackedDims pd(L->d_model, L->d_ff);
     ProjArgs d = a;
     d.w = (const uint8_t*)L->down;
@@ -461,8 +466,8 @@ static int ffn_entry(const moe_layer_t* L, bool decode, bool fused, int stages, 
   if (!decode && L->d_model % 256 == 0 && (2 * L->d_ff) % 256 == 0)
     return prefill_run(L, stages, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y, ws,
                        (hipStream_t)stream);
-  return ffn_run(L, stages, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y, ws,
-                 (hipStream_t)stream);
+  return ffn_run(L, decode, stages, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y,
+                 ws, (hipStream_t)stream);
 }
 
 }  // namespace moe

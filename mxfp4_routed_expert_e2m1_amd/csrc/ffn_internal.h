@@ -60,6 +60,15 @@ int fused_decode_run(const moe_layer_t* L, const int8_t* q, int64_t ld_q, const 
                      const int32_t* offsets, const int32_t* sorted, float* y, int64_t ld_y,
                      void* ws, hipStream_t s);
 
+// Down projection + combine by output rows for one-row decode steps (partials,
+// 1 KiB per tile, and the step's hidden rows in at most kDownRowsMaxLds bytes
+// of LDS).
+constexpr int kDownRowsMaxLds = 150 * 1024;
+bool down_rows_supported(const moe_layer_t* L, int rows);
+int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const float* w,
+                  const int32_t* offsets, const int32_t* sorted, const uint16_t* h,
+                  const float* hs, float* y, int64_t ld_y, hipStream_t s);
+
 // Prefill stages on the grouped matrix-core GEMM (validated arguments).
 int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
                 const float* qs, int64_t ld_qs, int rows, const int32_t* ids, const float* w,

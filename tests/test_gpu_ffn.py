@@ -172,7 +172,7 @@ def test_decode_deterministic_and_padded():
     assert torch.equal(r1["y"], r2["y"])
 
 
-@pytest.mark.parametrize("T", [6, 12])
+@pytest.mark.parametrize("T", [1, 3, 6, 12])
 def test_decode_sentinel_routes(T):
     c = synth.DECODE_BATCH
     x = synth.activations(c["seed"], 7, T, DSV4.d_model)
@@ -180,8 +180,8 @@ def test_decode_sentinel_routes(T):
     ids_o, _ = oracle.route(lg, DSV4.top_k)
     ids_s = ids_o.copy()
     ids_s[0, 1] = -1
-    ids_s[3, :] = -1          # a token owned by no local expert: shared expert only
-    ids_s[5, 5] = -1
+    ids_s[min(3, T - 1), :] = -1   # a token owned by no local expert: shared expert only
+    ids_s[T - 1, 5] = -1
     run_case(DSV4, c["seed"], x, lg, ids_override=ids_s)
 
 
@@ -365,3 +365,21 @@ def test_prefill_stages_match_full_call():
     m.moe_ffn_stages(layer, 1, m.MOE_STAGE_DOWN, q, qs, ids, w, offsets, srt, y2, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("shape", range(len(FUSED_SHAPES)))
+def test_decode_one_row_other_shapes(shape):
+    # one row takes the row-organised down kernel: d_ff 1024..4096, with and
+    # without a shared expert
+    L = FUSED_SHAPES[shape]
+    seed = 31 + shape
+    x = synth.activations(seed, 1, 1, L.d_model)
+    lg = synth.router_logits(seed, 1, 1, L.n_experts)
+    run_case(L, seed, x, lg)
+
+
+def test_decode_one_row_tiny_and_odd():
+    for L, seed in ((TINY, 41), (ODD, 42)):
+        x = synth.activations(seed, 1, 1, L.d_model)
+        lg = synth.router_logits(seed, 1, 1, L.n_experts)
+        run_case(L, seed, x, lg)
