@@ -116,7 +116,7 @@ def main():
                  torch.empty(L.n_experts + 1, dtype=torch.int32, device=dev),
                  torch.empty(T * L.top_k, dtype=torch.int32, device=dev))
     y = torch.empty((T, L.d_model), dtype=torch.float32, device=dev)
-    ws = torch.zeros(m.moe_ffn_workspace_bytes(layers[0], T), dtype=torch.uint8, device=dev)
+    ws = torch.empty(m.moe_ffn_workspace_bytes(layers[0], T), dtype=torch.uint8, device=dev)
     ffn = m.moe_ffn_prefill if prefill else m.moe_ffn_decode
 
     def step(i):
@@ -175,18 +175,12 @@ def main():
     mean_touched = float(np.mean(touched))
     step_bytes = mean_touched * (gu_bytes + dn_bytes) + act_bytes + T * L.d_model * 4
 
-    # dominant kernel, alone over the rotated sets in a graph: decode = the
-    # single-launch layer kernel when moe_ffn_decode uses it (8+ rows), else
-    # the gate/up projection kernel; prefill = the gate/up GEMM stage
+    # dominant kernel, alone over the rotated sets in a graph: the gate/up
+    # projection (decode) or the gate/up GEMM (prefill)
     ids, w, counts, offsets, srt = route_out   # routes of input `last`
     n_k = sets * max(1, 64 // sets)
-    single = (not prefill) and m.moe_ffn_decode_single_launch(layers[0], T)
-    if single:
-        kcall = lambda i: m.moe_ffn_decode(layers[i % sets], q, qs, ids, w, offsets, srt, y=y,
-                                           ws=ws)
-    else:
-        kcall = lambda i: m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
-                                           q, qs, ids, w, offsets, srt, y, ws)
+    kcall = lambda i: m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
+                                       q, qs, ids, w, offsets, srt, y, ws)
     g_k = capture(torch, lambda: [kcall(i) for i in range(n_k)])
     g_k.replay()
     torch.cuda.synchronize()
@@ -209,17 +203,10 @@ def main():
                     i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
                     hbm_gbs=round(k_bytes / (k_us * 1e-6) / 1e9, 1))
     else:
-        if single:
-            # algorithmic bytes: every touched expert's gate/up + down once, the
-            # activation codes and scales read, y written
-            k_bytes = (last_touched * (gu_bytes + dn_bytes) + T * (L.d_model + L.d_model // 8)
-                       + T * L.d_model * 4)
-            kname = "fused_decode_kernel"
-        else:
-            # gate/up weights of the touched experts, activations, hidden codes out
-            k_bytes = (last_touched * gu_bytes + T * (L.d_model + L.d_model // 8)
-                       + A * (L.d_ff + L.d_ff // 32 * 4))
-            kname = "proj_kernel<gate/up>"
+        # gate/up weights of the touched experts, activations, hidden codes out
+        k_bytes = (last_touched * gu_bytes + T * (L.d_model + L.d_model // 8)
+                   + A * (L.d_ff + L.d_ff // 32 * 4))
+        kname = "proj_kernel<gate/up>"
         achieved = k_bytes / (k_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,

@@ -20,10 +20,9 @@
  *   - Pointers marked "device" are HIP device pointers; "host" are host
  *     memory.  The caller allocates and frees every buffer, including the
  *     workspace; the library allocates nothing and keeps no state between
- *     calls except a per-device cache of the architecture check and the
- *     counter words at the start of an FFN workspace (zero between calls,
- *     see moe_ffn_workspace_bytes).  Calls are re-entrant; FFN calls that
- *     share a workspace must not overlap (order them on one stream).
+ *     calls except per-device caches of the architecture check and a kernel
+ *     attribute.  Calls are re-entrant; FFN calls that share a workspace
+ *     must not overlap (order them on one stream).
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Work is enqueued asynchronously; results are valid after the stream
  *     is synchronised; buffers must stay alive until then.  No call
@@ -168,10 +167,6 @@ typedef struct moe_layer {
 /* Workspace of one FFN call with `rows` tokens (same for decode/prefill).
  * With A' = rows*top_k + (has_shared ? rows : 0) hidden rows, it holds, in
  * order, each region 256-byte aligned:
- *   counters      i32  [4 + 288 + d_model/64]  work queue and completion
- *                                      counters of the single-launch decode
- *                                      kernel (bytes [0, off_hidden); the
- *                                      size does not depend on rows)
  *   hidden codes  bf16 [A'][d_ff]     requantised intermediate, the int8
  *                                      codes stored as exact bf16 values
  *   hidden scales f32  [A'][d_ff/32]
@@ -182,20 +177,15 @@ typedef struct moe_layer {
  * Hidden row of routed assignment at sorted position p is p; the shared
  * expert's row for token t is rows*top_k + t.  Partials row of routed
  * assignment a is a; shared: rows*top_k + t.  The byte offsets are returned
- * by moe_ffn_workspace_layout (any output pointer may be NULL).
- * The counter words must be zero before a workspace's first moe_ffn_decode
- * call: zero-fill a new workspace once (e.g. hipMemset at allocation).  Every
- * call leaves them zero again, so the same workspace serves any number of
- * later calls, of any rows, and graph replays.  Word 2 becomes non-zero if a
- * bounded wait inside the decode kernel expired (that call's y is invalid);
- * the library never clears it.  Other regions need no initialisation. */
+ * by moe_ffn_workspace_layout (any output pointer may be NULL).  No region
+ * needs initialisation; a call overwrites what it reads. */
 size_t moe_ffn_workspace_bytes(const moe_layer_t* L, int rows);
 int moe_ffn_workspace_layout(const moe_layer_t* L, int rows, size_t* off_hidden,
                              size_t* off_hidden_scales, size_t* off_partials);
 
 /* Decode ([strix] "The exact-rows contract" and [lucebox] "Tune small HIP
- * batches": one weight pass serves every resident row; [gfx90a] §1/§2:
- * decode and prefill need different execution geometries).
+ * batches": each weight byte is read once for all resident rows; [gfx90a]
+ * §1/§2: decode and prefill are given different kernel shapes).
  *   q       int8  [rows][ld_q]  (device) activation codes (moe_quant_act_q8)
  *   qs      f32   [rows][ld_qs] (device) their block scales
  *   ids, w  [rows][top_k] (device) from moe_route_group (or sentinel-edited)
@@ -204,20 +194,14 @@ int moe_ffn_workspace_layout(const moe_layer_t* L, int rows, size_t* off_hidden,
  *   ws      workspace (device, 256-byte aligned), ws_bytes >= the query
  * 1 <= rows <= MOE_MAX_DECODE_ROWS.  q, ld_q as for moe_quant_act_q8; qs and
  * ld_qs 16-byte aligned / % 4 == 0; ld_y % 4 == 0 and y 16-byte aligned.
- * With rows >= 8 and d_model/128, d_ff/128 each 16, 32 or 64 the whole
- * layer is one persistent kernel (gate/up, SwiGLU + requant, down and
- * combine, linked by the workspace counters); otherwise it runs the three
- * kernels of moe_ffn_stages (faster for fewer rows).  Both leave the hidden codes and scales in the workspace
- * and are held to the same error bound. */
+ * The gate/up projection (+ SwiGLU + requant), the down projection and the
+ * combine run as three kernels; with one row the down projection and the
+ * combine are one kernel that keeps the partials on chip. */
 int moe_ffn_decode(const moe_layer_t* L, const int8_t* q, int64_t ld_q,
                    const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                    const float* w, const int32_t* offsets, const int32_t* sorted,
                    float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream);
 
-/* Host-only query: 1 if moe_ffn_decode with this layer and row count runs
- * the single persistent kernel, 0 if it runs the three separate kernels,
- * or a negative MOE_ERR_* for an invalid layer or row count. */
-int moe_ffn_decode_single_launch(const moe_layer_t* L, int rows);
 
 /* Prefill chunk: same arguments and results as moe_ffn_decode for any
  * rows >= 1 (tuned for 512..4096).  Grid sizes derive from host-known bounds
@@ -249,8 +233,8 @@ int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask, const int8
                    size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* Stand-alone k-row matvec ([strix] "The exact-rows contract": one weight
- * pass serves K resident rows of a 4096x14336 matvec): y[t][n] =
+/* Stand-alone k-row matvec ([strix] "The exact-rows contract": the weights
+ * of a 4096x14336 matvec are read once for all K resident rows): y[t][n] =
  * sum_b dot_b(q[t], W[n]) * qs[t][b] * 2^(u[n][b]-128), fp32.
  *   w_packed (device) from moe_pack_mxfp4(..., gate_up_interleave = 0)
  *   q, qs, y as for moe_ffn_decode; 1 <= rows <= MOE_MAX_DECODE_ROWS. */

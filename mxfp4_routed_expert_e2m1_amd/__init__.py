@@ -22,8 +22,7 @@ MOE_MAX_DECODE_ROWS = 16
 EXPORTS = [
     "moe_packed_bytes", "moe_pack_mxfp4", "moe_unpack_mxfp4", "moe_quant_act_q8",
     "moe_route_group", "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout",
-    "moe_ffn_decode", "moe_ffn_decode_single_launch", "moe_ffn_prefill", "moe_ffn_stages",
-    "moe_matvec_mxfp4",
+    "moe_ffn_decode", "moe_ffn_prefill", "moe_ffn_stages", "moe_matvec_mxfp4",
     "moe_debug_block_dots", "moe_status_string",
 ]
 
@@ -68,7 +67,6 @@ def lib():
                                                C.POINTER(SZ), C.POINTER(SZ), C.POINTER(SZ)]
         ffn_args = [C.POINTER(moe_layer_t), P, I64, P, I64, I, P, P, P, P, P, I64, P, SZ, P]
         L.moe_ffn_decode.argtypes = ffn_args
-        L.moe_ffn_decode_single_launch.argtypes = [C.POINTER(moe_layer_t), I]
         L.moe_ffn_prefill.argtypes = ffn_args
         L.moe_ffn_stages.argtypes = [C.POINTER(moe_layer_t), I, I] + ffn_args[1:]
         L.moe_matvec_mxfp4.argtypes = [P, I, I, P, I64, P, I64, I, P, I64, P]
@@ -203,18 +201,11 @@ def _ffn(fn, layer, q, qs, ids, w, offsets, srt, y, ws, stream):
     if y is None:
         y = torch.empty((rows, layer.d_model), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = torch.zeros(moe_ffn_workspace_bytes(layer, rows), dtype=torch.uint8,
+        ws = torch.empty(moe_ffn_workspace_bytes(layer, rows), dtype=torch.uint8,
                          device=q.device)
     _call(fn, C.byref(layer.c), _ptr(q), _ld(q), _ptr(qs), _ld(qs), rows, _ptr(ids), _ptr(w),
           _ptr(offsets), _ptr(srt), _ptr(y), _ld(y), _ptr(ws), ws.numel(), _stream(stream))
     return y
-
-
-def moe_ffn_decode_single_launch(layer: Layer, rows: int) -> bool:
-    r = int(lib().moe_ffn_decode_single_launch(C.byref(layer.c), rows))
-    if r < 0:
-        raise MoeError("moe_ffn_decode_single_launch", r)
-    return bool(r)
 
 
 def moe_ffn_decode(layer, q, qs, ids, w, offsets, srt, y=None, ws=None, stream=None):

@@ -110,43 +110,6 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
-// ---------------------------------------------- cross-workgroup handoff
-// Device-coherent (sc1) loads and stores and relaxed agent-scope atomics:
-// data handed from one workgroup to another in the same launch moves only
-// through these, so no whole-L2 writeback or invalidate (__threadfence) is
-// needed; a producer waits for its stores (vmcnt) before it bumps a counter.
-__device__ inline int ld_coherent(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint32_t ld_coherent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t ld_coherent(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_coherent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_coherent(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int add_coherent(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// all of this wave's stores have completed (gfx9: vmcnt counts stores too)
-__device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0xF70); }
-
-// LDS-only barrier: waits for this wave's LDS traffic, not for its global
-// loads, so prefetched chunks stay in flight across it.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-
-
 // ------------------------------------------------------------- tiles
 // A "tile" is up to 16 token columns of one expert that share one weight
 // pass.  Tiles run over routed experts in expert order (ceil(count/16)

@@ -5,16 +5,17 @@
 // projection's cost is latency: a per-expert kernel has to store fp32
 // partials, and a combine kernel has to read them back.
 // Here a workgroup owns 16 output rows (one packed row group) of every tile.
-// It first copies every hidden row of the step (codes and scales, 4.3 KB per
-// row at d_ff 2048) into LDS with one round of loads; then wave w streams row
-// group `blockIdx.x` of tiles w, w+8, ... (16 K chunks at a time in flight,
-// the first tile's before the copy) against the LDS copy, keeps the 16x16 partial tile in LDS, and when
-// all tiles are done the workgroup adds, for every token and row, the
-// partials of the token's slots in slot order, shared expert last (gfx90a
-// report §8.2: fp32 partials, fixed reduction order) and writes y.  No partials leave the
-// chip and no combine kernel runs.  Same exact block dots as every other
-// projection here (FP4 converter with the E8M0 scale folded in, one 16x16x32
-// bf16 matrix-core op per 32-element block, fp32 FMA with the hidden scale).
+// Each wave issues its first tile's 16 weight chunks, then the workgroup
+// copies every hidden row of the step (codes and scales, 4.3 KB per row at
+// d_ff 2048) into LDS, so both arrive in one round trip.  Wave w streams row
+// group `blockIdx.x` of tiles w, w+8, ... against the LDS copy and keeps the
+// 16x16 partial tile in LDS; when all tiles are done the workgroup adds, for
+// every token and row, the partials of the token's slots in slot order,
+// shared expert last (gfx90a report §8.2: fp32 partials, fixed reduction
+// order) and writes y.  No partials leave the chip and no combine kernel runs.
+// Same exact block dots as every other projection here (FP4 converter with
+// the E8M0 scale folded in, one 16x16x32 bf16 matrix-core op per 32-element
+// block, fp32 FMA with the hidden scale).
 #include "ffn_internal.h"
 
 namespace moe {
@@ -45,7 +46,8 @@ struct DownRowsArgs {
 // rows of the step [R][d_ff] bf16 and their scales [R][d_ff/32] f32, R =
 // valid routed assignments + shared rows (row r < n_valid is sorted position
 // r, row n_valid + t the shared expert's row of token t).
-__global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p, int tiles_cap) {
+__global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p,
+                                                                    int tiles_cap) {
   extern __shared__ __align__(16) float dyn[];
   float* part = dyn;
   __shared__ int4 s_tiles[kMaxDecodeTiles];  // expert, start, count
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   uint32_t s[kDRGroup];
   auto issue = [&](int ti, int kg) {
     const int4 te = s_tiles[ti];
-    const uint8_t* blob = te.x == p.n_experts ? p.dn_shared : p.dn + (int64_t)te.x * p.dn_stride;
+    const uint8_t* blob =
+        te.x == p.n_experts ? p.dn_shared : p.dn + (int64_t)te.x * p.dn_stride;
     const u32x4* nib = (const u32x4*)blob;
     const uint8_t* scl = blob + p.nib_bytes;
     const int n_in = min(kDRGroup, p.kc_total - kg);
@@ -96,8 +99,8 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
       if (kk < n_in) {
         const int kc = kg + kk;
         a[kk] = nib[((int64_t)rg * p.kc_total + kc) * 64 + lane];
-        s[kk] = *(const uint32_t*)(scl + (((int64_t)rg * p.sc_total + (kc >> 2)) * 16 + col) * 16 +
-                                   (kc & 3) * 4);
+        s[kk] = *(const uint32_t*)(scl + (((int64_t)rg * p.sc_total + (kc >> 2)) * 16 + col) *
+                                             16 + (kc & 3) * 4);
       }
     }
   };

@@ -3,10 +3,10 @@
 //
 // One projection kernel family serves the k-row matvec and both FFN passes:
 //   * A workgroup owns RGW packed 16-row groups of one weight matrix and one
-//     "tile" of up to 16 token columns that share the weight pass ("one
-//     weight pass serves K resident rows", Strix record, the exact-rows
-//     contract; weight reuse across 2..16 columns, lucebox PR "Tune small
-//     HIP batches").
+//     "tile" of up to 16 token columns that share the weight pass (each
+//     weight byte is read once for all resident rows: Strix record, "The
+//     exact-rows contract"; weight reuse across 2..16 columns: lucebox PR,
+//     "Tune small HIP batches").
 //   * Its W waves split the K dimension; each wave streams its K chunks of
 //     all RGW row groups as contiguous 1 KiB bursts, turns every dword of 8
 //     E2M1 codes into the bf16 A fragment with one FP4 converter instruction
@@ -442,7 +442,7 @@ static int ffn_run(const moe_layer_t* L, bool decode, int stages, const int8_t* 
   return launch_status();
 }
 
-static int ffn_entry(const moe_layer_t* L, bool decode, bool fused, int stages, const int8_t* q,
+static int ffn_entry(const moe_layer_t* L, bool decode, int stages, const int8_t* q,
                      int64_t ld_q, const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                      const float* w, const int32_t* offsets, const int32_t* sorted, float* y,
                      int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
@@ -458,10 +458,6 @@ static int ffn_entry(const moe_layer_t* L, bool decode, bool fused, int stages, 
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
   if (ws_bytes < ws_layout(L, rows).total) return MOE_ERR_WORKSPACE;
   if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
-  if (decode && fused && stages == MOE_STAGE_ALL && rows >= kFusedDecodeMinRows &&
-      fused_decode_supported(L))
-    return fused_decode_run(L, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y, ws,
-                            (hipStream_t)stream);
   // the prefill GEMM works in 256-row weight blocks; other shapes use the tiles
   if (!decode && L->d_model % 256 == 0 && (2 * L->d_ff) % 256 == 0)
     return prefill_run(L, stages, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y, ws,
@@ -495,15 +491,8 @@ extern "C" int moe_ffn_decode(const moe_layer_t* L, const int8_t* q, int64_t ld_
                               const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                               const float* w, const int32_t* offsets, const int32_t* sorted,
                               float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
-  return ffn_entry(L, true, true, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets,
-                   sorted, y, ld_y, ws, ws_bytes, stream);
-}
-
-extern "C" int moe_ffn_decode_single_launch(const moe_layer_t* L, int rows) {
-  const int rc = check_layer(L);
-  if (rc != MOE_OK) return rc;
-  if (rows < 1 || rows > MOE_MAX_DECODE_ROWS) return MOE_ERR_SHAPE;
-  return rows >= kFusedDecodeMinRows && fused_decode_supported(L) ? 1 : 0;
+  return ffn_entry(L, true, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y,
+                   ld_y, ws, ws_bytes, stream);
 }
 
 extern "C" int moe_matvec_mxfp4(const void* w_packed, int n_out, int d_in, const int8_t* q,
@@ -558,8 +547,8 @@ extern "C" int moe_ffn_prefill(const moe_layer_t* L, const int8_t* q, int64_t ld
                                const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                                const float* w, const int32_t* offsets, const int32_t* sorted,
                                float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
-  return ffn_entry(L, false, false, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets,
-                   sorted, y, ld_y, ws, ws_bytes, stream);
+  return ffn_entry(L, false, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted,
+                   y, ld_y, ws, ws_bytes, stream);
 }
 
 extern "C" int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask,
@@ -568,6 +557,6 @@ extern "C" int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask,
                               const int32_t* offsets, const int32_t* sorted, float* y,
                               int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
   if (prefill != 0 && prefill != 1) return MOE_ERR_INVALID_ARG;
-  return ffn_entry(L, prefill == 0, false, stage_mask, q, ld_q, qs, ld_qs, rows, ids, w,
-                   offsets, sorted, y, ld_y, ws, ws_bytes, stream);
+  return ffn_entry(L, prefill == 0, stage_mask, q, ld_q, qs, ld_qs, rows, ids, w, offsets,
+                   sorted, y, ld_y, ws, ws_bytes, stream);
 }

@@ -1,5 +1,5 @@
-// ffn_internal.h -- workspace layout and the prefill entry shared by ffn.hip and
-// prefill.hip.
+// ffn_internal.h -- workspace layout and the entries ffn.hip shares with
+// down_rows.hip and prefill.hip.
 #pragma once
 
 #include "common.h"
@@ -8,10 +8,6 @@ namespace moe {
 
 // Workspace regions (each 256-byte aligned), for A' = rows*top_k (+ rows when
 // a shared expert is present) hidden rows:
-//   counters      i32  [counter_words(d_model)]  completion
-//                                      counters of the persistent decode kernel;
-//                                      zero before the first call, left zero by
-//                                      every call (fixed size, independent of rows)
 //   hidden        bf16 [A'][d_ff]      requantised intermediate codes
 //   hidden_scales f32  [A'][d_ff/32]
 //   partials      f32  [A'][d_model]   per-slot down projections
@@ -19,23 +15,16 @@ namespace moe {
 //                                      hidden row (tile order), exact in bf16
 //   act_scales    f32  [A'][d_model/32]
 struct WsLayout {
-  size_t counters, hidden, hidden_scales, partials, act, act_scales, total;
+  size_t hidden, hidden_scales, partials, act, act_scales, total;
 };
 
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Counter words: combined row blocks, spare, error flag, spare; one per tile
-// (a decode call has at most min(E, 256) + 16 + 1 <= kMaxDecodeTiles tiles);
-// one per 64-row block of the output.
-constexpr int kCtrCombined = 0, kCtrError = 2, kCtrTiles = 4;
-constexpr int kMaxDecodeTiles = 288;
-inline int counter_words(int d_model) { return kCtrTiles + kMaxDecodeTiles + d_model / 64; }
 
 inline WsLayout ws_layout(const moe_layer_t* L, int rows) {
   const size_t hrows = (size_t)rows * L->top_k + (L->has_shared ? (size_t)rows : 0);
   WsLayout w;
-  w.counters = 0;
-  w.hidden = round256((size_t)counter_words(L->d_model) * 4);
+  w.hidden = 0;
   w.hidden_scales = w.hidden + round256(hrows * L->d_ff * 2);
   w.partials = w.hidden_scales + round256(hrows * (L->d_ff / kBlock) * 4);
   w.act = w.partials + round256(hrows * L->d_model * 4);
@@ -48,22 +37,12 @@ inline WsLayout ws_layout(const moe_layer_t* L, int rows) {
 void launch_combine(const float* P, const int32_t* ids, const float* w, int rows, int top_k,
                     int has_shared, int d_model, float* y, int64_t ld_y, hipStream_t s);
 
-// The whole decode layer in one persistent kernel (validated arguments).
-// Below kFusedDecodeMinRows rows its chain of dependent phases is latency
-// bound and the three separate kernels are faster (measured on MI355X: 1 row
-// 58 vs 40 us, 4 rows 119 vs 105 us; 16 rows 265 vs 260 us, 16 rows on hot
-// experts 145 vs 185 us).
-constexpr int kFusedDecodeMinRows = 8;
-bool fused_decode_supported(const moe_layer_t* L);
-int fused_decode_run(const moe_layer_t* L, const int8_t* q, int64_t ld_q, const float* qs,
-                     int64_t ld_qs, int rows, const int32_t* ids, const float* w,
-                     const int32_t* offsets, const int32_t* sorted, float* y, int64_t ld_y,
-                     void* ws, hipStream_t s);
-
 // Down projection + combine by output rows for one-row decode steps (partials,
 // 1 KiB per tile, and the step's hidden rows in at most kDownRowsMaxLds bytes
-// of LDS).
+// of LDS; a decode step has at most min(E, 256) + 16 + 1 <= kMaxDecodeTiles
+// tiles).
 constexpr int kDownRowsMaxLds = 150 * 1024;
+constexpr int kMaxDecodeTiles = 288;
 bool down_rows_supported(const moe_layer_t* L, int rows);
 int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const float* w,
                   const int32_t* offsets, const int32_t* sorted, const uint16_t* h,
