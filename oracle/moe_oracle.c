@@ -38,9 +38,9 @@ int oracle_e2m1_x2(int code) {
 
 double oracle_e2m1(int code) { return 0.5 * (double)oracle_e2m1_x2(code); }
 
-/* E8M0 shared block exponent: 2^(u-127), 0xFF is NaN.  The pages name
- * "E8M0 scaling" ([gfx90a] §6.1) without printing the bias; the MX
- * definition is used. */
+/* E8M0 shared block exponent: 2^(u-127), 0xFF is NaN.  [gfx90a] §6.1 names
+ * the E8M0 scaling step without printing the bias; the MX definition is
+ * used. */
 double oracle_e8m0(int u) {
   if (u == 255) return NAN;
   return ldexp(1.0, u - 127);
@@ -226,7 +226,7 @@ int oracle_block_dots(const uint8_t* codes, int64_t ld_c, int n_out, int d_in,
 
 /* ------------------------------------------------------------- SwiGLU */
 
-/* SwiGLU between gate/up and down ([gfx90a] Fig. 1 "gate/up -> down";
+/* SwiGLU between gate/up and down ([gfx90a] Fig. 1, gate/up followed by down;
  * [lucebox] "Tune small HIP batches": SwiGLU folded into the second
  * projection pass).  Reading used: h = silu(gate) * up with
  * silu(z) = z / (1 + exp(-z)), no clamp, evaluated in fp64 from the fp32
