@@ -99,6 +99,42 @@ __device__ inline f32x4 mfma_block(bf16x8 a, bf16x8 b) {
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
+// Gate/up epilogue arithmetic, shared by every kernel that finishes a gate/up
+// pass so all of them round alike: h = silu(gate) * up, then the group-32
+// int8 code of h for the group scale d = amax/127 (0 when the group is zero).
+__device__ inline float swiglu(float gate, float up) { return gate / (1.0f + expf(-gate)) * up; }
+__device__ inline float q8_code(float v, float d) {
+  return d != 0.f ? fminf(fmaxf(rintf(v / d), -127.f), 127.f) : 0.f;
+}
+
+// Max over each aligned group of 32 lanes (lanes 0-31, 32-63), returned in
+// every lane: quad swaps and the row half-mirror / mirror on DPP give each
+// 16-lane row its max, then one lane-xor-16 shuffle combines rows 0/1 and
+// 2/3.  Exact: max does not round.  (permlane16_swap(v, v) would do the last
+// step without LDS, but this compiler folds the max of its two results away.)
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, false));
+}
+__device__ inline float max32(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+  return fmaxf(v, __shfl_xor(v, 16, 32));
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt 0) but not for its global loads, which stay in flight across it
+// (__syncthreads would also wait for vmcnt 0).
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // inclusive prefix sum over a wave64
 __device__ inline int wave_incl_scan(int v) {
   const int l = lane_id();
@@ -201,6 +237,7 @@ __device__ inline Tile find_tile(const int32_t* __restrict__ offsets, int n_expe
 
 // ------------------------------------------------------------ host side
 bool device_is_gfx950();  // cached per device
+int device_cu_count();    // compute units of the current device, cached; 0 if unknown
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 

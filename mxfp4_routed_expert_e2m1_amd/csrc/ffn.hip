@@ -31,29 +31,6 @@ enum Pass : int { PASS_MATVEC = 0, PASS_GATEUP = 1, PASS_DOWN = 2 };
 
 constexpr int kMaxPrefillRows = 1 << 22;
 
-struct ProjArgs {
-  const uint8_t* w;         // matrix blob (matvec) or routed expert 0 blob
-  int64_t w_stride;         // bytes between routed experts
-  const uint8_t* w_shared;  // shared expert blob
-  int64_t nib_bytes;        // offset of the scale region inside a blob
-  int rg_total, kc_total, sc_total;
-  // tiles
-  const int32_t* offsets;
-  const int32_t* sorted;
-  int n_experts, top_k, has_shared, rows;
-  // B operand: int8 codes (matvec, gate/up) or bf16 hidden codes (down)
-  const void* b;
-  int64_t ld_b;
-  const float* bs;
-  int64_t ld_bs;
-  // epilogue
-  float* y;  // matvec output / down partials
-  int64_t ld_y;
-  uint16_t* h;  // gate/up: requantised hidden codes (bf16 bits) and scales
-  float* hs;
-  int64_t ld_h, ld_hs;
-};
-
 // One wave's share of a projection: RGW row groups x K chunks [kc0, kc0 + n),
 // accumulated into acc.  KPW > 0: exactly KPW chunks, every weight load issued
 // up front (kc0 % 4 == 0 when KPW == 4, so one 16-byte load per row group
@@ -245,12 +222,9 @@ __global__ __launch_bounds__(W * 64, 4) void proj_kernel(ProjArgs p) {
       const int l = 16 * ((f & 15) >> 2) + n;
       const float gv = red[0][gsel * 4 + (f & 3)][l];
       const float uv = red[0][(gsel + 1) * 4 + (f & 3)][l];
-      const float hv = gv / (1.0f + expf(-gv)) * uv;
-      float m = fabsf(hv);
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
-      const float d = m / 127.0f;
-      const float qf = d != 0.f ? fminf(fmaxf(rintf(hv / d), -127.f), 127.f) : 0.f;
+      const float hv = swiglu(gv, uv);
+      const float d = max32(fabsf(hv)) / 127.0f;
+      const float qf = q8_code(hv, d);
       if (n < t.count) {
         const int64_t hrow = shared ? n_tok_assign + t.start + n : t.start + n;
         p.h[hrow * p.ld_h + f0 + f] = (uint16_t)(__float_as_uint(qf) >> 16);
@@ -411,7 +385,8 @@ static int ffn_run(const moe_layer_t* L, bool decode, int stages, const int8_t* 
     g.hs = (float*)(base + lay.hidden_scales);
     g.ld_h = L->d_ff;
     g.ld_hs = L->d_ff / kBlock;
-    launch_proj<PASS_GATEUP, 4>(g, tiles, s);
+    if (decode && stream_supported(g.kc_total, g.rg_total)) launch_stream(STREAM_GATEUP, g, tiles, s);
+    else launch_proj<PASS_GATEUP, 4>(g, tiles, s);
   }
   // down projection -> per-slot partials -> fixed-order combine into y
   if ((stages & MOE_STAGE_DOWN) && decode && down_rows_supported(L, rows)) {
@@ -435,7 +410,8 @@ static int ffn_run(const moe_layer_t* L, bool decode, int stages, const int8_t* 
     d.ld_bs = L->d_ff / kBlock;
     d.y = (float*)(base + lay.partials);
     d.ld_y = L->d_model;
-    launch_proj<PASS_DOWN, 4>(d, tiles, s);
+    if (decode && stream_supported(d.kc_total, d.rg_total)) launch_stream(STREAM_DOWN, d, tiles, s);
+    else launch_proj<PASS_DOWN, 4>(d, tiles, s);
     launch_combine((const float*)(base + lay.partials), ids, w, rows, L->top_k, L->has_shared,
                    L->d_model, y, ld_y, s);
   }

@@ -1,5 +1,5 @@
 // ffn_internal.h -- workspace layout and the entries ffn.hip shares with
-// down_rows.hip and prefill.hip.
+// stream.hip, down_rows.hip and prefill.hip.
 #pragma once
 
 #include "common.h"
@@ -32,6 +32,37 @@ inline WsLayout ws_layout(const moe_layer_t* L, int rows) {
   w.total = w.act_scales + round256(hrows * (L->d_model / kBlock) * 4);
   return w;
 }
+
+// Persistent decode projections (stream.hip).  MATVEC: y[n][row] for the rows
+// columns of q; GATEUP: SwiGLU + group-32 requant into h/hs; DOWN: per-slot
+// fp32 partials into y (assignment rows, shared-expert rows after them).
+enum StreamPass : int { STREAM_MATVEC = 0, STREAM_GATEUP = 1, STREAM_DOWN = 2 };
+
+// Arguments of a projection pass (ffn.hip one-item kernels and stream.hip).
+struct ProjArgs {
+  const uint8_t* w;         // matrix blob (matvec) or routed expert 0 blob
+  int64_t w_stride;         // bytes between routed experts
+  const uint8_t* w_shared;  // shared expert blob
+  int64_t nib_bytes;        // offset of the scale region inside a blob
+  int rg_total, kc_total, sc_total;
+  const int32_t* offsets;   // [n_experts + 1] (not read by MATVEC)
+  const int32_t* sorted;    // [rows * top_k] (not read by MATVEC)
+  int n_experts, top_k, has_shared, rows;  // rows <= MOE_MAX_DECODE_ROWS
+  const void* b;            // int8 codes (MATVEC, GATEUP) or bf16 hidden codes (DOWN)
+  int64_t ld_b;
+  const float* bs;
+  int64_t ld_bs;
+  float* y;                 // MATVEC output / DOWN partials
+  int64_t ld_y;
+  uint16_t* h;              // GATEUP: requantised hidden codes (bf16 bits) and scales
+  float* hs;
+  int64_t ld_h, ld_hs;
+};
+
+// K/128 in {8, 16, 32} and whole 4-group items
+bool stream_supported(int kc_total, int rg_total);
+// tiles_bound: an upper bound on the call's tiles (1 for MATVEC)
+void launch_stream(int pass, const ProjArgs& a, int tiles_bound, hipStream_t s);
 
 // y = weighted combine of the partials (slot order, shared expert last)
 void launch_combine(const float* P, const int32_t* ids, const float* w, int rows, int top_k,

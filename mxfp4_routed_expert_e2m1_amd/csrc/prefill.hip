@@ -227,8 +227,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
         for (int i = 0; i < 4; ++i) {
           const float g0 = acc[0][q4][i], u0 = acc[1][q4][i];
           const float g1 = acc[2][q4][i], u1 = acc[3][q4][i];
-          hv[i] = g0 / (1.0f + expf(-g0)) * u0;
-          hv[4 + i] = g1 / (1.0f + expf(-g1)) * u1;
+          hv[i] = swiglu(g0, u0);
+          hv[4 + i] = swiglu(g1, u1);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(hv[i]));
@@ -240,8 +240,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
           uint32_t packed[4];
 #pragma unroll
           for (int i = 0; i < 8; i += 2) {
-            const float q0 = d != 0.f ? fminf(fmaxf(rintf(hv[i] / d), -127.f), 127.f) : 0.f;
-            const float q1 = d != 0.f ? fminf(fmaxf(rintf(hv[i + 1] / d), -127.f), 127.f) : 0.f;
+            const float q0 = q8_code(hv[i], d);
+            const float q1 = q8_code(hv[i + 1], d);
             packed[i / 2] = (__float_as_uint(q0) >> 16) | (__float_as_uint(q1) & 0xFFFF0000u);
           }
           uint16_t* hrow = p.h + (c.row0 + col) * p.ld_h;

@@ -1,4 +1,4 @@
-// status.cpp -- status strings and the cached gfx950 check.
+// status.cpp -- status strings and the cached per-device queries.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -21,6 +21,19 @@ bool device_is_gfx950() {
   const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev < 64) g_arch_ok[dev] = ok ? 1 : 0;
   return ok;
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+static int g_cus[64] = {0};
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && g_cus[dev] > 0) return g_cus[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) g_cus[dev] = n;
+  return n;
 }
 
 }  // namespace moe

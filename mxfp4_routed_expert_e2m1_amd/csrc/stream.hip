@@ -1,0 +1,344 @@
+// stream.hip -- persistent decode projections.
+//
+// The decode passes (gate/up + SwiGLU + requant, and the down projection into
+// per-slot partials) and the k-row matvec stream each weight byte once for
+// every resident row (Strix record, "The exact-rows contract"; lucebox PR,
+// "Tune small HIP batches").  Their cost is HBM time, so the kernel is shaped
+// to keep HBM busy rather than around one work item:
+//   * An item is one tile (up to 16 token columns of one expert) x 4 packed
+//     row groups (64 weight rows; 32 gate/up features).  A workgroup of W
+//     waves splits the item's K range, 4 chunks of 128 per wave, exactly as
+//     the one-item kernel does, so every block dot, every fp32 FMA and the
+//     wave-order reduction are the same operations in the same order.
+//   * Workgroups are persistent (one per CU for 8 waves) and walk a static
+//     item list (item = blockIdx.x + i * gridDim.x).  As soon as a wave has
+//     consumed chunk kk of its item it issues chunk kk of its next item into
+//     the same registers, so the next item's weights, scales and activations
+//     are in flight while the current item is reduced across waves and its
+//     epilogue runs.
+//   * The cross-wave reduction goes through a double-buffered LDS array with
+//     an LDS-only barrier: loads in flight are never drained.
+//   * The tile map (the call's expert offsets) and the sorted assignment list
+//     are read once per workgroup, not once per item.
+#include <algorithm>
+#include <type_traits>
+
+#include "ffn_internal.h"
+
+namespace moe {
+
+constexpr int kSRGW = 4;  // packed row groups per item
+constexpr int kSKPW = 4;  // K chunks of a wave per item
+
+// Uniform (wave-wide) values live in scalar registers: the compiler cannot
+// see that a value read from LDS or a shuffle is the same in every lane.
+// Pointers stay kernel arguments plus a uniform offset, so the loads keep
+// their global address space (an integer-to-pointer cast would make them
+// flat loads, which also count as LDS traffic).
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Raw buffer loads: a wave-uniform resource (base, size) in scalar registers,
+// a per-lane byte offset in one vector register, a uniform byte offset in a
+// scalar register and a constant in the instruction.  Offsets at or past the
+// resource size read as zero (the hardware range check covers the per-lane
+// offset and the constant).  The explicit form also keeps the compiler
+// from merging or re-deriving addresses per load.
+constexpr int kBufDword3 = 0x00020000;  // raw 32-bit data format (gfx9 family)
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufDword3);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+template <int PASS, int W>
+__global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
+  constexpr int RGW = kSRGW, KPW = kSKPW, NT = W * 64;
+  static_assert(PASS != STREAM_GATEUP || RGW == 4, "gate/up needs 2 gate/up pairs = 32 features");
+  using BV = std::conditional_t<PASS == STREAM_DOWN, u32x4, u32x2>;
+  constexpr int kBBytes = PASS == STREAM_DOWN ? 2 : 1;  // bytes per B element
+  __shared__ float red[2][W][RGW * 4][64];
+  __shared__ int s_sorted[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];
+  __shared__ int4 s_tiles[PASS == STREAM_MATVEC ? 1 : kMaxDecodeTiles];  // expert, start, count
+  __shared__ int s_ntiles;
+  __shared__ uint32_t s_amax[2][16];  // gate/up: per-column amax bits, by reduction buffer
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15;
+  const int n_rb = p.rg_total / RGW;
+  const int n_tok_assign = p.rows * p.top_k;
+  const int kc0 = wave * KPW;
+
+  // The call's tiles (one round trip, wave 0) and sorted list go to LDS.
+  int n_items = n_rb;
+  if constexpr (PASS != STREAM_MATVEC) {
+    for (int i = tid; i < n_tok_assign; i += NT) s_sorted[i] = p.sorted[i];
+    if (PASS == STREAM_GATEUP && tid < 32) s_amax[tid >> 4][tid & 15] = 0u;
+    if (wave == 0) {
+      TileMap<16> tm;
+      tm.load(p.offsets, p.n_experts, p.has_shared, p.rows);
+      int idx = tm.incl - tm.lsum;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        for (int r = 0; r < tm.nt[i]; ++r, ++idx)
+          s_tiles[idx] = int4{tm.e0 + i, tm.o[i] + 16 * r, min(16, tm.o[i + 1] - tm.o[i] - 16 * r), 0};
+      if (lane < tm.shared_tiles)
+        s_tiles[tm.routed + lane] = int4{p.n_experts, 16 * lane, min(16, p.rows - 16 * lane), 0};
+      if (lane == 0) s_ntiles = tm.n_tiles();
+    }
+    lds_barrier();
+    n_items = uniform(s_ntiles) * n_rb;
+  }
+  int it = blockIdx.x;
+  if (it >= n_items) return;  // the same for the whole workgroup
+
+  // per-item values, all wave-uniform
+  struct Item {
+    int expert, start, count, rb;
+    bool shared;
+    __amdgpu_buffer_rsrc_t w;  // the expert's blob
+    uint32_t a_soff, s_soff;   // row group pr0 in its nibble and scale regions
+  };
+  const uint32_t blob_bytes =
+      (uint32_t)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256);
+  auto item_at = [&](int i) {
+    Item x;
+    x.rb = i % n_rb;
+    const uint8_t* blob = p.w;
+    int64_t eoff = 0;
+    if constexpr (PASS == STREAM_MATVEC) {
+      x.expert = 0;
+      x.start = 0;
+      x.count = p.rows;
+      x.shared = false;
+    } else {
+      const int4 te = s_tiles[i / n_rb];
+      x.expert = uniform(te.x);
+      x.start = uniform(te.y);
+      x.count = uniform(te.z);
+      x.shared = x.expert == p.n_experts;
+      if (x.shared) blob = p.w_shared;
+      else eoff = (int64_t)x.expert * p.w_stride;
+    }
+    x.w = buf_rsrc(blob + uniform(eoff), blob_bytes);
+    const int pr0 = x.rb * RGW;
+    x.a_soff = (uint32_t)pr0 * (uint32_t)p.kc_total * 1024u;
+    x.s_soff = (uint32_t)p.nib_bytes + (uint32_t)pr0 * (uint32_t)p.sc_total * 256u;
+    return x;
+  };
+  // byte offset of this lane's B row (columns past the tile repeat column 0)
+  auto brow_of = [&](const Item& x) -> int {
+    const int ccol = col < x.count ? col : 0;
+    if (PASS == STREAM_MATVEC) return ccol;
+    if (PASS == STREAM_GATEUP) return x.shared ? x.start + ccol : s_sorted[x.start + ccol] / p.top_k;
+    return x.shared ? n_tok_assign + x.start + ccol : x.start + ccol;
+  };
+
+  // B operand rows: tokens (MATVEC, GATEUP) or hidden rows (DOWN)
+  const int b_rows = PASS == STREAM_DOWN ? n_tok_assign + (p.has_shared ? p.rows : 0) : p.rows;
+  const __amdgpu_buffer_rsrc_t rb_b = buf_rsrc(p.b, (uint32_t)(b_rows * p.ld_b * kBBytes));
+  const __amdgpu_buffer_rsrc_t rb_d = buf_rsrc(p.bs, (uint32_t)(b_rows * p.ld_bs * 4));
+  // lane offsets that do not depend on the item
+  const uint32_t a_lane = (uint32_t)(kc0 * 1024 + lane * 16);
+  const uint32_t a_gstride = (uint32_t)p.kc_total * 1024u;
+  const uint32_t s_lane = (uint32_t)(((kc0 >> 2) * 16 + col) * 16);
+  const uint32_t s_gstride = (uint32_t)p.sc_total * 256u;
+  const uint32_t b_lane = (uint32_t)((kc0 * kChunkK + 8 * (lane >> 4)) * kBBytes);
+
+  u32x4 a[KPW][RGW];
+  u32x4 sv[RGW], sv_n[RGW];
+  BV b[KPW][4];
+  f32x4 d[KPW];
+  // the 16 scale bytes of row `col` for this wave's 4 chunks (kc0 % 4 == 0)
+  auto issue_s = [&](const Item& x, u32x4 (&sd)[RGW]) {
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) sd[g] = buf_load16(x.w, s_lane, x.s_soff + g * s_gstride);
+  };
+  auto issue = [&](const Item& x, int brow, int kk) {
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) a[kk][g] = buf_load16(x.w, a_lane + kk * 1024, x.a_soff + g * a_gstride);
+    const uint32_t bo = (uint32_t)(brow * p.ld_b * kBBytes) + b_lane;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t o = bo + (kk * kChunkK + j * kBlock) * kBBytes;
+      if constexpr (PASS == STREAM_DOWN) b[kk][j] = buf_load16(rb_b, o, 0);
+      else b[kk][j] = buf_load8(rb_b, o, 0);
+    }
+    d[kk] = __builtin_bit_cast(f32x4, buf_load16(rb_d, (uint32_t)(brow * p.ld_bs * 4 + (kc0 + kk) * 16), 0));
+  };
+  auto compute = [&](int kk, const u32x4 (&sc4)[RGW], f32x4 (&acc)[RGW]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 bb;
+      if constexpr (PASS == STREAM_DOWN) bb = __builtin_bit_cast(bf16x8, b[kk][j]);
+      else bb = i8x8_to_bf16x8(b[kk][j]);
+#pragma unroll
+      for (int g = 0; g < RGW; ++g) {
+        const float sc = e8m0_to_f32((sc4[g][kk] >> (8 * j)) & 0xFFu);
+        const f32x4 r = mfma_block(fp4x8_to_bf16x8(a[kk][g][j], sc), bb);
+        acc[g] += r * d[kk][j];
+      }
+    }
+  };
+  // reduced item in red[buf] -> epilogue (fixed wave order, from 0.f)
+  auto epilogue = [&](const Item& x, int buf) {
+    if constexpr (PASS == STREAM_GATEUP) {
+      // Wave w reduces the (pair gp, row i) slices w*S .. w*S+S-1 over all 64
+      // lanes (contiguous LDS rows: no bank conflicts).  Lane l of slice
+      // (gp, i) holds feature 16 gp + 4 (l / 16) + i of column l % 16; its
+      // gate sits in packed group 2 gp, its up in 2 gp + 1.  The group-32
+      // amax of a column spans the 8 slices and the 4 lane rows: two lane
+      // xors, then an LDS max over the slices (exact, order-free: |h| >= 0
+      // compares like its bits).
+      constexpr int S = 8 / W;
+      const int f0 = x.rb * 32;
+      if (wave == 0 && lane < 16) s_amax[buf ^ 1][lane] = 0u;  // last item's slot is free
+      float hv[S];
+      float mq = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int sl = wave * S + s2, gp = sl >> 2, i = sl & 3;
+        float gv = 0.f, uv = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) gv += red[buf][w2][8 * gp + i][lane];
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) uv += red[buf][w2][8 * gp + 4 + i][lane];
+        hv[s2] = swiglu(gv, uv);
+        mq = fmaxf(mq, fabsf(hv[s2]));
+      }
+      mq = fmaxf(mq, __shfl_xor(mq, 16, 64));
+      mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+      if (lane < 16) atomicMax(&s_amax[buf][lane], __float_as_uint(mq));
+      lds_barrier();
+      const float dd = __uint_as_float(s_amax[buf][col]) / 127.0f;
+      if (col < x.count) {
+        const int64_t hrow = x.shared ? n_tok_assign + x.start + col : x.start + col;
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+          const int sl = wave * S + s2, gp = sl >> 2, i = sl & 3;
+          const float qf = q8_code(hv[s2], dd);
+          p.h[hrow * p.ld_h + f0 + 16 * gp + 4 * (lane >> 4) + i] =
+              (uint16_t)(__float_as_uint(qf) >> 16);
+        }
+        if (wave == 0 && lane < 16) p.hs[hrow * p.ld_hs + (f0 >> 5)] = dd;
+      }
+    } else {
+      for (int e = tid; e < RGW * 4 * 64; e += NT) {
+        const int gi = e >> 6, l = e & 63;
+        const int n = l & 15;
+        if (n >= x.count) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) v += red[buf][w2][gi][l];
+        const int row = (x.rb * RGW + (gi >> 2)) * 16 + 4 * (l >> 4) + (gi & 3);
+        int orow;
+        if (PASS == STREAM_MATVEC) orow = n;
+        else orow = x.shared ? n_tok_assign + x.start + n : s_sorted[x.start + n];
+        p.y[(int64_t)orow * p.ld_y + row] = v;
+      }
+    }
+  };
+
+  Item cur = item_at(it);
+  issue_s(cur, sv);
+  {
+    const int br = brow_of(cur);
+#pragma unroll
+    for (int kk = 0; kk < KPW; ++kk) issue(cur, br, kk);
+  }
+
+  // One item: (NEXT) the next item's scales into the other scale registers,
+  // then compute chunk kk and reuse its registers for chunk kk of the next
+  // item; reduce; epilogue.
+  int buf = 0;
+  auto step = [&](auto next_c, const Item& nx, const u32x4 (&sc_cur)[RGW], u32x4 (&sc_nxt)[RGW]) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    int br_n = 0;
+    if constexpr (NEXT) {
+      br_n = brow_of(nx);
+      issue_s(nx, sc_nxt);
+    }
+    f32x4 acc[RGW];
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KPW; ++kk) {
+      compute(kk, sc_cur, acc);
+      if constexpr (NEXT) {
+        // keep the scheduler from sinking the loads below later chunks
+        __builtin_amdgcn_sched_barrier(0);
+        issue(nx, br_n, kk);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < RGW; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[buf][wave][g * 4 + i][lane] = acc[g][i];
+    lds_barrier();
+    epilogue(cur, buf);
+    buf ^= 1;
+  };
+  // two items per trip so the scale registers alternate without copies
+  bool in_sv_n = false;
+  for (;;) {
+    int in = it + (int)gridDim.x;
+    if (in >= n_items) break;
+    Item nx = item_at(in);
+    step(std::true_type{}, nx, sv, sv_n);
+    cur = nx;
+    it = in;
+    in = it + (int)gridDim.x;
+    if (in >= n_items) {
+      in_sv_n = true;
+      break;
+    }
+    nx = item_at(in);
+    step(std::true_type{}, nx, sv_n, sv);
+    cur = nx;
+    it = in;
+  }
+  if (in_sv_n) step(std::false_type{}, cur, sv_n, sv);
+  else step(std::false_type{}, cur, sv, sv_n);
+}
+
+// KPW = 4 chunks per wave: K/128 = 4W for W = 2, 4, 8 waves.
+bool stream_supported(int kc_total, int rg_total) {
+  return (kc_total == 8 || kc_total == 16 || kc_total == 32) && rg_total % kSRGW == 0;
+}
+
+template <int PASS>
+static void launch_stream_w(const ProjArgs& a, int items_bound, hipStream_t s) {
+  const int cus = std::max(1, device_cu_count());
+  auto grid = [&](int wgs_per_cu) {
+    return (unsigned)std::max(1, std::min(items_bound, cus * wgs_per_cu));
+  };
+  switch (a.kc_total) {
+    case 32:
+      hipLaunchKernelGGL((stream_kernel<PASS, 8>), dim3(grid(1)), dim3(512), 0, s, a);
+      return;
+    case 16:
+      hipLaunchKernelGGL((stream_kernel<PASS, 4>), dim3(grid(2)), dim3(256), 0, s, a);
+      return;
+    default:
+      hipLaunchKernelGGL((stream_kernel<PASS, 2>), dim3(grid(4)), dim3(128), 0, s, a);
+      return;
+  }
+}
+
+void launch_stream(int pass, const ProjArgs& a, int tiles_bound, hipStream_t s) {
+  const int items_bound = tiles_bound * (a.rg_total / kSRGW);
+  if (pass == STREAM_GATEUP) launch_stream_w<STREAM_GATEUP>(a, items_bound, s);
+  else if (pass == STREAM_DOWN) launch_stream_w<STREAM_DOWN>(a, items_bound, s);
+  else launch_stream_w<STREAM_MATVEC>(a, items_bound, s);
+}
+
+}  // namespace moe
