@@ -117,6 +117,26 @@ __device__ inline float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
                                                             0xF, false));
 }
+// DPP move limited to the rows in ROWS (other rows keep v).
+template <int CTRL, int ROWS>
+__device__ inline float dpp_rows(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                              __builtin_bit_cast(int, v), CTRL,
+                                                              ROWS, 0xF, false));
+}
+
+// Max over the whole wave, returned as a wave-uniform value: row maxima on
+// DPP, row broadcasts 15 and 31 fold them into lane 63, read from there.
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));        // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));        // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x141>(v));       // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));       // row_mirror
+  v = fmaxf(v, dpp_rows<0x142, 0xA>(v)); // row_bcast:15 into rows 1, 3
+  v = fmaxf(v, dpp_rows<0x143, 0xC>(v)); // row_bcast:31 into rows 2, 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ inline float max32(float v) {
   v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
   v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
@@ -135,14 +155,20 @@ __device__ inline void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// inclusive prefix sum over a wave64
+// inclusive prefix sum over a wave64 on DPP: row shifts 1, 2, 4, 8 (zero
+// shifted in) scan each 16-lane row, row broadcasts 15 and 31 carry the row
+// totals forward.  Every lane must be active.
+template <int CTRL, int ROWS, bool ZERO_FILL>
+__device__ inline int dpp_add_src(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, ZERO_FILL);
+}
 __device__ inline int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (l >= d) v += o;
-  }
+  v += dpp_add_src<0x111, 0xF, true>(v);   // row_shr:1
+  v += dpp_add_src<0x112, 0xF, true>(v);   // row_shr:2
+  v += dpp_add_src<0x114, 0xF, true>(v);   // row_shr:4
+  v += dpp_add_src<0x118, 0xF, true>(v);   // row_shr:8
+  v += dpp_add_src<0x142, 0xA, false>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_add_src<0x143, 0xC, false>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 

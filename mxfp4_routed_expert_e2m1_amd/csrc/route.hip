@@ -23,7 +23,10 @@ constexpr int kMaxExperts = 512;  // keeps the grouping LDS under 64 KiB
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 
-// One wave: top_k picks of one row; lane s < top_k receives slot s.
+// One wave: top_k picks of one row; lane s < top_k receives slot s.  Each
+// round takes the largest remaining logit (a wave max on DPP) and, among
+// the experts holding exactly that value, the lowest index (per-slot
+// ballots, lowest slot first: expert e sits in lane e % 64, slot e / 64).
 template <int PER_LANE>
 __device__ inline void topk_row(const float* __restrict__ l, int n_experts, int top_k,
                                 int* my_id, float* my_w) {
@@ -39,25 +42,19 @@ __device__ inline void topk_row(const float* __restrict__ l, int n_experts, int 
   float sum = 0.f;
   *my_id = 0;
   for (int s = 0; s < top_k; ++s) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    float lv = -INFINITY;
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) {
-      const int e = lane + 64 * j;
-      const bool ok = e < n_experts && !((taken >> j) & 1u);
-      if (ok && (v[j] > bv || (v[j] == bv && e < be))) {
-        bv = v[j];
-        be = e;
-      }
+      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
+      if (ok) lv = fmaxf(lv, v[j]);
     }
+    const float bv = wave_max(lv);
+    int be = -1;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
+    for (int j = 0; j < PER_LANE; ++j) {
+      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
+      const uint64_t hit = __ballot(ok && v[j] == bv);
+      if (be < 0 && hit != 0) be = 64 * j + __ffsll((unsigned long long)hit) - 1;
     }
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     const float sg = 1.0f / (1.0f + expf(-bv));
