@@ -145,6 +145,14 @@ __device__ inline float max32(float v) {
   return fmaxf(v, __shfl_xor(v, 16, 32));
 }
 
+// Direct global -> LDS load (no registers; counted by vmcnt): lane l of the
+// wave writes `bytes` (4 or 16) at lds_base + l * bytes, lds_base uniform.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+__device__ inline void load_to_lds(const void* src, void* lds_base, int bytes) {
+  if (bytes == 16) __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds_base, 16, 0, 0);
+  else __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds_base, 4, 0, 0);
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
 // (lgkmcnt 0) but not for its global loads, which stay in flight across it
 // (__syncthreads would also wait for vmcnt 0).

@@ -22,7 +22,8 @@ namespace moe {
 
 constexpr int kDRWaves = 8;
 constexpr int kDRThreads = kDRWaves * 64;
-constexpr int kDRGroup = 16;  // K chunks of a wave in flight at once (16 KiB)
+constexpr int kDRGroup = 16;  // K chunks of a wave's weight registers (16 KiB)
+constexpr int kDRAhead = 6;   // chunks a wave keeps in flight ahead of its math
 
 struct DownRowsArgs {
   const uint8_t* dn;  // routed expert 0 blob
@@ -46,6 +47,9 @@ struct DownRowsArgs {
 // rows of the step [R][d_ff] bf16 and their scales [R][d_ff/32] f32, R =
 // valid routed assignments + shared rows (row r < n_valid is sorted position
 // r, row n_valid + t the shared expert's row of token t).
+// NC: 16-byte pieces of hidden codes each thread copies (a constant, so the
+// number of loads in flight is known when the copy waits).
+template <int NC>
 __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p,
                                                                     int tiles_cap) {
   extern __shared__ __align__(16) float dyn[];
@@ -53,10 +57,15 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   __shared__ int4 s_tiles[kMaxDecodeTiles];  // expert, start, count
   __shared__ int s_pos[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // assignment -> sorted position
   __shared__ int s_ptile[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // sorted position -> tile
-  __shared__ int s_ntiles, s_routed;
+  __shared__ int s_ntiles, s_routed, s_nvalid;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
+  // one round trip: this step's sorted list (positions past the valid ones
+  // hold -1), the tile map and the valid count are loaded together
+  const int n_assign = p.rows * p.top_k;  // <= kDRThreads
+  const int srt = tid < n_assign ? p.sorted[tid] : -1;
   if (wave == 0) {
+    const int nv = p.offsets[p.n_experts];
     TileMap<16> tm;
     tm.load(p.offsets, p.n_experts, p.has_shared, p.rows);
     int idx = tm.incl - tm.lsum;
@@ -74,12 +83,13 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     if (lane == 0) {
       s_ntiles = min(tm.n_tiles(), kMaxDecodeTiles);
       s_routed = tm.routed;
+      s_nvalid = nv;
     }
   }
-  const int n_valid = p.offsets[p.n_experts];
-  for (int i = tid; i < n_valid; i += kDRThreads) s_pos[p.sorted[i]] = i;
+  if (srt >= 0) s_pos[srt] = tid;
   __syncthreads();
   const int n_tiles = s_ntiles;
+  const int n_valid = s_nvalid;
   const int F = p.kc_total * kChunkK;
   const int rg = blockIdx.x;  // 16 output rows 16*rg .. 16*rg+15
   const int col = lane & 15, g8 = 8 * (lane >> 4);
@@ -87,47 +97,68 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   // this wave's weight stream: row group rg of tile ti, K chunks kg..kg+15
   u32x4 a[kDRGroup];
   uint32_t s[kDRGroup];
-  auto issue = [&](int ti, int kg) {
-    const int4 te = s_tiles[ti];
+  // chunk kk of the group at kg (a group shorter than kDRGroup repeats its
+  // last chunk, so every issue is unconditional and the count in flight a
+  // constant)
+  auto issue_chunk = [&](const int4 te, int kg, int kk) {
     const uint8_t* blob =
         te.x == p.n_experts ? p.dn_shared : p.dn + (int64_t)te.x * p.dn_stride;
     const u32x4* nib = (const u32x4*)blob;
     const uint8_t* scl = blob + p.nib_bytes;
-    const int n_in = min(kDRGroup, p.kc_total - kg);
-#pragma unroll
-    for (int kk = 0; kk < kDRGroup; ++kk) {
-      if (kk < n_in) {
-        const int kc = kg + kk;
-        a[kk] = nib[((int64_t)rg * p.kc_total + kc) * 64 + lane];
-        s[kk] = *(const uint32_t*)(scl + (((int64_t)rg * p.sc_total + (kc >> 2)) * 16 + col) *
-                                             16 + (kc & 3) * 4);
-      }
-    }
+    const int kc = kg + min(kk, min(kDRGroup, p.kc_total - kg) - 1);
+    a[kk] = nib[((int64_t)rg * p.kc_total + kc) * 64 + lane];
+    s[kk] = *(const uint32_t*)(scl + (((int64_t)rg * p.sc_total + (kc >> 2)) * 16 + col) * 16 +
+                               (kc & 3) * 4);
   };
-  // the first tile's weights go out before the hidden rows are copied, so
-  // both arrive in one round trip
-  if (wave < n_tiles) issue(wave, 0);
+  auto issue_head = [&](const int4 te, int kg) {
+#pragma unroll
+    for (int kk = 0; kk < kDRAhead; ++kk) issue_chunk(te, kg, kk);
+  };
 
-  // hidden rows -> LDS (16-byte pieces)
+  // Hidden rows (codes and scales) go out first, into registers, then the
+  // first tile's weights; the copy pieces are stored to LDS as soon as they
+  // land (the weights stay in flight), and the math waits only for the LDS
+  // barrier and then for each chunk's own weights.  Pieces past the end
+  // are loaded but not stored, so every thread issues NC + 1 copy loads and
+  // then the same weight loads, on every path.
+  const bool has_tile = wave < n_tiles;
+  // A wave without a tile issues the loads of tile 0; with no tile at all (no
+  // shared expert and every slot a sentinel: s_tiles is empty) the loads of
+  // routed expert 0's row group, which always exists.
+  const int4 te0 = n_tiles > 0 ? s_tiles[has_tile ? wave : 0] : int4{0, 0, 0, 0};
   const int R = n_valid + (p.has_shared ? p.rows : 0);
   uint16_t* hl = (uint16_t*)(part + (size_t)tiles_cap * 256);
   float* hsl = (float*)(hl + (size_t)R * F);
-  {
-    const int per_row = F / 8;  // 16-byte pieces of codes per row
-    for (int e = tid; e < R * per_row; e += kDRThreads) {
-      const int r = e / per_row, c = e % per_row;
-      const int64_t src = r < n_valid ? r : (int64_t)p.rows * p.top_k + (r - n_valid);
-      *(u32x4*)(hl + (size_t)r * F + c * 8) = *(const u32x4*)(p.h + src * p.ld_h + c * 8);
-    }
-    const int per_row_s = F / kBlock / 4;  // 16-byte pieces of scales per row
-    for (int e = tid; e < R * per_row_s; e += kDRThreads) {
-      const int r = e / per_row_s, c = e % per_row_s;
-      const int64_t src = r < n_valid ? r : (int64_t)p.rows * p.top_k + (r - n_valid);
-      *(f32x4*)(hsl + (size_t)r * (F / kBlock) + c * 4) =
-          *(const f32x4*)(p.hs + src * p.ld_hs + c * 4);
-    }
+  const int per_row = F / 8;             // 16-byte pieces of codes per row
+  const int per_row_s = F / kBlock / 4;  // 16-byte pieces of scales per row
+  const int n_pc = R * per_row, n_ps = R * per_row_s;
+  auto src_row = [&](int r) -> int64_t {
+    return r < n_valid ? r : (int64_t)p.rows * p.top_k + (r - n_valid);
+  };
+  // (pieces past the end read piece 0 of hidden row 0, which always exists)
+  u32x4 cp[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int e = k * kDRThreads + tid;
+    const int64_t off = e < n_pc ? src_row(e / per_row) * p.ld_h + (e % per_row) * 8 : 0;
+    cp[k] = *(const u32x4*)(p.h + off);
   }
-  __syncthreads();
+  f32x4 cs;
+  {
+    const int64_t off = tid < n_ps ? src_row(tid / per_row_s) * p.ld_hs + (tid % per_row_s) * 4 : 0;
+    cs = *(const f32x4*)(p.hs + off);
+  }
+  // every wave issues (a wave without a tile repeats tile 0's addresses,
+  // which merge with that tile's misses in L2): a branch here would make
+  // the compiler wait for the weights before storing the copy
+  issue_head(te0, 0);
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int e = k * kDRThreads + tid;
+    if (e < n_pc) *(u32x4*)(hl + (size_t)e * 8) = cp[k];
+  }
+  if (tid < n_ps) *(f32x4*)(hsl + (size_t)tid * 4) = cs;
+  lds_barrier();  // every copy piece is in LDS; the weights stay in flight
 
   for (int ti = wave; ti < n_tiles; ti += kDRWaves) {
     const int4 te = s_tiles[ti];
@@ -142,11 +173,13 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int kg = 0; kg < p.kc_total; kg += kDRGroup) {
-      if (kg > 0) issue(ti, kg);  // the group at kg = 0 is already in flight
+      if (kg > 0) issue_head(te, kg);  // the head of the first group is already in flight
       const int n_in = min(kDRGroup, p.kc_total - kg);
       u32x4 b[2][4];
       f32x4 d[2];
       load_h(kg, b[0], d[0]);
+      // streamed: chunk kk's math waits for chunk kk only, then chunk
+      // kk + kDRAhead goes out, so the wave never stalls on a full queue
 #pragma unroll
       for (int kk = 0; kk < kDRGroup; ++kk) {
         if (kk < n_in) {
@@ -159,12 +192,17 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
                    d[kk & 1][j];
           }
         }
+        if (kk + kDRAhead < kDRGroup) {
+          __builtin_amdgcn_sched_barrier(0);  // keep the issue after this chunk's math
+          issue_chunk(te, kg, kk + kDRAhead);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     // lane l holds rows 4*(l/16) + i of column l % 16
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[(ti * 16 + col) * 16 + 4 * (lane >> 4) + i] = acc[i];
-    if (ti + kDRWaves < n_tiles) issue(ti + kDRWaves, 0);
+    if (ti + kDRWaves < n_tiles) issue_head(s_tiles[ti + kDRWaves], 0);
   }
   __syncthreads();
 
@@ -201,11 +239,20 @@ static size_t down_rows_lds(const moe_layer_t* L, int rows) {
          R * (size_t)(L->d_ff / kBlock) * 4;
 }
 
+// Copy pieces per thread for the largest hidden-row count of a step.
+static int copy_pieces(const moe_layer_t* L, int rows) {
+  const int r_max = rows * L->top_k + (L->has_shared ? rows : 0);
+  return (r_max * (L->d_ff / 8) + kDRThreads - 1) / kDRThreads;
+}
+
 // Measured on MI355X (DS-V4 layer, FFN of one step): 1 row 35.5 vs 38.1 us
 // for the per-expert kernels + combine; 2 rows 61.0 vs 56.8, 3 rows 79.6 vs
-// 74.7 -- so one row only.
+// 74.7 -- so one row only.  The copy takes at most 8 code pieces and one
+// scale piece per thread.
 bool down_rows_supported(const moe_layer_t* L, int rows) {
-  return rows == 1 && down_rows_lds(L, rows) <= kDownRowsMaxLds;
+  const int r_max = rows * L->top_k + (L->has_shared ? rows : 0);
+  return rows == 1 && down_rows_lds(L, rows) <= kDownRowsMaxLds &&
+         copy_pieces(L, rows) <= 8 && r_max * (L->d_ff / kBlock / 4) <= kDRThreads;
 }
 
 int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const float* w,
@@ -235,19 +282,41 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
   a.ld_y = ld_y;
   const size_t lds = down_rows_lds(L, rows);
   if (lds > (size_t)kDownRowsMaxLds) return MOE_ERR_SHAPE;
-  // allow more than 64 KiB of dynamic LDS: once per device
-  static bool lds_raised[64] = {false};
+  const int nc = copy_pieces(L, rows);
+  if (nc < 1 || nc > 8) return MOE_ERR_SHAPE;
+  // allow more than 64 KiB of dynamic LDS: once per device and variant
+  static bool lds_raised[64][9] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
-  if (!lds_raised[dev]) {
-    if (hipFuncSetAttribute((const void*)down_rows_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kDownRowsMaxLds) != hipSuccess)
-      return MOE_ERR_HIP;
-    lds_raised[dev] = true;
+  const void* fn = nullptr;
+  switch (nc) {
+    case 1: fn = (const void*)down_rows_kernel<1>; break;
+    case 2: fn = (const void*)down_rows_kernel<2>; break;
+    case 3: fn = (const void*)down_rows_kernel<3>; break;
+    case 4: fn = (const void*)down_rows_kernel<4>; break;
+    case 5: fn = (const void*)down_rows_kernel<5>; break;
+    case 6: fn = (const void*)down_rows_kernel<6>; break;
+    case 7: fn = (const void*)down_rows_kernel<7>; break;
+    default: fn = (const void*)down_rows_kernel<8>; break;
   }
-  hipLaunchKernelGGL(down_rows_kernel, dim3((unsigned)pd.rg), dim3(kDRThreads), lds, s, a,
-                     tiles_bound(L, rows));
+  if (!lds_raised[dev][nc]) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDownRowsMaxLds) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    lds_raised[dev][nc] = true;
+  }
+  const int cap = tiles_bound(L, rows);
+  const dim3 grid((unsigned)pd.rg), block(kDRThreads);
+  switch (nc) {
+    case 1: hipLaunchKernelGGL(down_rows_kernel<1>, grid, block, lds, s, a, cap); break;
+    case 2: hipLaunchKernelGGL(down_rows_kernel<2>, grid, block, lds, s, a, cap); break;
+    case 3: hipLaunchKernelGGL(down_rows_kernel<3>, grid, block, lds, s, a, cap); break;
+    case 4: hipLaunchKernelGGL(down_rows_kernel<4>, grid, block, lds, s, a, cap); break;
+    case 5: hipLaunchKernelGGL(down_rows_kernel<5>, grid, block, lds, s, a, cap); break;
+    case 6: hipLaunchKernelGGL(down_rows_kernel<6>, grid, block, lds, s, a, cap); break;
+    case 7: hipLaunchKernelGGL(down_rows_kernel<7>, grid, block, lds, s, a, cap); break;
+    default: hipLaunchKernelGGL(down_rows_kernel<8>, grid, block, lds, s, a, cap); break;
+  }
   return launch_status();
 }
 

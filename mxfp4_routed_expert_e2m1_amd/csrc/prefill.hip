@@ -66,13 +66,6 @@ struct Stage {
   float d[8][4][16];        // activation scales, [token group][block][token] 2 KiB
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-__device__ inline void load_to_lds(const void* src, void* lds_base, int bytes) {
-  if (bytes == 16) __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds_base, 16, 0, 0);
-  else __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds_base, 4, 0, 0);
-}
-
 // vmcnt <= n (n < 16), no wait on the other counters (gfx9 encoding)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | (n))
 

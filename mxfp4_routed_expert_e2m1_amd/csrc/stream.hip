@@ -80,7 +80,11 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   // The call's tiles (one round trip, wave 0) and sorted list go to LDS.
   int n_items = n_rb;
   if constexpr (PASS != STREAM_MATVEC) {
-    for (int i = tid; i < n_tok_assign; i += NT) s_sorted[i] = p.sorted[i];
+    // sorted list and tile map are loaded together: one round trip
+    constexpr int NS = (MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K + NT - 1) / NT;
+    int srt[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) srt[k] = tid + k * NT < n_tok_assign ? p.sorted[tid + k * NT] : 0;
     if (PASS == STREAM_GATEUP && tid < 32) s_amax[tid >> 4][tid & 15] = 0u;
     if (wave == 0) {
       TileMap<16> tm;
@@ -94,6 +98,9 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
         s_tiles[tm.routed + lane] = int4{p.n_experts, 16 * lane, min(16, p.rows - 16 * lane), 0};
       if (lane == 0) s_ntiles = tm.n_tiles();
     }
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+      if (tid + k * NT < n_tok_assign) s_sorted[tid + k * NT] = srt[k];
     lds_barrier();
     n_items = uniform(s_ntiles) * n_rb;
   }
