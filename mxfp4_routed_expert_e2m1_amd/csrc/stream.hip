@@ -29,6 +29,13 @@ namespace moe {
 
 constexpr int kSRGW = 4;  // packed row groups per item
 constexpr int kSKPW = 4;  // K chunks of a wave per item
+// Chunks a wave keeps in flight ahead of its math, over the item sequence
+// (kSKPW: the next item's chunk kk goes out after this item's chunk kk).
+#ifndef STREAM_AHEAD
+#define STREAM_AHEAD 2
+#endif
+constexpr int kSAhead = STREAM_AHEAD;
+static_assert(kSAhead >= 1 && kSAhead <= kSKPW, "prefetch distance");
 
 // Uniform (wave-wide) values live in scalar registers: the compiler cannot
 // see that a value read from LDS or a shuffle is the same in every lane.
@@ -255,12 +262,10 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   };
 
   Item cur = item_at(it);
+  int br_cur = brow_of(cur);
   issue_s(cur, sv);
-  {
-    const int br = brow_of(cur);
 #pragma unroll
-    for (int kk = 0; kk < KPW; ++kk) issue(cur, br, kk);
-  }
+  for (int kk = 0; kk < kSAhead; ++kk) issue(cur, br_cur, kk);
 
   // One item: (NEXT) the next item's scales into the other scale registers,
   // then compute chunk kk and reuse its registers for chunk kk of the next
@@ -279,10 +284,14 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
 #pragma unroll
     for (int kk = 0; kk < KPW; ++kk) {
       compute(kk, sc_cur, acc);
-      if constexpr (NEXT) {
-        // keep the scheduler from sinking the loads below later chunks
+      // then chunk kk + kSAhead of the sequence: this item's, or the next's
+      // (its registers are chunk kk's, just consumed, or an older slot)
+      const int ka = kk + kSAhead;
+      if (ka < KPW || NEXT) {
+        // keep the scheduler from moving the loads across the math
         __builtin_amdgcn_sched_barrier(0);
-        issue(nx, br_n, kk);
+        if (ka < KPW) issue(cur, br_cur, ka);
+        else issue(nx, br_n, ka - KPW);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -302,6 +311,7 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
     Item nx = item_at(in);
     step(std::true_type{}, nx, sv, sv_n);
     cur = nx;
+    br_cur = brow_of(cur);
     it = in;
     in = it + (int)gridDim.x;
     if (in >= n_items) {
@@ -311,6 +321,7 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
     nx = item_at(in);
     step(std::true_type{}, nx, sv_n, sv);
     cur = nx;
+    br_cur = brow_of(cur);
     it = in;
   }
   if (in_sv_n) step(std::false_type{}, cur, sv_n, sv);
