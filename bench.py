@@ -206,7 +206,7 @@ def main():
         # gate/up weights of the touched experts, activations, hidden codes out
         k_bytes = (last_touched * gu_bytes + T * (L.d_model + L.d_model // 8)
                    + A * (L.d_ff + L.d_ff // 32 * 4))
-        kname = "proj_kernel<gate/up>"
+        kname = "stream_kernel<gate/up>"
         achieved = k_bytes / (k_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
