@@ -7,12 +7,15 @@
 // the k picks.
 //
 // Grouping: gfx90a report §7.1 item 8 (the expert sorter groups assignments
-// so each expert scans its packed weights once).  One workgroup: an LDS
-// histogram (order-free), an exclusive scan, then a chunked stable scatter in
-// which a lane's destination is the expert's running base + the counts of
-// earlier waves in the chunk + its rank among earlier lanes of its wave with
-// the same expert (from ballots).  Atomics only add counts; no atomic decides
-// an order, so the permutation is unique and bit-exact.
+// so each expert scans its packed weights once); the result is the stable
+// counting sort by expert.  Decode-sized calls (one workgroup, top-k
+// included): an assignment's position is its rank by (expert, index),
+// counted over the few ids in LDS.  Larger calls: an LDS histogram
+// (order-free), an exclusive scan, then a chunked stable scatter in which a
+// lane's destination is the expert's running base + the counts of earlier
+// waves in the chunk + its rank among earlier lanes of its wave with the
+// same expert (from ballots).  Atomics only add counts; no atomic decides an
+// order, so the permutation is unique and bit-exact.
 #include <float.h>
 
 #include "common.h"
@@ -84,35 +87,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
 }
 
-// Grouping of ids (global, or LDS when FUSED: then the first `rows` waves
-// first compute the top-k of one row each, for rows <= kGroupWaves).
+// Grouping of the ids of any number of rows (after route_topk_kernel).
 constexpr int kFusedMaxAssign = kGroupWaves * MOE_MAX_TOP_K;
 
-template <bool FUSED, int PER_LANE>
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(
-    const float* __restrict__ logits, int64_t ld_l, int rows, int top_k,
-    int32_t* __restrict__ ids_g, float* __restrict__ w_g, int n_assign, int n_experts,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
+    const int32_t* __restrict__ ids_g, int n_assign, int n_experts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
   __shared__ int hist[kMaxExperts];
   __shared__ int running[kMaxExperts];
   __shared__ int wave_tot[kGroupWaves];
-  __shared__ int ids_l[FUSED ? kFusedMaxAssign : 1];
   extern __shared__ int wcnt[];  // [kGroupWaves][n_experts]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if constexpr (FUSED) {
-    if (wave < rows) {
-      int id;
-      float wt;
-      topk_row<PER_LANE>(logits + (int64_t)wave * ld_l, n_experts, top_k, &id, &wt);
-      if (lane < top_k) {
-        ids_g[wave * top_k + lane] = id;
-        w_g[wave * top_k + lane] = wt;
-        ids_l[wave * top_k + lane] = id;
-      }
-    }
-    __syncthreads();
-  }
-  auto id_at = [&](int a) -> int { return FUSED ? ids_l[a] : ids_g[a]; };
+  auto id_at = [&](int a) -> int { return ids_g[a]; };
 
   for (int e = tid; e < n_experts; e += kGroupThreads) hist[e] = 0;
   for (int e = tid; e < kGroupWaves * n_experts; e += kGroupThreads) wcnt[e] = 0;
@@ -174,6 +160,71 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
   for (int p = n_valid + tid; p < n_assign; p += kGroupThreads) sorted[p] = -1;
 }
 
+// Decode-sized rows (<= kGroupWaves, so at most kFusedMaxAssign
+// assignments): top-k of each row by one wave, then, after one barrier,
+// every assignment's sorted position is its rank by (expert, index) -- the
+// stable counting sort's result -- and every expert's count and offset are
+// counted directly over the (few) ids in LDS.  No histogram atomics, no scan
+// phases.
+template <int PER_LANE>
+__global__ __launch_bounds__(kGroupThreads) void route_decode_kernel(
+    const float* __restrict__ logits, int64_t ld_l, int rows, int top_k,
+    int32_t* __restrict__ ids_g, float* __restrict__ w_g, int n_experts,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
+  __shared__ __align__(16) int ids_l[kFusedMaxAssign + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_assign = rows * top_k;
+  if (wave < rows) {
+    int id;
+    float wt;
+    topk_row<PER_LANE>(logits + (int64_t)wave * ld_l, n_experts, top_k, &id, &wt);
+    if (lane < top_k) {
+      ids_g[wave * top_k + lane] = id;
+      w_g[wave * top_k + lane] = wt;
+      ids_l[wave * top_k + lane] = id;
+    }
+  }
+  if (tid < 4) ids_l[n_assign + tid] = -1;  // pad to a multiple of 4
+  __syncthreads();
+  const int n4 = (n_assign + 3) >> 2;
+  // sorted position of assignment tid
+  if (tid < n_assign) {
+    const int e = ids_l[tid];
+    int pos = 0;
+    for (int b4 = 0; b4 < n4; ++b4) {
+      const int4 v = *(const int4*)&ids_l[4 * b4];
+      const int eb[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * b4 + q;
+        pos += (eb[q] >= 0 && (eb[q] < e || (eb[q] == e && b < tid))) ? 1 : 0;
+      }
+    }
+    if (e >= 0) sorted[pos] = tid;
+  }
+  // count and first position of every expert, and the valid total
+  for (int e = tid; e <= n_experts; e += kGroupThreads) {
+    int c = 0, o = 0;
+    for (int b4 = 0; b4 < n4; ++b4) {
+      const int4 v = *(const int4*)&ids_l[4 * b4];
+      const int eb[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c += eb[q] == e ? 1 : 0;
+        o += (eb[q] >= 0 && eb[q] < e) ? 1 : 0;
+      }
+    }
+    if (e < n_experts) counts[e] = c;
+    offsets[e] = o;  // offsets[n_experts]: every valid assignment
+  }
+  // positions past the valid ones
+  if (tid < n_assign) {
+    int n_valid = 0;
+    for (int b = 0; b < n_assign; ++b) n_valid += ids_l[b] >= 0 ? 1 : 0;
+    if (tid >= n_valid) sorted[tid] = -1;
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -199,11 +250,11 @@ extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int 
   if (rows > 0 && rows <= kGroupWaves) {
     // decode-sized: top-k and grouping in one workgroup, one launch
     if (per_lane <= 4)
-      hipLaunchKernelGGL((group_kernel<true, 4>), dim3(1), dim3(kGroupThreads), lds, s, logits,
-                         ld_l, rows, top_k, ids, w, n_assign, n_experts, counts, offsets, sorted);
+      hipLaunchKernelGGL(route_decode_kernel<4>, dim3(1), dim3(kGroupThreads), 0, s, logits, ld_l,
+                         rows, top_k, ids, w, n_experts, counts, offsets, sorted);
     else
-      hipLaunchKernelGGL((group_kernel<true, 8>), dim3(1), dim3(kGroupThreads), lds, s, logits,
-                         ld_l, rows, top_k, ids, w, n_assign, n_experts, counts, offsets, sorted);
+      hipLaunchKernelGGL(route_decode_kernel<8>, dim3(1), dim3(kGroupThreads), 0, s, logits, ld_l,
+                         rows, top_k, ids, w, n_experts, counts, offsets, sorted);
     return launch_status();
   }
   if (rows > 0) {
@@ -215,7 +266,7 @@ extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int 
       hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, ld_l, rows,
                          n_experts, top_k, ids, w);
   }
-  hipLaunchKernelGGL((group_kernel<false, 4>), dim3(1), dim3(kGroupThreads), lds, s, logits,
-                     ld_l, rows, top_k, ids, w, n_assign, n_experts, counts, offsets, sorted);
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds, s, ids, n_assign,
+                     n_experts, counts, offsets, sorted);
   return launch_status();
 }
