@@ -161,17 +161,18 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
 }
 
 // Decode-sized rows (<= kGroupWaves, so at most kFusedMaxAssign
-// assignments): top-k of each row by one wave, then, after one barrier,
-// every assignment's sorted position is its rank by (expert, index) -- the
-// stable counting sort's result -- and every expert's count and offset are
-// counted directly over the (few) ids in LDS.  No histogram atomics, no scan
-// phases.
+// assignments): top-k of each row by one wave; then every assignment's
+// sorted position is its rank by the key expert * 256 + index -- the stable
+// counting sort's result -- and every expert's count and offset are counts
+// of keys below two bounds, one compare per key over the (few) keys in LDS.
+// No histogram atomics, no scan phases.
 template <int PER_LANE>
 __global__ __launch_bounds__(kGroupThreads) void route_decode_kernel(
     const float* __restrict__ logits, int64_t ld_l, int rows, int top_k,
     int32_t* __restrict__ ids_g, float* __restrict__ w_g, int n_experts,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
-  __shared__ __align__(16) int ids_l[kFusedMaxAssign + 4];
+  __shared__ int ids_l[kFusedMaxAssign];
+  __shared__ __align__(16) int keys_l[kFusedMaxAssign + 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_assign = rows * top_k;
   if (wave < rows) {
@@ -184,44 +185,53 @@ __global__ __launch_bounds__(kGroupThreads) void route_decode_kernel(
       ids_l[wave * top_k + lane] = id;
     }
   }
-  if (tid < 4) ids_l[n_assign + tid] = -1;  // pad to a multiple of 4
   __syncthreads();
-  const int n4 = (n_assign + 3) >> 2;
-  // sorted position of assignment tid
-  if (tid < n_assign) {
-    const int e = ids_l[tid];
-    int pos = 0;
-    for (int b4 = 0; b4 < n4; ++b4) {
-      const int4 v = *(const int4*)&ids_l[4 * b4];
-      const int eb[4] = {v.x, v.y, v.z, v.w};
+  // one sortable key per assignment: expert * 256 + index (index < 256),
+  // sentinels and padding above every key
+  constexpr int kNone = 0x7FFFFFFF;
+  const int n16 = (n_assign + 15) >> 4;
+  for (int b = tid; b < 16 * n16; b += kGroupThreads) {
+    const int e = b < n_assign ? ids_l[b] : -1;
+    keys_l[b] = e >= 0 ? e * 256 + b : kNone;
+  }
+  __syncthreads();
+  // the keys, 16 at a time (four LDS reads in flight per step)
+  auto scan = [&](auto&& f) {
+    for (int b16 = 0; b16 < n16; ++b16) {
+      int4 v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int b = 4 * b4 + q;
-        pos += (eb[q] >= 0 && (eb[q] < e || (eb[q] == e && b < tid))) ? 1 : 0;
+      for (int u = 0; u < 4; ++u) v[u] = *(const int4*)&keys_l[16 * b16 + 4 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        f(v[u].x);
+        f(v[u].y);
+        f(v[u].z);
+        f(v[u].w);
       }
     }
-    if (e >= 0) sorted[pos] = tid;
-  }
-  // count and first position of every expert, and the valid total
-  for (int e = tid; e <= n_experts; e += kGroupThreads) {
-    int c = 0, o = 0;
-    for (int b4 = 0; b4 < n4; ++b4) {
-      const int4 v = *(const int4*)&ids_l[4 * b4];
-      const int eb[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c += eb[q] == e ? 1 : 0;
-        o += (eb[q] >= 0 && eb[q] < e) ? 1 : 0;
-      }
-    }
-    if (e < n_experts) counts[e] = c;
-    offsets[e] = o;  // offsets[n_experts]: every valid assignment
-  }
-  // positions past the valid ones
+  };
+  // sorted position of assignment tid: the keys below its own; positions
+  // past the valid ones get -1
   if (tid < n_assign) {
-    int n_valid = 0;
-    for (int b = 0; b < n_assign; ++b) n_valid += ids_l[b] >= 0 ? 1 : 0;
+    const int key = keys_l[tid];
+    int pos = 0, n_valid = 0;
+    scan([&](int k) {
+      pos += k < key ? 1 : 0;
+      n_valid += k != kNone ? 1 : 0;
+    });
+    if (key != kNone) sorted[pos] = tid;
     if (tid >= n_valid) sorted[tid] = -1;
+  }
+  // count and first position of every expert (offsets[n_experts]: all valid)
+  for (int e = tid; e <= n_experts; e += kGroupThreads) {
+    const int lo = e * 256, hi = e < n_experts ? lo + 256 : kNone;
+    int below = 0, upto = 0;
+    scan([&](int k) {
+      below += k < lo ? 1 : 0;
+      upto += k < hi ? 1 : 0;
+    });
+    if (e < n_experts) counts[e] = upto - below;
+    offsets[e] = below;
   }
 }
 
