@@ -120,9 +120,13 @@ def main():
     ffn = m.moe_ffn_prefill if prefill else m.moe_ffn_decode
 
     def step(i):
-        m.moe_quant_act_q8(xs[i % n_inputs], q=q, scales=qs)
-        ids, w, counts, offsets, srt = m.moe_route_group(lgs[i % n_inputs], L.top_k,
-                                                         out=route_out)
+        if prefill:
+            m.moe_quant_act_q8(xs[i % n_inputs], q=q, scales=qs)
+            m.moe_route_group(lgs[i % n_inputs], L.top_k, out=route_out)
+        else:  # decode rows: quantiser and router in one launch
+            m.moe_decode_prep(xs[i % n_inputs], lgs[i % n_inputs], L.top_k, q=q, scales=qs,
+                              out=route_out)
+        ids, w, counts, offsets, srt = route_out
         ffn(layers[i % sets], q, qs, ids, w, offsets, srt, y=y, ws=ws)
 
     # touched experts per input (bytes are counted from the actual routes)
@@ -353,7 +357,7 @@ def bench_matvec(args, m, synth, np, torch, dev):
                                         "rows": K},
         "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
-                         kernel="proj_kernel<matvec>", avg_us=round(us, 3)),
+                         kernel="stream_kernel<matvec>", avg_us=round(us, 3)),
         "cpu_baseline": cpu,
     }
     emit(line, args)

@@ -140,6 +140,22 @@ int moe_route_group(const float* logits, int64_t ld_l, int rows, int n_experts,
                     int top_k, int32_t* ids, float* w, int32_t* counts,
                     int32_t* offsets, int32_t* sorted, void* stream);
 
+/* Decode-step inputs in one launch: moe_quant_act_q8 of x and
+ * moe_route_group of logits for the same rows, which depend on nothing from
+ * each other ([gfx90a] Fig. 1: the router and the activation quantisation
+ * both read only the layer input; [lucebox] "Reduce expert-route overhead":
+ * per-step routing work is overhead on the decode path).  One workgroup
+ * routes and groups while the others quantise, so the step pays one launch
+ * and one round trip instead of two.  Every output has the same bits as the
+ * two separate calls.  Arguments, layouts and checks are theirs:
+ *   x, ld_x, cols, q, ld_q, scales, ld_s   as for moe_quant_act_q8 (rows rows)
+ *   logits .. sorted                      as for moe_route_group
+ * 1 <= rows <= MOE_MAX_DECODE_ROWS (else MOE_ERR_SHAPE, nothing enqueued). */
+int moe_decode_prep(const float* x, int64_t ld_x, int cols, int8_t* q, int64_t ld_q,
+                    float* scales, int64_t ld_s, const float* logits, int64_t ld_l,
+                    int rows, int n_experts, int top_k, int32_t* ids, float* w,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* One routed-expert layer ([gfx90a] Fig. 1: router top-6, shared expert and
  * FP4 routed experts gate/up -> down, partials added; §6.1 the INT8-dot MoE

@@ -21,7 +21,7 @@ MOE_MAX_DECODE_ROWS = 16
 
 EXPORTS = [
     "moe_packed_bytes", "moe_pack_mxfp4", "moe_unpack_mxfp4", "moe_quant_act_q8",
-    "moe_route_group", "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout",
+    "moe_route_group", "moe_decode_prep", "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout",
     "moe_ffn_decode", "moe_ffn_prefill", "moe_ffn_stages", "moe_matvec_mxfp4",
     "moe_debug_block_dots", "moe_status_string",
 ]
@@ -61,6 +61,8 @@ def lib():
         L.moe_unpack_mxfp4.argtypes = [P, I, I, I, P, I64, P, I64, P]
         L.moe_quant_act_q8.argtypes = [P, I64, I, I, P, I64, P, I64, P]
         L.moe_route_group.argtypes = [P, I64, I, I, I, P, P, P, P, P, P]
+        L.moe_decode_prep.argtypes = [P, I64, I, P, I64, P, I64, P, I64, I, I, I, P, P, P, P, P,
+                                      P]
         L.moe_ffn_workspace_bytes.argtypes = [C.POINTER(moe_layer_t), I]
         L.moe_ffn_workspace_bytes.restype = SZ
         L.moe_ffn_workspace_layout.argtypes = [C.POINTER(moe_layer_t), I,
@@ -163,6 +165,30 @@ def moe_route_group(logits, top_k, n_experts=None, out=None, stream=None):
     _call("moe_route_group", _ptr(logits), _ld(logits), rows, E, top_k, _ptr(ids), _ptr(w),
           _ptr(counts), _ptr(offsets), _ptr(srt), _stream(stream))
     return out
+
+
+def moe_decode_prep(x, logits, top_k, n_experts=None, q=None, scales=None, out=None,
+                    stream=None):
+    """moe_quant_act_q8(x) and moe_route_group(logits, top_k) in one launch
+    (decode rows, 1..16).  Returns (q, scales, ids, w, counts, offsets, sorted)."""
+    rows, cols = x.shape[0], x.shape[1]
+    E = logits.shape[1] if n_experts is None else n_experts
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.float32, device=dev)
+    if out is None:
+        out = (torch.empty((rows, top_k), dtype=torch.int32, device=dev),
+               torch.empty((rows, top_k), dtype=torch.float32, device=dev),
+               torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(max(rows * top_k, 1), dtype=torch.int32, device=dev))
+    ids, w, counts, offsets, srt = out
+    _call("moe_decode_prep", _ptr(x), _ld(x), cols, _ptr(q), _ld(q), _ptr(scales), _ld(scales),
+          _ptr(logits), _ld(logits), rows, E, top_k, _ptr(ids), _ptr(w), _ptr(counts),
+          _ptr(offsets), _ptr(srt), _stream(stream))
+    return (q, scales) + tuple(out)
 
 
 # --------------------------------------------------------------------- layer

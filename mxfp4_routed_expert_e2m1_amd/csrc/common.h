@@ -107,6 +107,51 @@ __device__ inline float q8_code(float v, float d) {
   return d != 0.f ? fminf(fmaxf(rintf(v / d), -127.f), 127.f) : 0.f;
 }
 
+// Activation quantiser, one thread's share: thread i of a launch-wide index
+// handles 8 consecutive elements (i / (cols/8) is the row), 4 aligned lanes
+// form one 32-element block (amax by two lane xors), d = amax / 127 in fp32
+// and q = clamp(rint(x / d), +-127) (gfx90a report §6.1: INT8 per 32
+// elements; the rounding rule is the library's reading).  Threads past the
+// data take part in the shuffles and store nothing; cols % 32 == 0 keeps a
+// 4-lane group wholly in or out.
+__device__ inline void quant_q8_thread(int64_t i, const float* __restrict__ x, int64_t ld_x,
+                                       int rows, int cols, int8_t* __restrict__ q, int64_t ld_q,
+                                       float* __restrict__ s, int64_t ld_s) {
+  const int per_row = cols / 8;
+  const int64_t total = (int64_t)rows * per_row;
+  const bool valid = i < total;
+  const int r = valid ? (int)(i / per_row) : 0;
+  const int c8 = valid ? (int)(i % per_row) : 0;
+  float v[8];
+  if (valid) {
+    const float4 a = *(const float4*)(x + (int64_t)r * ld_x + (int64_t)c8 * 8);
+    const float4 b = *(const float4*)(x + (int64_t)r * ld_x + (int64_t)c8 * 8 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  const float d = m / 127.0f;
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t byte = (uint32_t)((int32_t)q8_code(v[k], d)) & 0xFFu;
+    if (k < 4) w0 |= byte << (8 * k);
+    else w1 |= byte << (8 * (k - 4));
+  }
+  if (valid) {
+    u32x2 packed = {w0, w1};
+    *(u32x2*)(q + (int64_t)r * ld_q + (int64_t)c8 * 8) = packed;
+    if ((c8 & 3) == 0) s[(int64_t)r * ld_s + c8 / 4] = d;
+  }
+}
+
 // Max over each aligned group of 32 lanes (lanes 0-31, 32-63), returned in
 // every lane: quad swaps and the row half-mirror / mirror on DPP give each
 // 16-lane row its max, then one lane-xor-16 shuffle combines rows 0/1 and
@@ -274,6 +319,11 @@ bool device_is_gfx950();  // cached per device
 int device_cu_count();    // compute units of the current device, cached; 0 if unknown
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Argument checks of the activation quantiser (MOE_OK or the first error);
+// rows == 0 or cols == 0 passes with nothing to do.
+int quant_args_check(const float* x, int64_t ld_x, int rows, int cols, const int8_t* q,
+                     int64_t ld_q, const float* scales, int64_t ld_s);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -497,7 +497,8 @@ extern "C" int moe_matvec_mxfp4(const void* w_packed, int n_out, int d_in, const
   a.y = y;
   a.ld_y = ld_y;
   hipStream_t s = (hipStream_t)stream;
-  if (pd.rg % 2 == 0) launch_proj<PASS_MATVEC, 2>(a, 1, s);
+  if (stream_supported(a.kc_total, a.rg_total)) launch_stream(STREAM_MATVEC, a, 1, s);
+  else if (pd.rg % 2 == 0) launch_proj<PASS_MATVEC, 2>(a, 1, s);
   else launch_proj<PASS_MATVEC, 1>(a, 1, s);
   return launch_status();
 }

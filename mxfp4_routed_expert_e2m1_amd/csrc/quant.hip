@@ -17,44 +17,20 @@ __global__ __launch_bounds__(256) void quant_q8_kernel(const float* __restrict__
                                                        int rows, int cols, int8_t* __restrict__ q,
                                                        int64_t ld_q, float* __restrict__ s,
                                                        int64_t ld_s) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int per_row = cols / 8;
-  const int64_t total = (int64_t)rows * per_row;
-  // groups of 4 lanes (one block) are either all valid or all invalid
-  const bool valid = i < total;
-  const int r = valid ? (int)(i / per_row) : 0;
-  const int c8 = valid ? (int)(i % per_row) : 0;
-  float v[8];
-  if (valid) {
-    const float4 a = *(const float4*)(x + (int64_t)r * ld_x + (int64_t)c8 * 8);
-    const float4 b = *(const float4*)(x + (int64_t)r * ld_x + (int64_t)c8 * 8 + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = 0.f;
-  }
-  float m = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
-  m = fmaxf(m, __shfl_xor(m, 2, 64));
-  const float d = m / 127.0f;
-  uint32_t w0 = 0, w1 = 0;
-  if (d != 0.f) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float qf = fminf(fmaxf(rintf(v[k] / d), -127.f), 127.f);
-      const uint32_t byte = (uint32_t)((int32_t)qf) & 0xFFu;
-      if (k < 4) w0 |= byte << (8 * k);
-      else w1 |= byte << (8 * (k - 4));
-    }
-  }
-  if (valid) {
-    u32x2 packed = {w0, w1};
-    *(u32x2*)(q + (int64_t)r * ld_q + (int64_t)c8 * 8) = packed;
-    if ((c8 & 3) == 0) s[(int64_t)r * ld_s + c8 / 4] = d;
-  }
+  quant_q8_thread((int64_t)blockIdx.x * blockDim.x + threadIdx.x, x, ld_x, rows, cols, q, ld_q, s,
+                  ld_s);
+}
+
+int quant_args_check(const float* x, int64_t ld_x, int rows, int cols, const int8_t* q,
+                     int64_t ld_q, const float* scales, int64_t ld_s) {
+  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (cols % kBlock) return MOE_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_INVALID_ARG;
+  if (ld_x < cols || ld_q < cols || ld_s < cols / kBlock) return MOE_ERR_STRIDE;
+  if (!aligned(x, 16) || ld_x % 4 || !aligned(q, 8) || ld_q % 8 || !aligned(scales, 4))
+    return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
 }
 
 }  // namespace moe
@@ -63,13 +39,9 @@ using namespace moe;
 
 extern "C" int moe_quant_act_q8(const float* x, int64_t ld_x, int rows, int cols, int8_t* q,
                                 int64_t ld_q, float* scales, int64_t ld_s, void* stream) {
-  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
-  if (cols % kBlock) return MOE_ERR_SHAPE;
+  const int rc = quant_args_check(x, ld_x, rows, cols, q, ld_q, scales, ld_s);
+  if (rc != MOE_OK) return rc;
   if (rows == 0 || cols == 0) return MOE_OK;
-  if (!x || !q || !scales) return MOE_ERR_INVALID_ARG;
-  if (ld_x < cols || ld_q < cols || ld_s < cols / kBlock) return MOE_ERR_STRIDE;
-  if (!aligned(x, 16) || ld_x % 4 || !aligned(q, 8) || ld_q % 8 || !aligned(scales, 4))
-    return MOE_ERR_ALIGNMENT;
   if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
   const int64_t threads = (int64_t)rows * (cols / 8);
   hipLaunchKernelGGL(quant_q8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,

@@ -166,11 +166,28 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
 // counting sort's result -- and every expert's count and offset are counts
 // of keys below two bounds, one compare per key over the (few) keys in LDS.
 // No histogram atomics, no scan phases.
+struct RouteArgs {
+  const float* logits;
+  int64_t ld_l;
+  int rows, top_k, n_experts;
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted;
+};
+
+// The whole decode route + group, run by one workgroup of kGroupThreads.
 template <int PER_LANE>
-__global__ __launch_bounds__(kGroupThreads) void route_decode_kernel(
-    const float* __restrict__ logits, int64_t ld_l, int rows, int top_k,
-    int32_t* __restrict__ ids_g, float* __restrict__ w_g, int n_experts,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
+__device__ inline void route_decode_wg(const RouteArgs& p) {
+  const float* __restrict__ logits = p.logits;
+  const int64_t ld_l = p.ld_l;
+  const int rows = p.rows, top_k = p.top_k, n_experts = p.n_experts;
+  int32_t* __restrict__ ids_g = p.ids;
+  float* __restrict__ w_g = p.w;
+  int32_t* __restrict__ counts = p.counts;
+  int32_t* __restrict__ offsets = p.offsets;
+  int32_t* __restrict__ sorted = p.sorted;
   __shared__ int ids_l[kFusedMaxAssign];
   __shared__ __align__(16) int keys_l[kFusedMaxAssign + 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,13 +252,38 @@ __global__ __launch_bounds__(kGroupThreads) void route_decode_kernel(
   }
 }
 
-}  // namespace moe
+template <int PER_LANE>
+__global__ __launch_bounds__(kGroupThreads) void route_decode_kernel(RouteArgs p) {
+  route_decode_wg<PER_LANE>(p);
+}
 
-using namespace moe;
+struct QuantArgs {
+  const float* x;
+  int64_t ld_x;
+  int rows, cols;
+  int8_t* q;
+  int64_t ld_q;
+  float* s;
+  int64_t ld_s;
+};
 
-extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int n_experts,
-                               int top_k, int32_t* ids, float* w, int32_t* counts,
-                               int32_t* offsets, int32_t* sorted, void* stream) {
+// A decode step's two independent inputs in one launch: workgroup 0 routes
+// and groups the rows; workgroups 1.. quantise the activations (the same
+// per-thread quantiser as moe_quant_act_q8, so the codes are the same bits).
+template <int PER_LANE>
+__global__ __launch_bounds__(kGroupThreads) void prep_decode_kernel(QuantArgs qa, RouteArgs ra) {
+  if (blockIdx.x == 0) {
+    route_decode_wg<PER_LANE>(ra);
+  } else {
+    quant_q8_thread((int64_t)(blockIdx.x - 1) * kGroupThreads + threadIdx.x, qa.x, qa.ld_x,
+                    qa.rows, qa.cols, qa.q, qa.ld_q, qa.s, qa.ld_s);
+  }
+}
+
+// Argument checks of moe_route_group (MOE_OK or the first error).
+static int route_args_check(const float* logits, int64_t ld_l, int rows, int n_experts,
+                            int top_k, const int32_t* ids, const float* w, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* sorted) {
   if (rows < 0) return MOE_ERR_INVALID_ARG;
   if (n_experts < 1 || n_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (top_k < 1 || top_k > n_experts || top_k > MOE_MAX_TOP_K) return MOE_ERR_SHAPE;
@@ -252,6 +294,19 @@ extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int 
   if (!aligned(counts, 4) || !aligned(offsets, 4) || (rows > 0 && (!aligned(logits, 4) ||
       !aligned(ids, 4) || !aligned(w, 4) || !aligned(sorted, 4))))
     return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int n_experts,
+                               int top_k, int32_t* ids, float* w, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted, void* stream) {
+  const int rc = route_args_check(logits, ld_l, rows, n_experts, top_k, ids, w, counts, offsets,
+                                  sorted);
+  if (rc != MOE_OK) return rc;
   if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
   hipStream_t s = (hipStream_t)stream;
   const int per_lane = (n_experts + 63) / 64;
@@ -259,12 +314,11 @@ extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int 
   const int n_assign = rows * top_k;
   if (rows > 0 && rows <= kGroupWaves) {
     // decode-sized: top-k and grouping in one workgroup, one launch
+    const RouteArgs ra{logits, ld_l, rows, top_k, n_experts, ids, w, counts, offsets, sorted};
     if (per_lane <= 4)
-      hipLaunchKernelGGL(route_decode_kernel<4>, dim3(1), dim3(kGroupThreads), 0, s, logits, ld_l,
-                         rows, top_k, ids, w, n_experts, counts, offsets, sorted);
+      hipLaunchKernelGGL(route_decode_kernel<4>, dim3(1), dim3(kGroupThreads), 0, s, ra);
     else
-      hipLaunchKernelGGL(route_decode_kernel<8>, dim3(1), dim3(kGroupThreads), 0, s, logits, ld_l,
-                         rows, top_k, ids, w, n_experts, counts, offsets, sorted);
+      hipLaunchKernelGGL(route_decode_kernel<8>, dim3(1), dim3(kGroupThreads), 0, s, ra);
     return launch_status();
   }
   if (rows > 0) {
@@ -278,5 +332,27 @@ extern "C" int moe_route_group(const float* logits, int64_t ld_l, int rows, int 
   }
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds, s, ids, n_assign,
                      n_experts, counts, offsets, sorted);
+  return launch_status();
+}
+
+extern "C" int moe_decode_prep(const float* x, int64_t ld_x, int cols, int8_t* q, int64_t ld_q,
+                               float* scales, int64_t ld_s, const float* logits, int64_t ld_l,
+                               int rows, int n_experts, int top_k, int32_t* ids, float* w,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted, void* stream) {
+  if (rows < 1 || rows > MOE_MAX_DECODE_ROWS || rows > kGroupWaves) return MOE_ERR_SHAPE;
+  int rc = quant_args_check(x, ld_x, rows, cols, q, ld_q, scales, ld_s);
+  if (rc != MOE_OK) return rc;
+  rc = route_args_check(logits, ld_l, rows, n_experts, top_k, ids, w, counts, offsets, sorted);
+  if (rc != MOE_OK) return rc;
+  if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
+  const QuantArgs qa{x, ld_x, rows, cols, q, ld_q, scales, ld_s};
+  const RouteArgs ra{logits, ld_l, rows, top_k, n_experts, ids, w, counts, offsets, sorted};
+  const int64_t q_threads = (int64_t)rows * (cols / 8);
+  const dim3 grid((unsigned)(1 + (q_threads + kGroupThreads - 1) / kGroupThreads));
+  hipStream_t s = (hipStream_t)stream;
+  if ((n_experts + 63) / 64 <= 4)
+    hipLaunchKernelGGL(prep_decode_kernel<4>, grid, dim3(kGroupThreads), 0, s, qa, ra);
+  else
+    hipLaunchKernelGGL(prep_decode_kernel<8>, grid, dim3(kGroupThreads), 0, s, qa, ra);
   return launch_status();
 }

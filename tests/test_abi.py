@@ -98,6 +98,25 @@ def test_route_validation():
     assert f(*args(1 << 22, 256, 6)) == SHAPE
 
 
+def test_decode_prep_validation():
+    f = m.lib().moe_decode_prep
+
+    def args(rows=4, cols=64, ldx=64, ldq=64, lds=2, x=A, E=256, k=6, ldl=256, counts=A):
+        return (x, ldx, cols, A, ldq, A, lds, A, ldl, rows, E, k, A, A, counts, A, A, None)
+    assert f(*args(rows=0)) == SHAPE                  # decode rows only: 1..16
+    assert f(*args(rows=17)) == SHAPE
+    assert f(*args(cols=48, ldx=64)) == SHAPE           # quantiser checks
+    assert f(*args(x=None)) == INVALID
+    assert f(*args(ldx=32)) == STRIDE
+    assert f(*args(lds=1)) == STRIDE
+    assert f(*args(x=MIS)) == ALIGN
+    assert f(*args(ldq=68)) == ALIGN
+    assert f(*args(k=0)) == SHAPE                       # router checks
+    assert f(*args(E=8, k=9)) == SHAPE
+    assert f(*args(ldl=255)) == STRIDE
+    assert f(*args(counts=None)) == INVALID
+
+
 def _layer(**kw):
     d = dict(d_model=4096, d_ff=2048, n_experts=256, top_k=6, has_shared=1,
              gate_up=0x1000000, gate_up_stride=8912896, down=0x2000000, down_stride=4456448,

@@ -130,6 +130,54 @@ def test_route_group_zero_rows():
     assert torch.all(counts == 0) and torch.all(offsets == 0)
 
 
+def _prep_case(x, logits, k, pad=0):
+    """moe_decode_prep against the oracle (quantiser, router, grouping) and
+    bitwise against the two separate calls."""
+    rows, cols = x.shape
+    xw = torch.from_numpy(np.pad(x, ((0, 0), (0, pad)))).to(DEV)
+    xt = xw[:, :cols]
+    lg = torch.from_numpy(logits).to(DEV)
+    q_w = torch.zeros((rows, cols + 2 * pad), dtype=torch.int8, device=DEV)
+    s_w = torch.zeros((rows, cols // 32 + pad // 8), dtype=torch.float32, device=DEV)
+    q, qs, ids, w, counts, offsets, srt = m.moe_decode_prep(
+        xt, lg, k, q=q_w[:, :cols], scales=s_w[:, : cols // 32])
+    q2, qs2 = m.moe_quant_act_q8(xt)
+    ids2, w2, counts2, offsets2, srt2 = m.moe_route_group(lg, k)
+    _sync()
+    q_o, s_o = oracle.quant_q8(x)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+    np.testing.assert_array_equal(qs.cpu().numpy(), s_o)
+    ids_o, w_o = oracle.route(logits, k)
+    c_o, off_o, srt_o = oracle.group(ids_o, logits.shape[1])
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c_o)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_o)
+    np.testing.assert_array_equal(srt.cpu().numpy()[: ids_o.size], srt_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=2e-6, atol=0)
+    for a, b in ((q, q2), (qs, qs2), (ids, ids2), (w, w2), (counts, counts2),
+                 (offsets, offsets2), (srt, srt2)):
+        assert torch.equal(a, b)
+    if pad:
+        assert torch.all(q_w[:, cols:] == 0) and torch.all(s_w[:, cols // 32:] == 0)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 5, 16])
+def test_decode_prep_dsv4(rows):
+    x = synth.activations(2, 0, rows, 4096)
+    _prep_case(x, synth.router_logits(3, rows, rows, 256), 6)
+
+
+def test_decode_prep_hot_ties_shapes():
+    _prep_case(synth.activations(2, 1, 16, 4096),
+               synth.router_logits(3, 16, 16, 256, hot_bias=2.0), 6)
+    tied = np.round(synth.normal(9, 12, (7, 256)), 1).astype(np.float32)
+    x = synth.normal(9, 13, (7, 256))
+    x[:, 64:96] = 0.0                                    # a zero block
+    _prep_case(x, tied, 6, pad=64)
+    _prep_case(synth.normal(9, 14, (3, 384)), synth.normal(9, 15, (3, 512)), 16)
+    _prep_case(synth.normal(9, 16, (4, 256)), synth.router_logits(0, 0, 4, 8), 2)
+
+
 # ------------------------------------------------------ matvec / block dots
 def _matvec_inputs(n_out, d_in, rows, seed, exp=(-8, 0)):
     codes = synth.codes(synth.stream_key(seed, 1), n_out, d_in, DEV)
