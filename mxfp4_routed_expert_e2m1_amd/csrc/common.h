@@ -9,7 +9,14 @@
 // block j.  That is exactly the A-operand fragment of one 16x16x32 matrix
 // core instruction per block, so every wave load is one contiguous 1 KiB
 // burst and every nibble lands in the lane that consumes it.
-//   nibbles: [RG][KC][64 lanes][16 B]
+//   nibbles: [RG][KC slots][64 lanes][16 B]
+// Within a row group the chunks are stored interleaved by 4 when KC % 4 ==
+// 0: chunk c sits in slot (c % 4) * (KC/4) + c / 4.  The decode streams give
+// each of their KC/4 waves a run of 4 chunks (wave w: chunks 4w..4w+3) and
+// step through the runs together, so at every step the waves of a
+// workgroup read KC/4 adjacent tiles (one contiguous burst) instead of tiles
+// 4 KiB apart; on MI355X that order streamed 3-10% faster at 1-4 tokens.
+// Other KC keep chunk order.
 //   scales : [RG][SC][16 rows][16 B]   SC = ceil(K/512); byte i of row r in
 //            super-chunk s is the E8M0 byte of block 16*s + i (0-padded).
 // Gate/up matrices interleave row groups: packed group 2j = gate group j,
@@ -49,6 +56,14 @@ struct PackedDims {
   }
   __host__ __device__ int64_t total() const { return nib_bytes + scale_bytes; }
 };
+
+// chunk <-> storage slot inside a row group (see the layout above)
+__host__ __device__ inline int chunk_slot(int c, int kc) {
+  return (kc & 3) ? c : (c & 3) * (kc >> 2) + (c >> 2);
+}
+__host__ __device__ inline int slot_chunk(int s, int kc) {
+  return (kc & 3) ? s : 4 * (s % (kc >> 2)) + s / (kc >> 2);
+}
 
 // packed row group -> first canonical row
 __host__ __device__ inline int packed_group_src_row(int pr, int n_out, int interleave) {

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     const u32x4* nib = (const u32x4*)blob;
     const uint8_t* scl = blob + p.nib_bytes;
     const int kc = kg + min(kk, min(kDRGroup, p.kc_total - kg) - 1);
-    a[kk] = nib[((int64_t)rg * p.kc_total + kc) * 64 + lane];
+    a[kk] = nib[((int64_t)rg * p.kc_total + chunk_slot(kc, p.kc_total)) * 64 + lane];
     s[kk] = *(const uint32_t*)(scl + (((int64_t)rg * p.sc_total + (kc >> 2)) * 16 + col) * 16 +
                                (kc & 3) * 4);
   };

@@ -78,7 +78,7 @@ __device__ inline void wave_project(const ProjArgs& p, const uint8_t* blob, int 
     for (int kk = 0; kk < KPW; ++kk)
 #pragma unroll
       for (int g = 0; g < RGW; ++g)
-        a[kk][g] = nib[((int64_t)(pr0 + g) * p.kc_total + kc0 + kk) * 64 + lane];
+        a[kk][g] = nib[((int64_t)(pr0 + g) * p.kc_total + chunk_slot(kc0 + kk, p.kc_total)) * 64 + lane];
     uint32_t s[KPW][RGW];
     if constexpr (KPW == 4) {
 #pragma unroll
@@ -113,7 +113,7 @@ __device__ inline void wave_project(const ProjArgs& p, const uint8_t* blob, int 
     auto load_a = [&](int kc, u32x4* a, uint32_t* s) {
 #pragma unroll
       for (int g = 0; g < RGW; ++g) {
-        a[g] = nib[((int64_t)(pr0 + g) * p.kc_total + kc) * 64 + lane];
+        a[g] = nib[((int64_t)(pr0 + g) * p.kc_total + chunk_slot(kc, p.kc_total)) * 64 + lane];
         s[g] = *(const uint32_t*)(scl + (((int64_t)(pr0 + g) * p.sc_total + (kc >> 2)) * 16 +
                                          (lane & 15)) * 16 + (kc & 3) * 4);
       }
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64) void block_dots_kernel(const uint8_t* __restric
   const int lane = threadIdx.x;
   const int col = lane & 15;
   const int brow = col < rows ? col : 0;
-  const u32x4 a = ((const u32x4*)blob)[((int64_t)pr * pd.kc + kc) * 64 + lane];
+  const u32x4 a = ((const u32x4*)blob)[((int64_t)pr * pd.kc + chunk_slot(kc, (int)pd.kc)) * 64 + lane];
   const int nb = d_in / kBlock;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

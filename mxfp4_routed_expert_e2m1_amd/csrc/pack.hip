@@ -9,7 +9,7 @@
 
 namespace moe {
 
-// One thread per packed nibble dword: (pr, kc, lane, j) -> 4 canonical bytes.
+// One thread per packed nibble dword: (pr, slot, lane, j) -> 4 canonical bytes.
 __global__ void pack_nibbles_kernel(const uint8_t* __restrict__ codes, int64_t ld_codes,
                                     int n_out, int d_in, int interleave, int64_t n_words,
                                     uint32_t* __restrict__ dst) {
@@ -18,8 +18,8 @@ __global__ void pack_nibbles_kernel(const uint8_t* __restrict__ codes, int64_t l
   const int64_t kcn = d_in / kChunkK;
   const int j = (int)(i & 3);
   const int lane = (int)((i >> 2) & 63);
-  const int64_t tile = i >> 8;  // pr * KC + kc
-  const int kc = (int)(tile % kcn);
+  const int64_t tile = i >> 8;  // pr * KC + storage slot
+  const int kc = slot_chunk((int)(tile % kcn), (int)kcn);
   const int pr = (int)(tile / kcn);
   const int row = packed_group_src_row(pr, n_out, interleave) + (lane & 15);
   const int64_t byte = ((int64_t)kc * kChunkK + j * kBlock + 8 * (lane >> 4)) / 2;
@@ -35,7 +35,7 @@ __global__ void unpack_nibbles_kernel(const uint32_t* __restrict__ src, int n_ou
   const int j = (int)(i & 3);
   const int lane = (int)((i >> 2) & 63);
   const int64_t tile = i >> 8;
-  const int kc = (int)(tile % kcn);
+  const int kc = slot_chunk((int)(tile % kcn), (int)kcn);
   const int pr = (int)(tile / kcn);
   const int row = packed_group_src_row(pr, n_out, interleave) + (lane & 15);
   const int64_t byte = ((int64_t)kc * kChunkK + j * kBlock + 8 * (lane >> 4)) / 2;

@@ -126,7 +126,8 @@ __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage& S,
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rg = 2 * wave + i;
-    load_to_lds(c.nib + ((int64_t)(c.prb + rg) * p.kc_total + kc) * 64 + lane, &S.a[rg][0], 16);
+    load_to_lds(c.nib + ((int64_t)(c.prb + rg) * p.kc_total + chunk_slot(kc, p.kc_total)) * 64 + lane,
+                &S.a[rg][0], 16);
   }
   {
     const int rg = 4 * rq + g4;

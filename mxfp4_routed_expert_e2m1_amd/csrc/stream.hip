@@ -166,7 +166,10 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   const __amdgpu_buffer_rsrc_t rb_b = buf_rsrc(p.b, (uint32_t)(b_rows * p.ld_b * kBBytes));
   const __amdgpu_buffer_rsrc_t rb_d = buf_rsrc(p.bs, (uint32_t)(b_rows * p.ld_bs * 4));
   // lane offsets that do not depend on the item
-  const uint32_t a_lane = (uint32_t)(kc0 * 1024 + lane * 16);
+  // chunk kc0 + kk of a row group sits in slot W * kk + wave (KC = 4W, the
+  // interleaved chunk order of the packed layout): at each kk the waves read
+  // adjacent tiles
+  const uint32_t a_lane = (uint32_t)(wave * 1024 + lane * 16);
   const uint32_t a_gstride = (uint32_t)p.kc_total * 1024u;
   const uint32_t s_lane = (uint32_t)(((kc0 >> 2) * 16 + col) * 16);
   const uint32_t s_gstride = (uint32_t)p.sc_total * 256u;
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   };
   auto issue = [&](const Item& x, int brow, int kk) {
 #pragma unroll
-    for (int g = 0; g < RGW; ++g) a[kk][g] = buf_load16(x.w, a_lane + kk * 1024, x.a_soff + g * a_gstride);
+    for (int g = 0; g < RGW; ++g) a[kk][g] = buf_load16(x.w, a_lane + kk * W * 1024, x.a_soff + g * a_gstride);
     const uint32_t bo = (uint32_t)(brow * p.ld_b * kBBytes) + b_lane;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
