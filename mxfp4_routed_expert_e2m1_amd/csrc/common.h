@@ -267,10 +267,21 @@ struct TileMap {
 
   __device__ inline void load(const int32_t* __restrict__ offsets, int n_experts, int has_shared,
                               int rows) {
+    fetch(offsets, n_experts);
+    count(n_experts, has_shared, rows);
+  }
+
+  // the loads alone (so a caller can put other loads in the same round trip)
+  __device__ inline void fetch(const int32_t* __restrict__ offsets, int n_experts) {
     const int per = (n_experts + 63) >> 6;  // <= 8 (n_experts <= 512)
     e0 = lane_id() * per;
 #pragma unroll
     for (int i = 0; i <= 8; ++i) o[i] = (i <= per && e0 + i <= n_experts) ? offsets[e0 + i] : 0;
+  }
+
+  // the tile counts, from the fetched offsets
+  __device__ inline void count(int n_experts, int has_shared, int rows) {
+    const int per = (n_experts + 63) >> 6;
     lsum = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

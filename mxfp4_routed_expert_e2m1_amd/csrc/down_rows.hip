@@ -5,9 +5,10 @@
 // projection's cost is latency: a per-expert kernel has to store fp32
 // partials, and a combine kernel has to read them back.
 // Here a workgroup owns 16 output rows (one packed row group) of every tile.
-// Each wave issues its first tile's 16 weight chunks, then the workgroup
-// copies every hidden row of the step (codes and scales, 4.3 KB per row at
-// d_ff 2048) into LDS, so both arrive in one round trip.  Wave w streams row
+// The workgroup copies every hidden row of the step (codes and scales, 4.3
+// KB per row at d_ff 2048) into LDS in the same round trip that brings the
+// routes and the tile map; then each wave issues its first tile's weight
+// chunks and streams them with a fixed number in flight.  Wave w streams row
 // group `blockIdx.x` of tiles w, w+8, ... against the LDS copy and keeps the
 // 16x16 partial tile in LDS; when all tiles are done the workgroup adds, for
 // every token and row, the partials of the token's slots in slot order,
@@ -45,8 +46,9 @@ struct DownRowsArgs {
 
 // Dynamic LDS: partials [n_tiles][16 columns][16 rows] f32, then the hidden
 // rows of the step [R][d_ff] bf16 and their scales [R][d_ff/32] f32, R =
-// valid routed assignments + shared rows (row r < n_valid is sorted position
-// r, row n_valid + t the shared expert's row of token t).
+// rows * top_k + shared rows, in the workspace's order (row r < rows * top_k
+// is sorted position r, row rows * top_k + t the shared expert's row of
+// token t).
 // NC: 16-byte pieces of hidden codes each thread copies (a constant, so the
 // number of loads in flight is known when the copy waits).
 template <int NC>
@@ -57,42 +59,47 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   __shared__ int4 s_tiles[kMaxDecodeTiles];  // expert, start, count
   __shared__ int s_pos[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // assignment -> sorted position
   __shared__ int s_ptile[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // sorted position -> tile
-  __shared__ int s_ntiles, s_routed, s_nvalid;
+  __shared__ float s_wt[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // the step's weights
+  __shared__ int s_ntiles, s_routed;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-
-  // one round trip: this step's sorted list (positions past the valid ones
-  // hold -1), the tile map and the valid count are loaded together
-  const int n_assign = p.rows * p.top_k;  // <= kDRThreads
-  const int srt = tid < n_assign ? p.sorted[tid] : -1;
-  if (wave == 0) {
-    const int nv = p.offsets[p.n_experts];
-    TileMap<16> tm;
-    tm.load(p.offsets, p.n_experts, p.has_shared, p.rows);
-    int idx = tm.incl - tm.lsum;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      for (int r = 0; r < tm.nt[i] && idx < kMaxDecodeTiles; ++r, ++idx) {
-        const int start = tm.o[i] + 16 * r;
-        const int cnt = min(16, tm.o[i + 1] - tm.o[i] - 16 * r);
-        s_tiles[idx] = int4{tm.e0 + i, start, cnt, 0};
-        for (int c = 0; c < cnt; ++c) s_ptile[start + c] = idx;
-      }
-    const int st = tm.routed + lane;
-    if (lane < tm.shared_tiles && st < kMaxDecodeTiles)
-      s_tiles[st] = int4{p.n_experts, 16 * lane, min(16, p.rows - 16 * lane), 0};
-    if (lane == 0) {
-      s_ntiles = min(tm.n_tiles(), kMaxDecodeTiles);
-      s_routed = tm.routed;
-      s_nvalid = nv;
-    }
-  }
-  if (srt >= 0) s_pos[srt] = tid;
-  __syncthreads();
-  const int n_tiles = s_ntiles;
-  const int n_valid = s_nvalid;
   const int F = p.kc_total * kChunkK;
   const int rg = blockIdx.x;  // 16 output rows 16*rg .. 16*rg+15
   const int col = lane & 15, g8 = 8 * (lane >> 4);
+
+  // One round trip for everything the weights do not need: the sorted list
+  // (positions past the valid ones hold -1), ids and weights, the tile map,
+  // and every hidden row of the step (codes and scales).  The copy takes
+  // all A = rows * top_k routed rows (sorted positions; those past the
+  // valid count are never read) and the shared rows after them, the
+  // workspace's own order, so its addresses do not wait for the routes.
+  const int n_assign = p.rows * p.top_k;  // <= kDRThreads
+  const int R = n_assign + (p.has_shared ? p.rows : 0);
+  const int per_row = F / 8;             // 16-byte pieces of codes per row
+  const int per_row_s = F / kBlock / 4;  // 16-byte pieces of scales per row
+  const int n_pc = R * per_row, n_ps = R * per_row_s;
+  const int srt = tid < n_assign ? p.sorted[tid] : -1;
+  const int idv = tid < n_assign ? p.ids[tid] : -1;
+  const float wv = tid < n_assign ? p.w[tid] : 0.f;
+  // every wave reads the offsets and finds its own first tile, so its
+  // weights go out without waiting for a workgroup barrier
+  TileMap<16> tm;
+  tm.fetch(p.offsets, p.n_experts);
+  // (copy pieces past the end read piece 0 of hidden row 0, which always
+  // exists)
+  u32x4 cp[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int e = k * kDRThreads + tid;
+    const int64_t off = e < n_pc ? (int64_t)(e / per_row) * p.ld_h + (e % per_row) * 8 : 0;
+    cp[k] = *(const u32x4*)(p.h + off);
+  }
+  f32x4 cs;
+  {
+    const int64_t off = tid < n_ps ? (int64_t)(tid / per_row_s) * p.ld_hs + (tid % per_row_s) * 4 : 0;
+    cs = *(const f32x4*)(p.hs + off);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load of the round trip goes out first
+  tm.count(p.n_experts, p.has_shared, p.rows);
 
   // this wave's weight stream: row group rg of tile ti, K chunks kg..kg+15
   u32x4 a[kDRGroup];
@@ -114,57 +121,68 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
 #pragma unroll
     for (int kk = 0; kk < kDRAhead; ++kk) issue_chunk(te, kg, kk);
   };
+  // Every wave issues: a wave without a tile repeats tile 0's addresses
+  // (they merge with that tile's misses in L2); with no tile at all (no
+  // shared expert and every slot a sentinel) routed expert 0's row group,
+  // which always exists.  So the issue is unconditional.
+  {
+    const int total = tm.n_tiles();
+    const Tile t0 = tm.lookup(p.n_experts, p.rows, wave < total ? wave : 0);
+    const int4 te0 = t0.expert >= 0 ? int4{t0.expert, t0.start, t0.count, 0} : int4{0, 0, 0, 0};
+    issue_head(te0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Hidden rows (codes and scales) go out first, into registers, then the
-  // first tile's weights; the copy pieces are stored to LDS as soon as they
-  // land (the weights stay in flight), and the math waits only for the LDS
-  // barrier and then for each chunk's own weights.  Pieces past the end
-  // are loaded but not stored, so every thread issues NC + 1 copy loads and
-  // then the same weight loads, on every path.
-  const bool has_tile = wave < n_tiles;
-  // A wave without a tile issues the loads of tile 0; with no tile at all (no
-  // shared expert and every slot a sentinel: s_tiles is empty) the loads of
-  // routed expert 0's row group, which always exists.
-  const int4 te0 = n_tiles > 0 ? s_tiles[has_tile ? wave : 0] : int4{0, 0, 0, 0};
-  const int R = n_valid + (p.has_shared ? p.rows : 0);
+  // the tile map, positions, ids, weights and hidden rows go to LDS while
+  // the weights are in flight
+  if (wave == 0) {
+    int idx = tm.incl - tm.lsum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      for (int r = 0; r < tm.nt[i] && idx < kMaxDecodeTiles; ++r, ++idx) {
+        const int start = tm.o[i] + 16 * r;
+        const int cnt = min(16, tm.o[i + 1] - tm.o[i] - 16 * r);
+        s_tiles[idx] = int4{tm.e0 + i, start, cnt, 0};
+        for (int c = 0; c < cnt; ++c) s_ptile[start + c] = idx;
+      }
+    const int st = tm.routed + lane;
+    if (lane < tm.shared_tiles && st < kMaxDecodeTiles)
+      s_tiles[st] = int4{p.n_experts, 16 * lane, min(16, p.rows - 16 * lane), 0};
+    if (lane == 0) {
+      s_ntiles = min(tm.n_tiles(), kMaxDecodeTiles);
+      s_routed = tm.routed;
+    }
+  }
+  if (srt >= 0) s_pos[srt] = tid;
+  if (tid < n_assign) s_wt[tid] = wv;
   uint16_t* hl = (uint16_t*)(part + (size_t)tiles_cap * 256);
   float* hsl = (float*)(hl + (size_t)R * F);
-  const int per_row = F / 8;             // 16-byte pieces of codes per row
-  const int per_row_s = F / kBlock / 4;  // 16-byte pieces of scales per row
-  const int n_pc = R * per_row, n_ps = R * per_row_s;
-  auto src_row = [&](int r) -> int64_t {
-    return r < n_valid ? r : (int64_t)p.rows * p.top_k + (r - n_valid);
-  };
-  // (pieces past the end read piece 0 of hidden row 0, which always exists)
-  u32x4 cp[NC];
-#pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    const int e = k * kDRThreads + tid;
-    const int64_t off = e < n_pc ? src_row(e / per_row) * p.ld_h + (e % per_row) * 8 : 0;
-    cp[k] = *(const u32x4*)(p.h + off);
-  }
-  f32x4 cs;
-  {
-    const int64_t off = tid < n_ps ? src_row(tid / per_row_s) * p.ld_hs + (tid % per_row_s) * 4 : 0;
-    cs = *(const f32x4*)(p.hs + off);
-  }
-  // every wave issues (a wave without a tile repeats tile 0's addresses,
-  // which merge with that tile's misses in L2): a branch here would make
-  // the compiler wait for the weights before storing the copy
-  issue_head(te0, 0);
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int e = k * kDRThreads + tid;
     if (e < n_pc) *(u32x4*)(hl + (size_t)e * 8) = cp[k];
   }
   if (tid < n_ps) *(f32x4*)(hsl + (size_t)tid * 4) = cs;
-  lds_barrier();  // every copy piece is in LDS; the weights stay in flight
+  lds_barrier();  // LDS only: the weights stay in flight
+  const int n_tiles = s_ntiles;
+  // the combine's index of each assignment's partial row (-1: a sentinel),
+  // found now, while the weights are in flight: s_pos[a] becomes
+  // (tile * 16 + column) * 16 (only thread a reads or writes entry a)
+  if (tid < n_assign) {
+    int pidx = -1;
+    if (idv >= 0) {
+      const int pos = s_pos[tid];
+      const int ti = s_ptile[pos];
+      pidx = (ti * 16 + (pos - s_tiles[ti].y)) * 16;
+    }
+    s_pos[tid] = pidx;
+  }
 
   for (int ti = wave; ti < n_tiles; ti += kDRWaves) {
     const int4 te = s_tiles[ti];
     const bool shared = te.x == p.n_experts;
     const int ccol = col < te.z ? col : 0;  // columns past the tile repeat column 0
-    const int lrow = shared ? n_valid + te.y + ccol : te.y + ccol;  // row of the LDS copy
+    const int lrow = shared ? n_assign + te.y + ccol : te.y + ccol;  // row of the LDS copy
     auto load_h = [&](int kc, u32x4 (&b)[4], f32x4& d) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -212,10 +230,8 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     float v = 0.f;
     for (int s2 = 0; s2 < p.top_k; ++s2) {
       const int a2 = t * p.top_k + s2;
-      if (p.ids[a2] < 0) continue;
-      const int pos = s_pos[a2];
-      const int ti = s_ptile[pos];
-      v += p.w[a2] * part[(ti * 16 + (pos - s_tiles[ti].y)) * 16 + r];
+      const int pidx = s_pos[a2];
+      if (pidx >= 0) v += s_wt[a2] * part[pidx + r];
     }
     if (p.has_shared) {
       const int ti = s_routed + (t >> 4);

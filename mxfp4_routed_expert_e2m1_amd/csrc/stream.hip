@@ -153,9 +153,12 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
     x.s_soff = (uint32_t)p.nib_bytes + (uint32_t)pr0 * (uint32_t)p.sc_total * 256u;
     return x;
   };
-  // byte offset of this lane's B row (columns past the tile repeat column 0)
+  // this lane's B row; columns past the tile point one row past the operand,
+  // where the buffer range check returns zeros without reading memory (their
+  // outputs are never stored)
   auto brow_of = [&](const Item& x) -> int {
-    const int ccol = col < x.count ? col : 0;
+    if (col >= x.count) return PASS == STREAM_DOWN ? n_tok_assign + (p.has_shared ? p.rows : 0) : p.rows;
+    const int ccol = col;
     if (PASS == STREAM_MATVEC) return ccol;
     if (PASS == STREAM_GATEUP) return x.shared ? x.start + ccol : s_sorted[x.start + ccol] / p.top_k;
     return x.shared ? n_tok_assign + x.start + ccol : x.start + ccol;
