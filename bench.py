@@ -123,11 +123,11 @@ def main():
         if prefill:
             m.moe_quant_act_q8(xs[i % n_inputs], q=q, scales=qs)
             m.moe_route_group(lgs[i % n_inputs], L.top_k, out=route_out)
-        else:  # decode rows: quantiser and router in one launch
-            m.moe_decode_prep(xs[i % n_inputs], lgs[i % n_inputs], L.top_k, q=q, scales=qs,
-                              out=route_out)
-        ids, w, counts, offsets, srt = route_out
-        ffn(layers[i % sets], q, qs, ids, w, offsets, srt, y=y, ws=ws)
+            ids, w, counts, offsets, srt = route_out
+            ffn(layers[i % sets], q, qs, ids, w, offsets, srt, y=y, ws=ws)
+        else:  # decode: the whole step from the layer input in one call
+            m.moe_ffn_decode_step(layers[i % sets], xs[i % n_inputs], lgs[i % n_inputs], q=q,
+                                  scales=qs, route_out=route_out, y=y, ws=ws)
 
     # touched experts per input (bytes are counted from the actual routes)
     touched = []
@@ -183,8 +183,14 @@ def main():
     # projection (decode) or the gate/up GEMM (prefill)
     ids, w, counts, offsets, srt = route_out   # routes of input `last`
     n_k = sets * max(1, 64 // sets)
-    kcall = lambda i: m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
-                                       q, qs, ids, w, offsets, srt, y, ws)
+    fused1 = not prefill and T == 1   # one row: quantiser + router + gate/up, one kernel
+    if fused1:
+        kcall = lambda i: m.moe_ffn_decode_step(
+            layers[i % sets], xs[last % n_inputs], lgs[last % n_inputs], q=q, scales=qs,
+            route_out=route_out, y=y, ws=ws, stage_mask=m.MOE_STAGE_GATE_UP)
+    else:
+        kcall = lambda i: m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
+                                           q, qs, ids, w, offsets, srt, y, ws)
     g_k = capture(torch, lambda: [kcall(i) for i in range(n_k)])
     g_k.replay()
     torch.cuda.synchronize()
@@ -208,9 +214,13 @@ def main():
                     hbm_gbs=round(k_bytes / (k_us * 1e-6) / 1e9, 1))
     else:
         # gate/up weights of the touched experts, activations, hidden codes out
+        # (one row: the fp32 row and the logits in, its codes and routes out)
         k_bytes = (last_touched * gu_bytes + T * (L.d_model + L.d_model // 8)
                    + A * (L.d_ff + L.d_ff // 32 * 4))
         kname = "stream_kernel<gate/up>"
+        if fused1:
+            k_bytes += T * (L.d_model * 4 + L.n_experts * 4)
+            kname = "stream_step1_kernel<quantise + route + gate/up>"
         achieved = k_bytes / (k_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,

@@ -218,6 +218,27 @@ int moe_ffn_decode(const moe_layer_t* L, const int8_t* q, int64_t ld_q,
                    const float* w, const int32_t* offsets, const int32_t* sorted,
                    float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step from the layer input ([gfx90a] Fig. 1: the router and the
+ * quantised activations both come from the layer input and feed the routed
+ * experts; [lucebox] "Reduce expert-route overhead": per-step routing work is
+ * decode overhead): moe_quant_act_q8(x), moe_route_group(logits) and
+ * moe_ffn_decode in one call, every output written as those calls write it
+ * (same bits).
+ *   x, ld_x      f32 [rows][ld_x] (device) layer input, as for moe_quant_act_q8
+ *   logits, ld_l f32 [rows][ld_l] (device) router logits, as for moe_route_group
+ *   q .. qs      out, as moe_quant_act_q8's (and as moe_ffn_decode requires)
+ *   ids .. sorted out, as moe_route_group's
+ *   y, ws        as for moe_ffn_decode
+ * 1 <= rows <= MOE_MAX_DECODE_ROWS; every check of the three calls applies
+ * and runs before anything is enqueued.  With one row (and d_model of 1024,
+ * 2048 or 4096) the gate/up kernel quantises and routes the row itself, so
+ * the step is two launches; otherwise it is the three calls in order. */
+int moe_ffn_decode_step(const moe_layer_t* L, const float* x, int64_t ld_x,
+                        const float* logits, int64_t ld_l, int rows, int8_t* q,
+                        int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted, float* y,
+                        int64_t ld_y, void* ws, size_t ws_bytes, void* stream);
+
 
 /* Prefill chunk: same arguments and results as moe_ffn_decode for any
  * rows >= 1 (tuned for 512..4096).  Grid sizes derive from host-known bounds
@@ -247,6 +268,17 @@ int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask, const int8
                    const int32_t* ids, const float* w, const int32_t* offsets,
                    const int32_t* sorted, float* y, int64_t ld_y, void* ws,
                    size_t ws_bytes, void* stream);
+
+/* The same two stages for moe_ffn_decode_step: MOE_STAGE_GATE_UP covers the
+ * quantiser, the router and the gate/up stage (one launch with one row),
+ * MOE_STAGE_DOWN the down stage and the combine, which read what a GATE_UP
+ * stage of the same inputs left in the outputs and the workspace.  Arguments
+ * and errors as moe_ffn_decode_step; stage_mask as for moe_ffn_stages. */
+int moe_ffn_decode_step_stages(const moe_layer_t* L, int stage_mask, const float* x,
+                               int64_t ld_x, const float* logits, int64_t ld_l, int rows,
+                               int8_t* q, int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids,
+                               float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                               float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Stand-alone k-row matvec ([strix] "The exact-rows contract": the weights

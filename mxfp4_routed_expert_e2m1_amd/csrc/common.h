@@ -122,6 +122,28 @@ __device__ inline float q8_code(float v, float d) {
   return d != 0.f ? fminf(fmaxf(rintf(v / d), -127.f), 127.f) : 0.f;
 }
 
+// The quantiser's arithmetic for 8 consecutive elements of a 32-element
+// block, 4 aligned lanes per block (all 4 must call it together): amax by
+// two lane xors, d = amax / 127 in fp32, codes packed little-endian into w0
+// (elements 0-3) and w1 (4-7).  Returns d.
+__device__ inline float q8_quant8(const float (&v)[8], uint32_t& w0, uint32_t& w1) {
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  const float d = m / 127.0f;
+  w0 = 0;
+  w1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t byte = (uint32_t)((int32_t)q8_code(v[k], d)) & 0xFFu;
+    if (k < 4) w0 |= byte << (8 * k);
+    else w1 |= byte << (8 * (k - 4));
+  }
+  return d;
+}
+
 // Activation quantiser, one thread's share: thread i of a launch-wide index
 // handles 8 consecutive elements (i / (cols/8) is the row), 4 aligned lanes
 // form one 32-element block (amax by two lane xors), d = amax / 127 in fp32
@@ -147,19 +169,8 @@ __device__ inline void quant_q8_thread(int64_t i, const float* __restrict__ x, i
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = 0.f;
   }
-  float m = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
-  m = fmaxf(m, __shfl_xor(m, 2, 64));
-  const float d = m / 127.0f;
-  uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t byte = (uint32_t)((int32_t)q8_code(v[k], d)) & 0xFFu;
-    if (k < 4) w0 |= byte << (8 * k);
-    else w1 |= byte << (8 * (k - 4));
-  }
+  uint32_t w0, w1;
+  const float d = q8_quant8(v, w0, w1);
   if (valid) {
     u32x2 packed = {w0, w1};
     *(u32x2*)(q + (int64_t)r * ld_q + (int64_t)c8 * 8) = packed;
@@ -340,6 +351,53 @@ __device__ inline Tile find_tile(const int32_t* __restrict__ offsets, int n_expe
   return m.lookup(n_experts, rows, tile);
 }
 
+// -------------------------------------------------------------- routing
+// gfx90a report §3.2 (top-6 of 256 routed experts) and §5.3 (membership
+// ties broken by logical id, selected positions in a fixed order).
+// One wave: top_k picks of one row; lane s < top_k receives slot s.  Each
+// round takes the largest remaining logit (a wave max on DPP) and, among
+// the experts holding exactly that value, the lowest index (per-slot
+// ballots, lowest slot first: expert e sits in lane e % 64, slot e / 64).
+template <int PER_LANE>
+__device__ inline void topk_row(const float* __restrict__ l, int n_experts, int top_k,
+                                int* my_id, float* my_w) {
+  const int lane = lane_id();
+  float v[PER_LANE];
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = (e < n_experts) ? l[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  float my_sig = 0.f;
+  float sum = 0.f;
+  *my_id = 0;
+  for (int s = 0; s < top_k; ++s) {
+    float lv = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
+      if (ok) lv = fmaxf(lv, v[j]);
+    }
+    const float bv = wave_max(lv);
+    int be = -1;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
+      const uint64_t hit = __ballot(ok && v[j] == bv);
+      if (be < 0 && hit != 0) be = 64 * j + __ffsll((unsigned long long)hit) - 1;
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    const float sg = 1.0f / (1.0f + expf(-bv));
+    sum += sg;
+    if (lane == s) {
+      my_sig = sg;
+      *my_id = be;
+    }
+  }
+  *my_w = my_sig / sum;
+}
+
 // ------------------------------------------------------------ host side
 bool device_is_gfx950();  // cached per device
 int device_cu_count();    // compute units of the current device, cached; 0 if unknown
@@ -350,6 +408,10 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // rows == 0 or cols == 0 passes with nothing to do.
 int quant_args_check(const float* x, int64_t ld_x, int rows, int cols, const int8_t* q,
                      int64_t ld_q, const float* scales, int64_t ld_s);
+// Argument checks of the router + grouping (MOE_OK or the first error).
+int route_args_check(const float* logits, int64_t ld_l, int rows, int n_experts, int top_k,
+                     const int32_t* ids, const float* w, const int32_t* counts,
+                     const int32_t* offsets, const int32_t* sorted);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -348,6 +348,39 @@ void launch_combine(const float* P, const int32_t* ids, const float* w, int rows
                      ids, w, rows, top_k, has_shared, d_model, y, ld_y);
 }
 
+// Arguments of the gate/up projection of one call (workspace regions
+// included).
+static ProjArgs gateup_args(const moe_layer_t* L, const int8_t* q, int64_t ld_q, const float* qs,
+                            int64_t ld_qs, int rows, const int32_t* offsets,
+                            const int32_t* sorted, void* ws) {
+  const WsLayout lay = ws_layout(L, rows);
+  uint8_t* base = (uint8_t*)ws;
+  const PackedDims pd(2 * L->d_ff, L->d_model);
+  ProjArgs g{};
+  g.offsets = offsets;
+  g.sorted = sorted;
+  g.n_experts = L->n_experts;
+  g.top_k = L->top_k;
+  g.has_shared = L->has_shared;
+  g.rows = rows;
+  g.w = (const uint8_t*)L->gate_up;
+  g.w_stride = L->gate_up_stride;
+  g.w_shared = (const uint8_t*)L->shared_gate_up;
+  g.nib_bytes = pd.nib_bytes;
+  g.rg_total = (int)pd.rg;
+  g.kc_total = (int)pd.kc;
+  g.sc_total = (int)pd.sc;
+  g.b = q;
+  g.ld_b = ld_q;
+  g.bs = qs;
+  g.ld_bs = ld_qs;
+  g.h = (uint16_t*)(base + lay.hidden);
+  g.hs = (float*)(base + lay.hidden_scales);
+  g.ld_h = L->d_ff;
+  g.ld_hs = L->d_ff / kBlock;
+  return g;
+}
+
 static int ffn_run(const moe_layer_t* L, bool decode, int stages, const int8_t* q,
                    int64_t ld_q, const float* qs, int64_t ld_qs, int rows, const int32_t* ids,
                    const float* w, const int32_t* offsets, const int32_t* sorted, float* y,
@@ -368,23 +401,7 @@ static int ffn_run(const moe_layer_t* L, bool decode, int stages, const int8_t* 
 
   // gate/up + SwiGLU + requant
   if (stages & MOE_STAGE_GATE_UP) {
-    const PackedDims pd(2 * L->d_ff, L->d_model);
-    ProjArgs g = a;
-    g.w = (const uint8_t*)L->gate_up;
-    g.w_stride = L->gate_up_stride;
-    g.w_shared = (const uint8_t*)L->shared_gate_up;
-    g.nib_bytes = pd.nib_bytes;
-    g.rg_total = (int)pd.rg;
-    g.kc_total = (int)pd.kc;
-    g.sc_total = (int)pd.sc;
-    g.b = q;
-    g.ld_b = ld_q;
-    g.bs = qs;
-    g.ld_bs = ld_qs;
-    g.h = (uint16_t*)(base + lay.hidden);
-    g.hs = (float*)(base + lay.hidden_scales);
-    g.ld_h = L->d_ff;
-    g.ld_hs = L->d_ff / kBlock;
+    const ProjArgs g = gateup_args(L, q, ld_q, qs, ld_qs, rows, offsets, sorted, ws);
     if (decode && stream_supported(g.kc_total, g.rg_total)) launch_stream(STREAM_GATEUP, g, tiles, s);
     else launch_proj<PASS_GATEUP, 4>(g, tiles, s);
   }
@@ -469,6 +486,63 @@ extern "C" int moe_ffn_decode(const moe_layer_t* L, const int8_t* q, int64_t ld_
                               float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
   return ffn_entry(L, true, MOE_STAGE_ALL, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y,
                    ld_y, ws, ws_bytes, stream);
+}
+
+extern "C" int moe_decode_prep(const float* x, int64_t ld_x, int cols, int8_t* q, int64_t ld_q,
+                               float* scales, int64_t ld_s, const float* logits, int64_t ld_l,
+                               int rows, int n_experts, int top_k, int32_t* ids, float* w,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted, void* stream);
+
+extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, const float* x,
+                                          int64_t ld_x, const float* logits, int64_t ld_l,
+                                          int rows, int8_t* q, int64_t ld_q, float* qs,
+                                          int64_t ld_qs, int32_t* ids, float* w, int32_t* counts,
+                                          int32_t* offsets, int32_t* sorted, float* y,
+                                          int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
+  if (stages <= 0 || stages > MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
+  int rc = check_layer(L);
+  if (rc != MOE_OK) return rc;
+  if (rows < 1 || rows > MOE_MAX_DECODE_ROWS) return MOE_ERR_SHAPE;
+  rc = quant_args_check(x, ld_x, rows, L->d_model, q, ld_q, qs, ld_qs);
+  if (rc != MOE_OK) return rc;
+  rc = route_args_check(logits, ld_l, rows, L->n_experts, L->top_k, ids, w, counts, offsets,
+                        sorted);
+  if (rc != MOE_OK) return rc;
+  rc = check_acts(q, ld_q, qs, ld_qs, L->d_model, y, ld_y, L->d_model);
+  if (rc != MOE_OK) return rc;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < ws_layout(L, rows).total) return MOE_ERR_WORKSPACE;
+  if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
+  hipStream_t s = (hipStream_t)stream;
+  const ProjArgs g = gateup_args(L, q, ld_q, qs, ld_qs, rows, offsets, sorted, ws);
+  if (rows == 1 && stream_supported(g.kc_total, g.rg_total)) {
+    // one launch quantises, routes and runs gate/up; then the down stage
+    if (stages & MOE_STAGE_GATE_UP) {
+      const StepIn in{x, logits, q, qs, ids, w, counts, offsets, sorted};
+      launch_stream_step1(g, in, s);
+    }
+    if (!(stages & MOE_STAGE_DOWN)) return launch_status();
+    return ffn_run(L, true, MOE_STAGE_DOWN, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y,
+                   ld_y, ws, s);
+  }
+  if (stages & MOE_STAGE_GATE_UP) {
+    rc = moe_decode_prep(x, ld_x, L->d_model, q, ld_q, qs, ld_qs, logits, ld_l, rows,
+                         L->n_experts, L->top_k, ids, w, counts, offsets, sorted, stream);
+    if (rc != MOE_OK) return rc;
+  }
+  return ffn_run(L, true, stages, q, ld_q, qs, ld_qs, rows, ids, w, offsets, sorted, y, ld_y, ws,
+                 s);
+}
+
+extern "C" int moe_ffn_decode_step(const moe_layer_t* L, const float* x, int64_t ld_x,
+                                   const float* logits, int64_t ld_l, int rows, int8_t* q,
+                                   int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids, float* w,
+                                   int32_t* counts, int32_t* offsets, int32_t* sorted, float* y,
+                                   int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
+  return moe_ffn_decode_step_stages(L, MOE_STAGE_ALL, x, ld_x, logits, ld_l, rows, q, ld_q, qs,
+                                    ld_qs, ids, w, counts, offsets, sorted, y, ld_y, ws, ws_bytes,
+                                    stream);
 }
 
 extern "C" int moe_matvec_mxfp4(const void* w_packed, int n_out, int d_in, const int8_t* q,

@@ -64,6 +64,23 @@ bool stream_supported(int kc_total, int rg_total);
 // tiles_bound: an upper bound on the call's tiles (1 for MATVEC)
 void launch_stream(int pass, const ProjArgs& a, int tiles_bound, hipStream_t s);
 
+// A one-row decode step from the layer input (x row, router logits): the
+// gate/up stream quantises and routes the row itself and writes the
+// quantiser's and the router's outputs (device pointers, row 0 only).
+struct StepIn {
+  const float* x;       // [d_model]
+  const float* logits;  // [n_experts]
+  int8_t* q;            // out [d_model]
+  float* qs;            // out [d_model / 32]
+  int32_t* ids;         // out [top_k]
+  float* w;             // out [top_k]
+  int32_t* counts;      // out [n_experts]
+  int32_t* offsets;     // out [n_experts + 1]
+  int32_t* sorted;      // out [top_k]
+};
+// needs stream_supported(kc_total, rg_total) for the gate/up matrix
+void launch_stream_step1(const ProjArgs& a, const StepIn& in, hipStream_t s);
+
 // y = weighted combine of the partials (slot order, shared expert last)
 void launch_combine(const float* P, const int32_t* ids, const float* w, int rows, int top_k,
                     int has_shared, int d_model, float* y, int64_t ld_y, hipStream_t s);

@@ -26,50 +26,6 @@ constexpr int kMaxExperts = 512;  // keeps the grouping LDS under 64 KiB
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 
-// One wave: top_k picks of one row; lane s < top_k receives slot s.  Each
-// round takes the largest remaining logit (a wave max on DPP) and, among
-// the experts holding exactly that value, the lowest index (per-slot
-// ballots, lowest slot first: expert e sits in lane e % 64, slot e / 64).
-template <int PER_LANE>
-__device__ inline void topk_row(const float* __restrict__ l, int n_experts, int top_k,
-                                int* my_id, float* my_w) {
-  const int lane = lane_id();
-  float v[PER_LANE];
-#pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = (e < n_experts) ? l[e] : -INFINITY;
-  }
-  uint32_t taken = 0;
-  float my_sig = 0.f;
-  float sum = 0.f;
-  *my_id = 0;
-  for (int s = 0; s < top_k; ++s) {
-    float lv = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
-      if (ok) lv = fmaxf(lv, v[j]);
-    }
-    const float bv = wave_max(lv);
-    int be = -1;
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
-      const uint64_t hit = __ballot(ok && v[j] == bv);
-      if (be < 0 && hit != 0) be = 64 * j + __ffsll((unsigned long long)hit) - 1;
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    const float sg = 1.0f / (1.0f + expf(-bv));
-    sum += sg;
-    if (lane == s) {
-      my_sig = sg;
-      *my_id = be;
-    }
-  }
-  *my_w = my_sig / sum;
-}
-
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                          int64_t ld_l, int rows, int n_experts,
@@ -280,8 +236,7 @@ __global__ __launch_bounds__(kGroupThreads) void prep_decode_kernel(QuantArgs qa
   }
 }
 
-// Argument checks of moe_route_group (MOE_OK or the first error).
-static int route_args_check(const float* logits, int64_t ld_l, int rows, int n_experts,
+int route_args_check(const float* logits, int64_t ld_l, int rows, int n_experts,
                             int top_k, const int32_t* ids, const float* w, const int32_t* counts,
                             const int32_t* offsets, const int32_t* sorted) {
   if (rows < 0) return MOE_ERR_INVALID_ARG;

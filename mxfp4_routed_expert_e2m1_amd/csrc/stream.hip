@@ -72,9 +72,12 @@ __device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint3
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-template <int PASS, int W>
-__global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
+// F1 (gate/up only): a one-row step straight from the layer input; see the
+// prologue.
+template <int PASS, int W, bool F1>
+__device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
   constexpr int RGW = kSRGW, KPW = kSKPW, NT = W * 64;
+  static_assert(!F1 || PASS == STREAM_GATEUP, "the one-row step fuses gate/up only");
   static_assert(PASS != STREAM_GATEUP || RGW == 4, "gate/up needs 2 gate/up pairs = 32 features");
   using BV = std::conditional_t<PASS == STREAM_DOWN, u32x4, u32x2>;
   constexpr int kBBytes = PASS == STREAM_DOWN ? 2 : 1;  // bytes per B element
@@ -83,6 +86,10 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   __shared__ int4 s_tiles[PASS == STREAM_MATVEC ? 1 : kMaxDecodeTiles];  // expert, start, count
   __shared__ int s_ntiles;
   __shared__ uint32_t s_amax[2][16];  // gate/up: per-column amax bits, by reduction buffer
+  // F1: the row's int8 codes and scales (K <= 4096), its picked experts
+  __shared__ __align__(16) uint8_t s_q8[F1 ? 4096 : 1];
+  __shared__ __align__(16) float s_qs[F1 ? 128 : 1];
+  __shared__ int s_rid[F1 ? MOE_MAX_TOP_K : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15;
   const int n_rb = p.rg_total / RGW;
@@ -91,7 +98,69 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
 
   // The call's tiles (one round trip, wave 0) and sorted list go to LDS.
   int n_items = n_rb;
-  if constexpr (PASS != STREAM_MATVEC) {
+  if constexpr (F1) {
+    // One row, straight from the layer input.  Every workgroup quantises the
+    // row into LDS (one 8-element piece per thread: K/8 = NT) and wave 0
+    // routes it (top-k of the logits), all in one round trip, so no earlier
+    // launch has to finish first.  With one row every picked expert is a
+    // tile of one column and its sorted position is its rank by expert id
+    // (the picks are distinct); the shared expert's tile follows.
+    // Workgroup 0 also writes what the quantiser and the router would:
+    // codes, scales, ids, weights, counts, offsets, sorted.
+    float v[8];
+    {
+      const float4 x0 = *(const float4*)(in.x + 8 * tid);
+      const float4 x1 = *(const float4*)(in.x + 8 * tid + 4);
+      v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+      v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+    }
+    int my_id = 0;
+    float my_w = 0.f;
+    if (wave == 0) {
+      if (p.n_experts <= 256) topk_row<4>(in.logits, p.n_experts, p.top_k, &my_id, &my_w);
+      else topk_row<8>(in.logits, p.n_experts, p.top_k, &my_id, &my_w);
+    }
+    uint32_t w0, w1;
+    const float dq = q8_quant8(v, w0, w1);
+    *(u32x2*)(s_q8 + 8 * tid) = u32x2{w0, w1};
+    if ((tid & 3) == 0) s_qs[tid >> 2] = dq;
+    if (blockIdx.x == 0) {
+      *(u32x2*)(in.q + 8 * tid) = u32x2{w0, w1};
+      if ((tid & 3) == 0) in.qs[tid >> 2] = dq;
+    }
+    if (tid < 32) s_amax[tid >> 4][tid & 15] = 0u;
+    if (wave == 0) {
+      int rank = 0;
+      for (int s2 = 0; s2 < p.top_k; ++s2) rank += __shfl(my_id, s2, 64) < my_id ? 1 : 0;
+      if (lane < p.top_k) {
+        s_sorted[rank] = lane;
+        s_tiles[rank] = int4{my_id, rank, 1, 0};
+        s_rid[lane] = my_id;
+        if (blockIdx.x == 0) {
+          in.ids[lane] = my_id;
+          in.w[lane] = my_w;
+          in.sorted[rank] = lane;
+        }
+      }
+      if (lane == 0) {
+        if (p.has_shared) s_tiles[p.top_k] = int4{p.n_experts, 0, 1, 0};
+        s_ntiles = p.top_k + p.has_shared;
+      }
+    }
+    lds_barrier();
+    if (blockIdx.x == 0) {
+      for (int e = tid; e <= p.n_experts; e += NT) {
+        int below = 0, same = 0;
+        for (int s2 = 0; s2 < p.top_k; ++s2) {
+          below += s_rid[s2] < e ? 1 : 0;
+          same += s_rid[s2] == e ? 1 : 0;
+        }
+        in.offsets[e] = below;
+        if (e < p.n_experts) in.counts[e] = same;
+      }
+    }
+    n_items = uniform(s_ntiles) * n_rb;
+  } else if constexpr (PASS != STREAM_MATVEC) {
     // sorted list and tile map are loaded together: one round trip
     constexpr int NS = (MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K + NT - 1) / NT;
     int srt[NS];
@@ -190,14 +259,23 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   auto issue = [&](const Item& x, int brow, int kk) {
 #pragma unroll
     for (int g = 0; g < RGW; ++g) a[kk][g] = buf_load16(x.w, a_lane + kk * W * 1024, x.a_soff + g * a_gstride);
-    const uint32_t bo = (uint32_t)(brow * p.ld_b * kBBytes) + b_lane;
+    if constexpr (F1) {
+      // the row from LDS, in every column: columns past the tile's one are
+      // computed alike and never stored (and their amax is their own)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t o = bo + (kk * kChunkK + j * kBlock) * kBBytes;
-      if constexpr (PASS == STREAM_DOWN) b[kk][j] = buf_load16(rb_b, o, 0);
-      else b[kk][j] = buf_load8(rb_b, o, 0);
+      for (int j = 0; j < 4; ++j)
+        b[kk][j] = *(const u32x2*)(s_q8 + (kc0 + kk) * kChunkK + j * kBlock + 8 * (lane >> 4));
+      d[kk] = *(const f32x4*)(s_qs + (kc0 + kk) * 4);
+    } else {
+      const uint32_t bo = (uint32_t)(brow * p.ld_b * kBBytes) + b_lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t o = bo + (kk * kChunkK + j * kBlock) * kBBytes;
+        if constexpr (PASS == STREAM_DOWN) b[kk][j] = buf_load16(rb_b, o, 0);
+        else b[kk][j] = buf_load8(rb_b, o, 0);
+      }
+      d[kk] = __builtin_bit_cast(f32x4, buf_load16(rb_d, (uint32_t)(brow * p.ld_bs * 4 + (kc0 + kk) * 16), 0));
     }
-    d[kk] = __builtin_bit_cast(f32x4, buf_load16(rb_d, (uint32_t)(brow * p.ld_bs * 4 + (kc0 + kk) * 16), 0));
   };
   auto compute = [&](int kk, const u32x4 (&sc4)[RGW], f32x4 (&acc)[RGW]) {
 #pragma unroll
@@ -339,6 +417,16 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   else step(std::false_type{}, cur, sv, sv_n);
 }
 
+template <int PASS, int W>
+__global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
+  stream_body<PASS, W, false>(p, StepIn{});
+}
+
+template <int W>
+__global__ __launch_bounds__(W * 64, 2) void stream_step1_kernel(ProjArgs p, StepIn in) {
+  stream_body<STREAM_GATEUP, W, true>(p, in);
+}
+
 // KPW = 4 chunks per wave: K/128 = 4W for W = 2, 4, 8 waves.
 bool stream_supported(int kc_total, int rg_total) {
   return (kc_total == 8 || kc_total == 16 || kc_total == 32) && rg_total % kSRGW == 0;
@@ -359,6 +447,23 @@ static void launch_stream_w(const ProjArgs& a, int items_bound, hipStream_t s) {
       return;
     default:
       hipLaunchKernelGGL((stream_kernel<PASS, 2>), dim3(grid(4)), dim3(128), 0, s, a);
+      return;
+  }
+}
+
+void launch_stream_step1(const ProjArgs& a, const StepIn& in, hipStream_t s) {
+  const int items = (a.top_k + a.has_shared) * (a.rg_total / kSRGW);
+  const int cus = std::max(1, device_cu_count());
+  auto grid = [&](int wgs_per_cu) { return (unsigned)std::max(1, std::min(items, cus * wgs_per_cu)); };
+  switch (a.kc_total) {
+    case 32:
+      hipLaunchKernelGGL(stream_step1_kernel<8>, dim3(grid(1)), dim3(512), 0, s, a, in);
+      return;
+    case 16:
+      hipLaunchKernelGGL(stream_step1_kernel<4>, dim3(grid(2)), dim3(256), 0, s, a, in);
+      return;
+    default:
+      hipLaunchKernelGGL(stream_step1_kernel<2>, dim3(grid(4)), dim3(128), 0, s, a, in);
       return;
   }
 }

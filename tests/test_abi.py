@@ -117,6 +117,30 @@ def test_decode_prep_validation():
     assert f(*args(counts=None)) == INVALID
 
 
+def test_decode_step_validation():
+    f = m.lib().moe_ffn_decode_step
+    lay = _layer()
+
+    def args(rows=1, x=A, ldx=4096, ldl=256, ldq=4096, ldqs=128, counts=A, y=A, ldy=4096,
+             ws=A, wsb=1 << 30):
+        return (C.byref(lay), x, ldx, A, ldl, rows, A, ldq, A, ldqs, A, A, counts, A, A, y, ldy,
+                ws, wsb, None)
+    assert f(*args(rows=0)) == SHAPE
+    assert f(*args(rows=17)) == SHAPE
+    assert f(*args(x=None)) == INVALID                  # quantiser checks
+    assert f(*args(ldx=4000)) == STRIDE
+    assert f(*args(x=MIS)) == ALIGN
+    assert f(*args(ldl=255)) == STRIDE                  # router checks
+    assert f(*args(counts=None)) == INVALID
+    assert f(*args(ldqs=130)) == ALIGN                  # FFN checks
+    assert f(*args(y=None)) == INVALID
+    assert f(*args(ldy=4095)) == STRIDE
+    assert f(*args(ws=None)) == INVALID
+    assert f(*args(ws=MIS)) == ALIGN
+    assert f(*args(wsb=1000)) == WORKSPACE
+    assert f(C.byref(_layer(top_k=0)), *args()[1:]) == SHAPE
+
+
 def _layer(**kw):
     d = dict(d_model=4096, d_ff=2048, n_experts=256, top_k=6, has_shared=1,
              gate_up=0x1000000, gate_up_stride=8912896, down=0x2000000, down_stride=4456448,

@@ -70,6 +70,18 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
     if entry == "stages":  # decode as two stage calls (gate/up, then down + combine)
         y = m.moe_ffn_stages(layer, 0, m.MOE_STAGE_ALL, q, qs, ids, w, offsets, srt,
                              yw[:, : L.d_model], ws)
+    elif entry == "step":  # from the layer input; its own outputs must equal the calls'
+        qw2 = torch.full((T, L.d_model + pad_q), 7, dtype=torch.int8, device=DEV)
+        sw2 = torch.full((T, L.d_model // 32 + pad_q // 8), 7.0, device=DEV)
+        outs = m.moe_ffn_decode_step(layer, xw[:, : L.d_model], torch.from_numpy(logits).to(DEV),
+                                     q=qw2[:, : L.d_model], scales=sw2[:, : L.d_model // 32],
+                                     y=yw[:, : L.d_model], ws=ws)
+        y = outs[-1]
+        torch.cuda.synchronize()
+        for got, want in zip(outs[:7], (q, qs, ids, w, counts, offsets, srt)):
+            assert torch.equal(got, want)
+        if pad_q:
+            assert torch.all(qw2[:, L.d_model:] == 7) and torch.all(sw2[:, L.d_model // 32:] == 7)
     else:
         y = getattr(m, entry)(layer, q, qs, ids, w, offsets, srt, y=yw[:, : L.d_model], ws=ws)
     torch.cuda.synchronize()
@@ -372,6 +384,69 @@ def test_decode_one_row_other_shapes(shape):
     x = synth.activations(seed, 1, 1, L.d_model)
     lg = synth.router_logits(seed, 1, 1, L.n_experts)
     run_case(L, seed, x, lg)
+
+
+@pytest.mark.parametrize("step", [0, 1])
+def test_decode_step_one_row(step):
+    # the whole step from the layer input; one row: quantiser and router inside
+    # the gate/up kernel (padded strides on the second case)
+    c = synth.DECODE
+    x = synth.activations(c["seed"], 500 + step, 1, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 500 + step, 1, DSV4.n_experts)
+    run_case(DSV4, c["seed"], x, lg, entry="step", pads=(16, 64, 32) if step else (0, 0, 0))
+
+
+@pytest.mark.parametrize("shape", range(len(OTHER_SHAPES)))
+@pytest.mark.parametrize("rows", [1, 5])
+def test_decode_step_other_shapes(shape, rows):
+    # d_model 2048 / 1024 take the fused one-row kernel (4 and 2 waves, with and
+    # without a shared expert); 8192 and every rows > 1 the three calls
+    L = OTHER_SHAPES[shape]
+    seed = 51 + shape
+    x = synth.activations(seed, rows, rows, L.d_model)
+    lg = synth.router_logits(seed, rows, rows, L.n_experts)
+    run_case(L, seed, x, lg, entry="step")
+
+
+def test_decode_step_tiny_and_hot():
+    x = synth.activations(43, 1, 4, TINY.d_model)
+    run_case(TINY, 43, x[:1], synth.router_logits(43, 1, 1, TINY.n_experts), entry="step")
+    run_case(TINY, 43, x, synth.router_logits(43, 2, 4, TINY.n_experts), entry="step")
+    c = synth.DECODE_BATCH
+    x = synth.activations(c["seed"], 600, 12, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 600, 12, DSV4.n_experts, hot_bias=2.0)
+    run_case(DSV4, c["seed"], x, lg, entry="step", sample=[0, 5, 11])
+
+
+def test_decode_step_graph_replays_match_eager():
+    c = synth.DECODE
+    layer = layer_for(DSV4, c["seed"])
+    xs = [torch.from_numpy(synth.activations(c["seed"], 700 + i, 1, DSV4.d_model)).to(DEV)
+          for i in range(2)]
+    lgs = [torch.from_numpy(synth.router_logits(c["seed"], 700 + i, 1, DSV4.n_experts)).to(DEV)
+           for i in range(2)]
+    ws = torch.empty(m.moe_ffn_workspace_bytes(layer, 1), dtype=torch.uint8, device=DEV)
+    outs = m.moe_ffn_decode_step(layer, xs[0], lgs[0], ws=ws)
+    eager = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        m.moe_ffn_decode_step(layer, xs[0], lgs[0], *outs[:2], route_out=outs[2:7], y=outs[7],
+                              ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        m.moe_ffn_decode_step(layer, xs[0], lgs[0], *outs[:2], route_out=outs[2:7], y=outs[7],
+                              ws=ws)
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {r}"
+        other = m.moe_ffn_decode_step(layer, xs[1], lgs[1])  # unrelated eager step
+        torch.cuda.synchronize()
+        assert torch.isfinite(other[-1]).all()
 
 
 def test_decode_one_row_tiny_and_odd():
