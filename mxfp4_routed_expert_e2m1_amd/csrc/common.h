@@ -369,9 +369,8 @@ __device__ inline void topk_row(const float* __restrict__ l, int n_experts, int 
     v[j] = (e < n_experts) ? l[e] : -INFINITY;
   }
   uint32_t taken = 0;
-  float my_sig = 0.f;
-  float sum = 0.f;
-  *my_id = 0;
+  float my_v = 0.f;
+  int id = 0;
   for (int s = 0; s < top_k; ++s) {
     float lv = -INFINITY;
 #pragma unroll
@@ -388,13 +387,18 @@ __device__ inline void topk_row(const float* __restrict__ l, int n_experts, int 
       if (be < 0 && hit != 0) be = 64 * j + __ffsll((unsigned long long)hit) - 1;
     }
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    const float sg = 1.0f / (1.0f + expf(-bv));
-    sum += sg;
     if (lane == s) {
-      my_sig = sg;
-      *my_id = be;
+      my_v = bv;
+      id = be;
     }
   }
+  // the weights off the selection's critical path: each pick's sigmoid in
+  // its own lane, then their sum in pick order (the same fp32 operations in
+  // the same order as summing inside the rounds)
+  const float my_sig = 1.0f / (1.0f + expf(-my_v));
+  float sum = 0.f;
+  for (int s = 0; s < top_k; ++s) sum += __shfl(my_sig, s, 64);
+  *my_id = id;
   *my_w = my_sig / sum;
 }
 

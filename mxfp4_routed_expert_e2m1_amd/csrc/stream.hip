@@ -74,7 +74,7 @@ __device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint3
 
 // F1 (gate/up only): a one-row step straight from the layer input; see the
 // prologue.
-template <int PASS, int W, bool F1>
+template <int PASS, int W, bool F1, int TOPK_PL = 4>
 __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
   constexpr int RGW = kSRGW, KPW = kSKPW, NT = W * 64;
   static_assert(!F1 || PASS == STREAM_GATEUP, "the one-row step fuses gate/up only");
@@ -116,10 +116,7 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
     }
     int my_id = 0;
     float my_w = 0.f;
-    if (wave == 0) {
-      if (p.n_experts <= 256) topk_row<4>(in.logits, p.n_experts, p.top_k, &my_id, &my_w);
-      else topk_row<8>(in.logits, p.n_experts, p.top_k, &my_id, &my_w);
-    }
+    if (wave == 0) topk_row<TOPK_PL>(in.logits, p.n_experts, p.top_k, &my_id, &my_w);
     uint32_t w0, w1;
     const float dq = q8_quant8(v, w0, w1);
     *(u32x2*)(s_q8 + 8 * tid) = u32x2{w0, w1};
@@ -422,9 +419,10 @@ __global__ __launch_bounds__(W * 64, 2) void stream_kernel(ProjArgs p) {
   stream_body<PASS, W, false>(p, StepIn{});
 }
 
-template <int W>
+// PL: logits per lane of the router's wave (n_experts <= 64 * PL)
+template <int W, int PL>
 __global__ __launch_bounds__(W * 64, 2) void stream_step1_kernel(ProjArgs p, StepIn in) {
-  stream_body<STREAM_GATEUP, W, true>(p, in);
+  stream_body<STREAM_GATEUP, W, true, PL>(p, in);
 }
 
 // KPW = 4 chunks per wave: K/128 = 4W for W = 2, 4, 8 waves.
@@ -455,15 +453,19 @@ void launch_stream_step1(const ProjArgs& a, const StepIn& in, hipStream_t s) {
   const int items = (a.top_k + a.has_shared) * (a.rg_total / kSRGW);
   const int cus = std::max(1, device_cu_count());
   auto grid = [&](int wgs_per_cu) { return (unsigned)std::max(1, std::min(items, cus * wgs_per_cu)); };
+  const bool pl4 = a.n_experts <= 256;
   switch (a.kc_total) {
     case 32:
-      hipLaunchKernelGGL(stream_step1_kernel<8>, dim3(grid(1)), dim3(512), 0, s, a, in);
+      if (pl4) hipLaunchKernelGGL((stream_step1_kernel<8, 4>), dim3(grid(1)), dim3(512), 0, s, a, in);
+      else hipLaunchKernelGGL((stream_step1_kernel<8, 8>), dim3(grid(1)), dim3(512), 0, s, a, in);
       return;
     case 16:
-      hipLaunchKernelGGL(stream_step1_kernel<4>, dim3(grid(2)), dim3(256), 0, s, a, in);
+      if (pl4) hipLaunchKernelGGL((stream_step1_kernel<4, 4>), dim3(grid(2)), dim3(256), 0, s, a, in);
+      else hipLaunchKernelGGL((stream_step1_kernel<4, 8>), dim3(grid(2)), dim3(256), 0, s, a, in);
       return;
     default:
-      hipLaunchKernelGGL(stream_step1_kernel<2>, dim3(grid(4)), dim3(128), 0, s, a, in);
+      if (pl4) hipLaunchKernelGGL((stream_step1_kernel<2, 4>), dim3(grid(4)), dim3(128), 0, s, a, in);
+      else hipLaunchKernelGGL((stream_step1_kernel<2, 8>), dim3(grid(4)), dim3(128), 0, s, a, in);
       return;
   }
 }
