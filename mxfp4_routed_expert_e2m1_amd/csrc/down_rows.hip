@@ -261,14 +261,18 @@ static int copy_pieces(const moe_layer_t* L, int rows) {
   return (r_max * (L->d_ff / 8) + kDRThreads - 1) / kDRThreads;
 }
 
-// Measured on MI355X (DS-V4 layer, FFN of one step): 1 row 35.5 vs 38.1 us
-// for the per-expert kernels + combine; 2 rows 61.0 vs 56.8, 3 rows 79.6 vs
-// 74.7 -- so one row only.  The copy takes at most 8 code pieces and one
-// scale piece per thread.
+// Rows up to DOWN_ROWS_MAX: measured on MI355X against the streaming down
+// kernel + combine (DS-V4 layer): 2 rows 16.6 vs 21.2 us for the down stage,
+// whole steps 63.7 vs 66.1 us at 3 rows and 79.2 vs 80.9 us at 4; at 5 rows
+// and more the hidden rows no longer fit in LDS next to the partials.  The
+// copy takes at most 16 code pieces and one scale piece per thread.
+#ifndef DOWN_ROWS_MAX
+#define DOWN_ROWS_MAX 4
+#endif
 bool down_rows_supported(const moe_layer_t* L, int rows) {
   const int r_max = rows * L->top_k + (L->has_shared ? rows : 0);
-  return rows == 1 && down_rows_lds(L, rows) <= kDownRowsMaxLds &&
-         copy_pieces(L, rows) <= 8 && r_max * (L->d_ff / kBlock / 4) <= kDRThreads;
+  return rows <= DOWN_ROWS_MAX && down_rows_lds(L, rows) <= kDownRowsMaxLds &&
+         copy_pieces(L, rows) <= 16 && r_max * (L->d_ff / kBlock / 4) <= kDRThreads;
 }
 
 int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const float* w,
@@ -298,10 +302,13 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
   a.ld_y = ld_y;
   const size_t lds = down_rows_lds(L, rows);
   if (lds > (size_t)kDownRowsMaxLds) return MOE_ERR_SHAPE;
-  const int nc = copy_pieces(L, rows);
-  if (nc < 1 || nc > 8) return MOE_ERR_SHAPE;
+  // the copy's pieces per thread, a template constant: 1..8, else 12 or 16
+  // (pieces past the end are dummy loads, never stored)
+  int nc = copy_pieces(L, rows);
+  if (nc < 1 || nc > 16) return MOE_ERR_SHAPE;
+  if (nc > 8) nc = nc <= 12 ? 12 : 16;
   // allow more than 64 KiB of dynamic LDS: once per device and variant
-  static bool lds_raised[64][9] = {};
+  static bool lds_raised[64][17] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
   const void* fn = nullptr;
@@ -313,7 +320,9 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
     case 5: fn = (const void*)down_rows_kernel<5>; break;
     case 6: fn = (const void*)down_rows_kernel<6>; break;
     case 7: fn = (const void*)down_rows_kernel<7>; break;
-    default: fn = (const void*)down_rows_kernel<8>; break;
+    case 8: fn = (const void*)down_rows_kernel<8>; break;
+    case 12: fn = (const void*)down_rows_kernel<12>; break;
+    default: fn = (const void*)down_rows_kernel<16>; break;
   }
   if (!lds_raised[dev][nc]) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDownRowsMaxLds) !=
@@ -331,7 +340,9 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
     case 5: hipLaunchKernelGGL(down_rows_kernel<5>, grid, block, lds, s, a, cap); break;
     case 6: hipLaunchKernelGGL(down_rows_kernel<6>, grid, block, lds, s, a, cap); break;
     case 7: hipLaunchKernelGGL(down_rows_kernel<7>, grid, block, lds, s, a, cap); break;
-    default: hipLaunchKernelGGL(down_rows_kernel<8>, grid, block, lds, s, a, cap); break;
+    case 8: hipLaunchKernelGGL(down_rows_kernel<8>, grid, block, lds, s, a, cap); break;
+    case 12: hipLaunchKernelGGL(down_rows_kernel<12>, grid, block, lds, s, a, cap); break;
+    default: hipLaunchKernelGGL(down_rows_kernel<16>, grid, block, lds, s, a, cap); break;
   }
   return launch_status();
 }
