@@ -127,21 +127,31 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
     }
     if (tid < 32) s_amax[tid >> 4][tid & 15] = 0u;
     if (wave == 0) {
-      int rank = 0;
-      for (int s2 = 0; s2 < p.top_k; ++s2) rank += __shfl(my_id, s2, 64) < my_id ? 1 : 0;
+      // (an id < 0 -- the router found no pick, e.g. NaN logits, outside the
+      // contract -- is a sentinel as in moe_route_group: in no tile)
+      const bool ok = lane < p.top_k && my_id >= 0;
+      int rank = 0, n_valid = 0;
+      for (int s2 = 0; s2 < p.top_k; ++s2) {
+        const int o = __shfl(my_id, s2, 64);
+        rank += o >= 0 && o < my_id ? 1 : 0;
+        n_valid += o >= 0 ? 1 : 0;
+      }
       if (lane < p.top_k) {
-        s_sorted[rank] = lane;
-        s_tiles[rank] = int4{my_id, rank, 1, 0};
         s_rid[lane] = my_id;
         if (blockIdx.x == 0) {
           in.ids[lane] = my_id;
           in.w[lane] = my_w;
-          in.sorted[rank] = lane;
+          if (lane >= n_valid) in.sorted[lane] = -1;
         }
       }
+      if (ok) {
+        s_sorted[rank] = lane;
+        s_tiles[rank] = int4{my_id, rank, 1, 0};
+        if (blockIdx.x == 0) in.sorted[rank] = lane;
+      }
       if (lane == 0) {
-        if (p.has_shared) s_tiles[p.top_k] = int4{p.n_experts, 0, 1, 0};
-        s_ntiles = p.top_k + p.has_shared;
+        if (p.has_shared) s_tiles[n_valid] = int4{p.n_experts, 0, 1, 0};
+        s_ntiles = n_valid + p.has_shared;
       }
     }
     lds_barrier();
@@ -149,8 +159,9 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
       for (int e = tid; e <= p.n_experts; e += NT) {
         int below = 0, same = 0;
         for (int s2 = 0; s2 < p.top_k; ++s2) {
-          below += s_rid[s2] < e ? 1 : 0;
-          same += s_rid[s2] == e ? 1 : 0;
+          const int o = s_rid[s2];
+          below += o >= 0 && o < e ? 1 : 0;
+          same += o == e ? 1 : 0;
         }
         in.offsets[e] = below;
         if (e < p.n_experts) in.counts[e] = same;

@@ -397,15 +397,26 @@ def test_decode_step_one_row(step):
 
 
 @pytest.mark.parametrize("shape", range(len(OTHER_SHAPES)))
-@pytest.mark.parametrize("rows", [1, 5])
+@pytest.mark.parametrize("rows", [1, 3, 5])
 def test_decode_step_other_shapes(shape, rows):
-    # d_model 2048 / 1024 take the fused one-row kernel (4 and 2 waves, with and
-    # without a shared expert); 8192 and every rows > 1 the three calls
+    # one row with d_model 2048 / 1024 takes the fused kernel (4 and 2 waves,
+    # with and without a shared expert); 8192 and more rows the three calls
     L = OTHER_SHAPES[shape]
     seed = 51 + shape
     x = synth.activations(seed, rows, rows, L.d_model)
     lg = synth.router_logits(seed, rows, rows, L.n_experts)
     run_case(L, seed, x, lg, entry="step")
+
+
+@pytest.mark.parametrize("rows,hot", [(2, 0.0), (3, 2.0), (4, 0.0), (4, 2.0)])
+def test_decode_step_few_rows(rows, hot):
+    # 2-4 rows through the step entry (the three calls; down and combine by
+    # output rows); hot experts give tiles of several columns; padded strides
+    # on the 4-row cases
+    c = synth.DECODE_BATCH
+    x = synth.activations(c["seed"], 800 + rows, rows, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], 800 + rows, rows, DSV4.n_experts, hot_bias=hot)
+    run_case(DSV4, c["seed"], x, lg, entry="step", pads=(16, 64, 32) if rows == 4 else (0, 0, 0))
 
 
 def test_decode_step_tiny_and_hot():
