@@ -28,10 +28,15 @@
 
 namespace moe {
 
-constexpr int kBM = 128;          // token rows per tile (8 groups of 16)
+// Token rows per tile: 128 (8 groups of 16), or 32 when experts hold few rows
+// each (a short tile needs a quarter of the LDS per stage, so the ring runs
+// deeper and more of the weight stream is in flight).
+constexpr int kBMFull = 128;
+constexpr int kBMShort = 32;
 constexpr int kBNGroups = 16;     // 16-row weight groups per workgroup (256 rows)
 constexpr int kGemmThreads = 512; // 8 waves: 4 row quarters x 2 token halves
-constexpr int kStages = 3;        // LDS ring depth (prefetch distance 2 chunks)
+// LDS ring depth (prefetch distance: stages - 1 chunks)
+template <int BM> constexpr int ring_stages() { return BM == kBMFull ? 3 : 5; }
 constexpr int kLoadsPerChunk = 8; // direct-to-LDS loads per wave per K chunk
 
 enum GemmPass : int { GEMM_GATEUP = 0, GEMM_DOWN = 1 };
@@ -59,15 +64,17 @@ struct GemmArgs {
 
 // One LDS stage = one 128-element K chunk of the workgroup's operands, each
 // piece in the lane order its consumer reads (conflict-free ds_read_b128):
+template <int BM>
 struct Stage {
-  u32x4 a[kBNGroups][64];   // weight fragments, [row group][lane]         16 KiB
-  uint32_t s[kBNGroups][16];  // E8M0 bytes of the chunk's 4 blocks, per row   1 KiB
-  u32x4 b[8][4][64];        // token fragments, [token group][block][lane] 32 KiB
-  float d[8][4][16];        // activation scales, [token group][block][token] 2 KiB
+  u32x4 a[kBNGroups][64];        // weight fragments, [row group][lane]      16 KiB
+  uint32_t s[kBNGroups][16];     // E8M0 bytes of the chunk's 4 blocks, per row 1 KiB
+  u32x4 b[BM / 16][4][64];       // token fragments, [token group][block][lane] BM/4 KiB
+  float d[BM / 16][4][16];       // activation scales, [token group][block][token]
 };
 
-// vmcnt <= n (n < 16), no wait on the other counters (gfx9 encoding)
-#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | (n))
+// vmcnt <= n (n < 64), no wait on the other counters (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | ((n) & 15) | (((n) >> 4) << 14))
 
 // Workgroup barrier for the LDS ring.  __syncthreads() (and any LDS fence)
 // would wait for every outstanding direct-to-LDS load (vmcnt(0)) and collapse
@@ -120,7 +127,8 @@ struct GemmCtx {
 
 // Issue wave `wave`'s share of K chunk kc into `S`: 2 weight tiles, 1 scale
 // load, and -- when its token group is live -- 4 token fragments + 1 scale load.
-__device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage& S, int kc,
+template <int BM>
+__device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>& S, int kc,
                                   int wave, int lane, bool b_live) {
   const int n = lane & 15, g4 = lane >> 4, rq = wave & 3;
 #pragma unroll
@@ -145,8 +153,9 @@ __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage& S,
 
 // K loop + epilogue of one wave owning row groups prb+4*rq .. +3 and token
 // groups th, th+2, .. (NQ of them live).  Branch-free inner loop.
-template <int PASS, int NQ>
-__device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage* ring) {
+template <int PASS, int NQ, int BM>
+__device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring) {
+  constexpr int NST = ring_stages<BM>();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g4 = lane >> 4;
@@ -161,19 +170,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
     for (int q4 = 0; q4 < NQ; ++q4) acc[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KC = p.kc_total;
-  gemm_issue(p, c, ring[0], 0, wave, lane, b_live);
-  if (KC > 1) gemm_issue(p, c, ring[1], 1, wave, lane, b_live);
+  // chunks 0 .. NST-2 go out first; chunk kc + NST - 1 after chunk kc lands
+#pragma unroll
+  for (int k0 = 0; k0 < NST - 1; ++k0)
+    if (k0 < KC) gemm_issue(p, c, ring[k0], k0, wave, lane, b_live);
   for (int kc = 0; kc < KC; ++kc) {
-    if (kc + 1 < KC) {
-      if (b_live) WAIT_VMCNT(kLoadsPerChunk);
-      else WAIT_VMCNT(3);
-    } else {
-      WAIT_VMCNT(0);
+    // chunk kc has landed when no more than the loads of the chunks issued
+    // after it are outstanding (loads complete in issue order)
+    static_assert(NST - 2 <= 3 && 3 * kLoadsPerChunk < 64, "vmcnt range");
+    switch (min(NST - 2, KC - 1 - kc)) {
+      case 0: WAIT_VMCNT(0); break;
+      case 1: if (b_live) WAIT_VMCNT(kLoadsPerChunk); else WAIT_VMCNT(3); break;
+      case 2: if (b_live) WAIT_VMCNT(2 * kLoadsPerChunk); else WAIT_VMCNT(6); break;
+      default: if (b_live) WAIT_VMCNT(3 * kLoadsPerChunk); else WAIT_VMCNT(9); break;
     }
     ring_barrier();  // every wave's loads of chunk kc have landed; chunk kc-1 is consumed
-    if (kc + 2 < KC) gemm_issue(p, c, ring[(kc + 2) % kStages], kc + 2, wave, lane, b_live);
+    if (kc + NST - 1 < KC)
+      gemm_issue(p, c, ring[(kc + NST - 1) % NST], kc + NST - 1, wave, lane, b_live);
     if constexpr (NQ > 0) {
-      const Stage& S = ring[kc % kStages];
+      const Stage<BM>& S = ring[kc % NST];
       float dxv[NQ][4];
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4)
@@ -258,9 +273,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
   }
 }
 
-template <int PASS>
+template <int PASS, int BM>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs p) {
-  __shared__ Stage ring[kStages];
+  __shared__ Stage<BM> ring[ring_stages<BM>()];
 
   // Block b runs on XCD b % 8 (round-robin dispatch).  XCD x walks tiles
   // x, x+8, x+16, ... and all weight-row blocks of a tile back to back, so the
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs p) {
   if (tile_idx * n_nb >= p.n_items) return;
   int n_tiles;
   GemmCtx c;
-  c.t = find_tile<kBM>(p.offsets, p.n_experts, p.has_shared, p.rows, tile_idx, &n_tiles);
+  c.t = find_tile<BM>(p.offsets, p.n_experts, p.has_shared, p.rows, tile_idx, &n_tiles);
   if (c.t.expert < 0) return;
   c.shared = c.t.expert == p.n_experts;
   const uint8_t* blob = c.shared ? p.w_shared : p.w + (int64_t)c.t.expert * p.w_stride;
@@ -286,13 +301,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs p) {
   // live token groups of this wave's half: th, th+2, th+4, th+6 below nnt
   const int nnt = (c.t.count + 15) >> 4;
   const int th = (threadIdx.x >> 6) >> 2;
-  const int nq = min(4, max(0, (nnt - th + 1) / 2));
-  switch (nq) {  // wave-uniform
-    case 4: gemm_body<PASS, 4>(p, c, ring); break;
-    case 3: gemm_body<PASS, 3>(p, c, ring); break;
-    case 2: gemm_body<PASS, 2>(p, c, ring); break;
-    case 1: gemm_body<PASS, 1>(p, c, ring); break;
-    default: gemm_body<PASS, 0>(p, c, ring); break;
+  const int nq = min(BM / 32, max(0, (nnt - th + 1) / 2));
+  if constexpr (BM == kBMShort) {
+    if (nq == 1) gemm_body<PASS, 1, BM>(p, c, ring);  // wave-uniform
+    else gemm_body<PASS, 0, BM>(p, c, ring);
+  } else {
+    switch (nq) {  // wave-uniform
+      case 4: gemm_body<PASS, 4, BM>(p, c, ring); break;
+      case 3: gemm_body<PASS, 3, BM>(p, c, ring); break;
+      case 2: gemm_body<PASS, 2, BM>(p, c, ring); break;
+      case 1: gemm_body<PASS, 1, BM>(p, c, ring); break;
+      default: gemm_body<PASS, 0, BM>(p, c, ring); break;
+    }
   }
 }
 
@@ -304,8 +324,12 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
   uint8_t* base = (uint8_t*)ws;
   const int A = rows * L->top_k;
   const int n_h = A + (L->has_shared ? rows : 0);
-  const int tiles = std::min(L->n_experts, A) + A / kBM + 1 +
-                    (L->has_shared ? (rows + kBM - 1) / kBM : 0);
+  // short tiles when experts average at most 16 rows (then more than 32 in
+  // one expert is rare, and a second tile is the only cost)
+  const bool short_tiles = (int64_t)A <= 16LL * L->n_experts;
+  const int BM = short_tiles ? kBMShort : kBMFull;
+  const int tiles = std::min(L->n_experts, A) + A / BM + 1 +
+                    (L->has_shared ? (rows + BM - 1) / BM : 0);
 
   GemmArgs a{};
   a.offsets = offsets;
@@ -342,7 +366,10 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     g.ld_hs = L->d_ff / kBlock;
     g.n_items = tiles * (g.rg_total / kBNGroups);
     const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
-    hipLaunchKernelGGL(gemm_kernel<GEMM_GATEUP>, dim3(grid), dim3(kGemmThreads), 0, s, g);
+    if (short_tiles)
+      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), dim3(kGemmThreads), 0, s, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMFull>), dim3(grid), dim3(kGemmThreads), 0, s, g);
   }
   if (stages & MOE_STAGE_DOWN) {
     const PackedDims pd(L->d_model, L->d_ff);
@@ -362,7 +389,10 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     d.ld_y = L->d_model;
     d.n_items = tiles * (d.rg_total / kBNGroups);
     const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (d.rg_total / kBNGroups));
-    hipLaunchKernelGGL(gemm_kernel<GEMM_DOWN>, dim3(grid), dim3(kGemmThreads), 0, s, d);
+    if (short_tiles)
+      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMShort>), dim3(grid), dim3(kGemmThreads), 0, s, d);
+    else
+      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMFull>), dim3(grid), dim3(kGemmThreads), 0, s, d);
     launch_combine((const float*)(base + lay.partials), ids, w, rows, L->top_k, L->has_shared,
                    L->d_model, y, ld_y, s);
   }
