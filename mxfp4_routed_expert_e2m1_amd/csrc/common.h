@@ -354,48 +354,70 @@ __device__ inline Tile find_tile(const int32_t* __restrict__ offsets, int n_expe
 // -------------------------------------------------------------- routing
 // gfx90a report §3.2 (top-6 of 256 routed experts) and §5.3 (membership
 // ties broken by logical id, selected positions in a fixed order).
+// Order-preserving integer key of a logit: a larger value gets a larger key,
+// -0 and +0 the same one (x + 0 turns -0 into +0), and every real logit a key
+// >= 1, so 0 can mark an expert that is absent or already picked.
+__device__ inline uint32_t logit_key(float x) {
+  const uint32_t b = __float_as_uint(x + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ inline float logit_of_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Max of an unsigned value over the whole wave (the DPP steps of wave_max).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  auto f = [](uint32_t u) { return __builtin_bit_cast(float, u); };
+  auto u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+  v = max(v, u(dpp_mov<0xB1>(f(v))));
+  v = max(v, u(dpp_mov<0x4E>(f(v))));
+  v = max(v, u(dpp_mov<0x141>(f(v))));
+  v = max(v, u(dpp_mov<0x140>(f(v))));
+  v = max(v, u(dpp_rows<0x142, 0xA>(f(v))));
+  v = max(v, u(dpp_rows<0x143, 0xC>(f(v))));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // One wave: top_k picks of one row; lane s < top_k receives slot s.  Each
-// round takes the largest remaining logit (a wave max on DPP) and, among
-// the experts holding exactly that value, the lowest index (per-slot
-// ballots, lowest slot first: expert e sits in lane e % 64, slot e / 64).
+// round takes the largest remaining logit (a wave max of the keys on DPP)
+// and, among the experts holding exactly that value, the lowest index
+// (per-slot ballots, lowest slot first: expert e sits in lane e % 64, slot
+// e / 64); the pick's key becomes 0.  The weights follow the rounds: each
+// pick's sigmoid in its own lane, then their sum in pick order.
 template <int PER_LANE>
 __device__ inline void topk_row(const float* __restrict__ l, int n_experts, int top_k,
                                 int* my_id, float* my_w) {
   const int lane = lane_id();
-  float v[PER_LANE];
+  uint32_t kv[PER_LANE];
 #pragma unroll
   for (int j = 0; j < PER_LANE; ++j) {
     const int e = lane + 64 * j;
-    v[j] = (e < n_experts) ? l[e] : -INFINITY;
+    kv[j] = (e < n_experts) ? logit_key(l[e]) : 0u;
   }
-  uint32_t taken = 0;
-  float my_v = 0.f;
+  uint32_t my_k = 0;
   int id = 0;
   for (int s = 0; s < top_k; ++s) {
-    float lv = -INFINITY;
+    uint32_t lk = kv[0];
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
-      if (ok) lv = fmaxf(lv, v[j]);
-    }
-    const float bv = wave_max(lv);
+    for (int j = 1; j < PER_LANE; ++j) lk = max(lk, kv[j]);
+    const uint32_t bk = wave_max_u32(lk);
     int be = -1;
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) {
-      const bool ok = lane + 64 * j < n_experts && !((taken >> j) & 1u);
-      const uint64_t hit = __ballot(ok && v[j] == bv);
+      const uint64_t hit = __ballot(kv[j] == bk);
       if (be < 0 && hit != 0) be = 64 * j + __ffsll((unsigned long long)hit) - 1;
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if ((be & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < PER_LANE; ++j)
+        if ((be >> 6) == j) kv[j] = 0u;
+    }
     if (lane == s) {
-      my_v = bv;
+      my_k = bk;
       id = be;
     }
   }
-  // the weights off the selection's critical path: each pick's sigmoid in
-  // its own lane, then their sum in pick order (the same fp32 operations in
-  // the same order as summing inside the rounds)
-  const float my_sig = 1.0f / (1.0f + expf(-my_v));
+  const float my_sig = 1.0f / (1.0f + expf(-logit_of_key(my_k)));
   float sum = 0.f;
   for (int s = 0; s < top_k; ++s) sum += __shfl(my_sig, s, 64);
   *my_id = id;

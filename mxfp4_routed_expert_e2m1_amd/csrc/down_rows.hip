@@ -189,7 +189,13 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
         b[j] = *(const u32x4*)(hl + (size_t)lrow * F + kc * kChunkK + j * kBlock + g8);
       d = *(const f32x4*)(hsl + (size_t)lrow * (F / kBlock) + kc * 4);
     };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Exact rows: the sum over K is taken as the streaming down kernel takes
+    // it for 5-16 rows -- a partial per run of 4 chunks (one wave's share
+    // there), each from zero in chunk and block order, the partials added in
+    // run order -- so a row's output does not depend on how many rows share
+    // its step.
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};  // the runs so far
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};  // the current run of 4 chunks
     for (int kg = 0; kg < p.kc_total; kg += kDRGroup) {
       if (kg > 0) issue_head(te, kg);  // the head of the first group is already in flight
       const int n_in = min(kDRGroup, p.kc_total - kg);
@@ -201,11 +207,15 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
 #pragma unroll
       for (int kk = 0; kk < kDRGroup; ++kk) {
         if (kk < n_in) {
+          if (kk % 4 == 0) {  // (kg % 4 == 0) a run starts: fold the last one in
+            acc += run;
+            run = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
           if (kk + 1 < n_in) load_h(kg + kk + 1, b[(kk + 1) & 1], d[(kk + 1) & 1]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float sc = e8m0_to_f32((s[kk] >> (8 * j)) & 0xFFu);
-            acc += mfma_block(fp4x8_to_bf16x8(a[kk][j], sc),
+            run += mfma_block(fp4x8_to_bf16x8(a[kk][j], sc),
                               __builtin_bit_cast(bf16x8, b[kk & 1][j])) *
                    d[kk & 1][j];
           }
@@ -217,6 +227,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
         }
       }
     }
+    acc += run;
     // lane l holds rows 4*(l/16) + i of column l % 16
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[(ti * 16 + col) * 16 + 4 * (lane >> 4) + i] = acc[i];
@@ -231,11 +242,11 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     for (int s2 = 0; s2 < p.top_k; ++s2) {
       const int a2 = t * p.top_k + s2;
       const int pidx = s_pos[a2];
-      if (pidx >= 0) v += s_wt[a2] * part[pidx + r];
+      if (pidx >= 0) v = fmaf(s_wt[a2], part[pidx + r], v);  // as the combine kernel
     }
     if (p.has_shared) {
       const int ti = s_routed + (t >> 4);
-      v += part[(ti * 16 + (t & 15)) * 16 + r];
+      v = v + part[(ti * 16 + (t & 15)) * 16 + r];
     }
     p.y[(int64_t)t * p.ld_y + 16 * rg + r] = v;
   }

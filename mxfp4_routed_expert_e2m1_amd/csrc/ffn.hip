@@ -245,11 +245,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (i >= (int64_t)rows * per_row) return;
   const int t = (int)(i / per_row);
   const int c = (int)(i % per_row) * 4;
+  // y = fma over the slots in slot order from 0, then + the shared expert's
+  // partial: the one order every decode path uses (exact rows)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < top_k; ++s) {
     const int64_t a = (int64_t)t * top_k + s;
     if (ids[a] < 0) continue;
-    acc += w[a] * *(const f32x4*)(P + a * d_model + c);
+    const float wa = w[a];
+    const f32x4 pa = *(const f32x4*)(P + a * d_model + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(wa, pa[i], acc[i]);
   }
   if (has_shared) acc += *(const f32x4*)(P + ((int64_t)rows * top_k + t) * d_model + c);
   *(f32x4*)(y + (int64_t)t * ld_y + c) = acc;

@@ -460,6 +460,33 @@ def test_decode_step_graph_replays_match_eager():
         assert torch.isfinite(other[-1]).all()
 
 
+def test_decode_exact_rows_across_batch_sizes():
+    # Exact rows ([strix] "The exact-rows contract"): a row's output does not
+    # depend on the rows sharing its step.  The same rows decoded all 16
+    # together (streaming down + combine), in groups of 8 and 5 (the same),
+    # of 4, 3 and 2 (down + combine by rows) and one at a time (the one-row
+    # step kernel, and the three calls) give the same bits.
+    c = synth.DECODE_BATCH
+    layer = layer_for(DSV4, c["seed"])
+    x = torch.from_numpy(synth.activations(c["seed"], 900, 16, DSV4.d_model)).to(DEV)
+    lg = torch.from_numpy(synth.router_logits(c["seed"], 900, 16, DSV4.n_experts,
+                                              hot_bias=1.0)).to(DEV)
+    y_all = m.moe_ffn_decode_step(layer, x, lg)[-1].clone()
+    groups = [list(range(0, 8)), list(range(8, 13)), [13, 14, 15, 0], [1, 5, 9], [2, 3],
+              [4], [11], [15]]
+    for g in groups:
+        idx = torch.tensor(g, device=DEV)
+        y = m.moe_ffn_decode_step(layer, x[idx].contiguous(), lg[idx].contiguous())[-1]
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_all[idx]), g
+    # one row through the three separate calls
+    q, qs = m.moe_quant_act_q8(x[7:8])
+    ids, w, counts, offsets, srt = m.moe_route_group(lg[7:8].contiguous(), DSV4.top_k)
+    y = m.moe_ffn_decode(layer, q, qs, ids, w, offsets, srt)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_all[7:8])
+
+
 def test_decode_one_row_tiny_and_odd():
     for L, seed in ((TINY, 41), (ODD, 42)):
         x = synth.activations(seed, 1, 1, L.d_model)
