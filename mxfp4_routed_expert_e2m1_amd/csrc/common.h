@@ -114,10 +114,35 @@ __device__ inline f32x4 mfma_block(bf16x8 a, bf16x8 b) {
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
+// exp in fp32 by a fixed, named sequence of operations, so a CPU reference
+// can repeat it bit for bit (exact rows): Cody-Waite reduction x = k ln2 + r
+// with ln2 split in two (the high part exact in 16 bits), the degree-7 Taylor
+// polynomial of exp on |r| <= ln2/2 in Horner form with fused multiply-adds
+// (coefficients 1/n! rounded to fp32), then scaling by 2^k.  Within 2 ulp
+// of exp; 0 below -104, infinity above 89.
+__device__ inline float exp_rows(float x) {
+  if (!(x >= -104.0f)) return x != x ? x : 0.0f;
+  if (x > 89.0f) return __builtin_inff();
+  const float k = rintf(x * 0x1.715476p+0f);
+  float r = fmaf(-k, 0x1.62e4p-1f, x);
+  r = fmaf(-k, 0x1.7f7d1cp-20f, r);
+  float p = 0x1.a01a02p-13f;
+  p = fmaf(p, r, 0x1.6c16c2p-10f);
+  p = fmaf(p, r, 0x1.111112p-7f);
+  p = fmaf(p, r, 0x1.555556p-5f);
+  p = fmaf(p, r, 0x1.555556p-3f);
+  p = fmaf(p, r, 0x1p-1f);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)k);
+}
+
 // Gate/up epilogue arithmetic, shared by every kernel that finishes a gate/up
 // pass so all of them round alike: h = silu(gate) * up, then the group-32
 // int8 code of h for the group scale d = amax/127 (0 when the group is zero).
-__device__ inline float swiglu(float gate, float up) { return gate / (1.0f + expf(-gate)) * up; }
+__device__ inline float swiglu(float gate, float up) {
+  return gate / (1.0f + exp_rows(-gate)) * up;
+}
 __device__ inline float q8_code(float v, float d) {
   return d != 0.f ? fminf(fmaxf(rintf(v / d), -127.f), 127.f) : 0.f;
 }
@@ -417,7 +442,7 @@ __device__ inline void topk_row(const float* __restrict__ l, int n_experts, int 
       id = be;
     }
   }
-  const float my_sig = 1.0f / (1.0f + expf(-logit_of_key(my_k)));
+  const float my_sig = 1.0f / (1.0f + exp_rows(-logit_of_key(my_k)));
   float sum = 0.f;
   for (int s = 0; s < top_k; ++s) sum += __shfl(my_sig, s, 64);
   *my_id = id;

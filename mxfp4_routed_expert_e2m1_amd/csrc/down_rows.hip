@@ -215,9 +215,10 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float sc = e8m0_to_f32((s[kk] >> (8 * j)) & 0xFFu);
-            run += mfma_block(fp4x8_to_bf16x8(a[kk][j], sc),
-                              __builtin_bit_cast(bf16x8, b[kk & 1][j])) *
-                   d[kk & 1][j];
+            const f32x4 r = mfma_block(fp4x8_to_bf16x8(a[kk][j], sc),
+                                       __builtin_bit_cast(bf16x8, b[kk & 1][j]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) run[i] = fmaf(r[i], d[kk & 1][j], run[i]);
           }
         }
         if (kk + kDRAhead < kDRGroup) {

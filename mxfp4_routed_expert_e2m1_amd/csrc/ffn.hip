@@ -67,7 +67,8 @@ __device__ inline void wave_project(const ProjArgs& p, const uint8_t* blob, int 
       for (int g = 0; g < RGW; ++g) {
         const float sc = e8m0_to_f32((s[g] >> (8 * j)) & 0xFFu);
         const f32x4 r = mfma_block(fp4x8_to_bf16x8(a[g][j], sc), bb);
-        acc[g] += r * d[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][i] = fmaf(r[i], d[j], acc[g][i]);
       }
     }
   };

@@ -220,7 +220,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int q4 = 0; q4 < NQ; ++q4) acc[g][q4] += r[g][q4] * dxv[q4][j];
+          for (int q4 = 0; q4 < NQ; ++q4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[g][q4][i] = fmaf(r[g][q4][i], dxv[q4][j], acc[g][q4][i]);
       }
     }
   }

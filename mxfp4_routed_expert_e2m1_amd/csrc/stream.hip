@@ -295,7 +295,8 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
       for (int g = 0; g < RGW; ++g) {
         const float sc = e8m0_to_f32((sc4[g][kk] >> (8 * j)) & 0xFFu);
         const f32x4 r = mfma_block(fp4x8_to_bf16x8(a[kk][g][j], sc), bb);
-        acc[g] += r * d[kk][j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][i] = fmaf(r[i], d[kk][j], acc[g][i]);
       }
     }
   };

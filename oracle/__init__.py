@@ -42,6 +42,10 @@ I64 = C.c_int64
 def _declare(L):
     L.oracle_set_threads.argtypes = [I]
     L.oracle_get_threads.restype = I
+    L.oracle_set_exact_rows.argtypes = [I]
+    L.oracle_set_exact_rows.restype = I
+    L.oracle_exp_rows.argtypes = [P, I, P]
+    L.oracle_exp_rows.restype = None
     L.oracle_e2m1_x2.argtypes = [I]
     L.oracle_e2m1_x2.restype = I
     L.oracle_e2m1.argtypes = [I]
@@ -86,6 +90,30 @@ def set_threads(n: int) -> None:
 
 def get_threads() -> int:
     return lib().oracle_get_threads()
+
+
+def set_exact_rows(on: bool) -> bool:
+    """Exact-rows mode (fp32 in one named order, see moe_oracle.h) on or off;
+    returns the previous setting."""
+    return bool(lib().oracle_set_exact_rows(int(bool(on))))
+
+
+class exact_rows:
+    """with oracle.exact_rows(): ... runs its body in exact-rows mode."""
+
+    def __enter__(self):
+        self.old = set_exact_rows(True)
+
+    def __exit__(self, *exc):
+        set_exact_rows(self.old)
+
+
+def exp_rows(x):
+    """The oracle's named fp32 exp, elementwise."""
+    x = _c(x, np.float32)
+    y = np.empty_like(x)
+    lib().oracle_exp_rows(_p(x), x.size, _p(y))
+    return y
 
 
 def e2m1_x2(code: int) -> int:

@@ -17,9 +17,44 @@
 #endif
 
 static int g_threads = 1;
+static int g_exact = 0;
 
 void oracle_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
 int oracle_get_threads(void) { return g_threads; }
+int oracle_set_exact_rows(int on) {
+  const int old = g_exact;
+  g_exact = on ? 1 : 0;
+  return old;
+}
+
+/* ------------------------------------------------------------ exp_rows */
+
+/* Cody-Waite: k = nearest integer to x / ln2, r = x - k*ln2 taken in two
+ * fused steps with ln2 = LN2_HI + LN2_LO (LN2_HI has 16 significant bits,
+ * so k*LN2_HI is exact for |k| <= 256); exp(r) for |r| <= ln2/2 by its
+ * Taylor series to r^7 (truncation below 1e-8 relative); exp(x) =
+ * 2^k exp(r). */
+static float exp_rows1(float x) {
+  static const float LOG2E = 0x1.715476p+0f;   /* 1/ln2 rounded to fp32 */
+  static const float LN2_HI = 0x1.62e4p-1f;    /* 0.693145751953125 */
+  static const float LN2_LO = 0x1.7f7d1cp-20f; /* ln2 - LN2_HI, to fp32 */
+  static const float C[8] = {1.0f, 1.0f, 0x1p-1f, 0x1.555556p-3f,
+                             0x1.555556p-5f, 0x1.111112p-7f, 0x1.6c16c2p-10f,
+                             0x1.a01a02p-13f}; /* 1/n!, n = 0..7, to fp32 */
+  if (x != x) return x;
+  if (x < -104.0f) return 0.0f;
+  if (x > 89.0f) return INFINITY;
+  const float k = rintf(x * LOG2E);
+  float r = fmaf(-k, LN2_HI, x);
+  r = fmaf(-k, LN2_LO, r);
+  float p = C[7];
+  for (int n = 6; n >= 0; --n) p = fmaf(p, r, C[n]);
+  return ldexpf(p, (int)k);
+}
+
+void oracle_exp_rows(const float* x, int n, float* y) {
+  for (int i = 0; i < n; ++i) y[i] = exp_rows1(x[i]);
+}
 
 /* ---------------------------------------------------------------- tables */
 
@@ -130,6 +165,17 @@ int oracle_route(const float* logits, int64_t ld_l, int rows, int n_experts,
       taken[best] = 1;
       ids[(int64_t)r * top_k + i] = best;
     }
+    if (g_exact) { /* fp32: sigmoid with exp_rows, sum in pick order */
+      float sum = 0.0f;
+      float* sgf = (float*)sg;
+      for (int i = 0; i < top_k; ++i) {
+        const float z = l[ids[(int64_t)r * top_k + i]];
+        sgf[i] = 1.0f / (1.0f + exp_rows1(-z));
+        sum = sum + sgf[i];
+      }
+      for (int i = 0; i < top_k; ++i) w[(int64_t)r * top_k + i] = sgf[i] / sum;
+      continue;
+    }
     double sum = 0.0;
     for (int i = 0; i < top_k; ++i) {
       const double z = (double)l[ids[(int64_t)r * top_k + i]];
@@ -191,6 +237,25 @@ static int matvec_impl(const uint8_t* codes, int64_t ld_c, const uint8_t* scales
   for (int64_t idx = 0; idx < total; ++idx) {
     const int t = (int)(idx / n_out);
     const int n = (int)(idx % n_out);
+    if (g_exact) {
+      /* runs of 16 blocks: each from zero, block terms (exact in fp32: a
+       * dot of at most 16 bits times a power of two) folded in with fmaf
+       * against the activation scale, runs added in order */
+      float total = 0.0f;
+      for (int b0 = 0; b0 < nb; b0 += 16) {
+        float run = 0.0f;
+        for (int b = b0; b < nb && b < b0 + 16; ++b) {
+          const int32_t dot = oracle_block_dot(codes + (int64_t)n * ld_c + b * 16,
+                                               q + (int64_t)t * ld_q + b * 32);
+          const double wscale = 0.5 * oracle_e8m0(scales[(int64_t)n * ld_s + b]);
+          const float term = (float)((double)dot * wscale);
+          run = fmaf(term, qs[(int64_t)t * ld_qs + b], run);
+        }
+        total = total + run;
+      }
+      y[(int64_t)t * ld_y + n] = total;
+      continue;
+    }
     double acc = 0.0;
     for (int b = 0; b < nb; ++b) {
       const int32_t dot = oracle_block_dot(codes + (int64_t)n * ld_c + b * 16,
@@ -232,6 +297,14 @@ int oracle_block_dots(const uint8_t* codes, int64_t ld_c, int n_out, int d_in,
  * silu(z) = z / (1 + exp(-z)), no clamp, evaluated in fp64 from the fp32
  * projections and rounded once to fp32. */
 void oracle_swiglu(const float* g, const float* u, int n, float* h) {
+  if (g_exact) { /* fp32 with exp_rows: (g / (1 + exp(-g))) * u */
+    for (int i = 0; i < n; ++i) {
+      const float den = 1.0f + exp_rows1(-g[i]);
+      const float silu = g[i] / den;
+      h[i] = silu * u[i];
+    }
+    return;
+  }
   for (int i = 0; i < n; ++i) {
     const double z = (double)g[i];
     const double silu = z / (1.0 + exp(-z));
@@ -279,6 +352,16 @@ int oracle_combine(int rows, int top_k, int has_shared, int d_model,
   const int slots = top_k + 1;
   for (int t = 0; t < rows; ++t) {
     for (int n = 0; n < d_model; ++n) {
+      if (g_exact) { /* fmaf per slot in slot order from zero, shared last */
+        float v = 0.0f;
+        for (int i = 0; i < top_k; ++i) {
+          if (ids[(int64_t)t * top_k + i] < 0) continue;
+          v = fmaf(w[(int64_t)t * top_k + i], Y[((int64_t)t * slots + i) * d_model + n], v);
+        }
+        if (has_shared) v = v + Y[((int64_t)t * slots + top_k) * d_model + n];
+        y[(int64_t)t * ld_y + n] = v;
+        continue;
+      }
       double acc = 0.0;
       for (int i = 0; i < top_k; ++i) {
         if (ids[(int64_t)t * top_k + i] < 0) continue;

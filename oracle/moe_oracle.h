@@ -27,6 +27,15 @@
  * fp64; sums over blocks are fp64 and rounded once to fp32.  Quantisation
  * decisions (absmax, d = amax/127, rint(x/d)) are taken in fp32, the
  * precision the kernels use.
+ *
+ * Exact-rows mode ([strix] "The exact-rows contract": every row keeps one
+ * fixed operand order), off by default: the same steps in fp32 in one named
+ * order, so results can be compared bit for bit -- projections sum the
+ * scaled block terms of each run of 16 blocks (512 elements) from zero with
+ * fused multiply-adds in block order and add the runs in order; SwiGLU and
+ * the router's sigmoid use exp_rows (below) in fp32; router weights sum in
+ * pick order; the combine folds the slots with fused multiply-adds in slot
+ * order and adds the shared expert last.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -43,6 +52,16 @@ extern "C" {
  * reduction, so results do not depend on it) */
 void oracle_set_threads(int n);
 int oracle_get_threads(void);
+
+/* exact-rows mode on (1) or off (0, the fp64 reference); returns the old one */
+int oracle_set_exact_rows(int on);
+
+/* exp in fp32 by a named sequence: Cody-Waite reduction x = k ln2 + r (ln2 as
+ * a 16-bit high part plus a low part), the degree-7 Taylor polynomial of exp
+ * in r (coefficients 1/n! rounded to fp32) in Horner form with fused
+ * multiply-adds, scaling by 2^k; 0 below -104, infinity above 89.  y[i] =
+ * exp_rows(x[i]). */
+void oracle_exp_rows(const float* x, int n, float* y);
 
 /* E2M1 code -> 2*value (an integer in {0,+-1,+-2,+-3,+-4,+-6,+-8,+-12}) */
 int oracle_e2m1_x2(int code);

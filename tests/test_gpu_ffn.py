@@ -487,6 +487,53 @@ def test_decode_exact_rows_across_batch_sizes():
     assert torch.equal(y, y_all[7:8])
 
 
+@pytest.mark.parametrize("rows", [1, 3, 16])
+def test_decode_bitwise_equals_exact_rows_oracle(rows):
+    # Exact rows, second half: the oracle's exact-rows mode takes the same fp32
+    # steps in the same named order (runs of 16 blocks, fmaf, exp_rows, slot
+    # order), so every output of a decode step -- codes, scales, routes,
+    # weights, hidden codes and scales, y -- must have the oracle's bits.
+    # 1 row: the one-row step kernel; 3: down by rows; 16: streaming down.
+    c = synth.DECODE_BATCH
+    L = DSV4
+    layer = layer_for(L, c["seed"])
+    x = synth.activations(c["seed"], 950 + rows, rows, L.d_model)
+    lg = synth.router_logits(c["seed"], 950 + rows, rows, L.n_experts)
+    ws = torch.full((m.moe_ffn_workspace_bytes(layer, rows),), 0x7F, dtype=torch.uint8,
+                    device=DEV)
+    q, qs, ids, w, counts, offsets, srt, y = m.moe_ffn_decode_step(
+        layer, torch.from_numpy(x).to(DEV), torch.from_numpy(lg).to(DEV), ws=ws)
+    torch.cuda.synchronize()
+    with oracle.exact_rows():
+        q_o, qs_o = oracle.quant_q8(x)
+        ids_o, w_o = oracle.route(lg, L.top_k)
+        need = set(int(e) for e in ids_o.reshape(-1)) | {L.n_experts}
+        ex = canonical_experts(L, c["seed"], 0, need)
+        y_o, mid = oracle.ffn(ex, L.n_experts, L.top_k, L.has_shared, q_o, qs_o, ids_o,
+                              w_o, want_intermediates=True)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+    np.testing.assert_array_equal(qs.cpu().numpy(), qs_o)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    np.testing.assert_array_equal(w.cpu().numpy(), w_o)
+    # hidden codes and scales from the workspace: sorted position p for the
+    # routed slots, rows*k + t for the shared expert
+    off_h, off_hs, _ = m.moe_ffn_workspace_layout(layer, rows)
+    k, slots, A = L.top_k, L.top_k + 1, rows * L.top_k
+    hb = ws[off_h: off_h + (A + rows) * L.d_ff * 2].view(torch.bfloat16).view(A + rows, L.d_ff)
+    hs = ws[off_hs: off_hs + (A + rows) * (L.d_ff // 32) * 4].view(torch.float32)
+    hb = hb.float().cpu().numpy()
+    hs = hs.view(A + rows, L.d_ff // 32).cpu().numpy()
+    srt_n = srt.cpu().numpy()
+    pos = np.empty(A, np.int64)
+    pos[srt_n[:A]] = np.arange(A)
+    for t in range(rows):
+        for i in range(slots):
+            g_row = pos[t * k + i] if i < k else A + t
+            np.testing.assert_array_equal(hb[g_row], mid["hq"][t * slots + i].astype(np.float32))
+            np.testing.assert_array_equal(hs[g_row], mid["hs"][t * slots + i])
+    np.testing.assert_array_equal(y.cpu().numpy(), y_o)
+
+
 def test_decode_one_row_tiny_and_odd():
     for L, seed in ((TINY, 41), (ODD, 42)):
         x = synth.activations(seed, 1, 1, L.d_model)
