@@ -199,6 +199,21 @@ def test_matvec_parity(n_out, d_in, rows):
     assert_rows_close(y.cpu().numpy(), y_o, what=f"matvec {n_out}x{d_in} rows={rows}")
 
 
+@pytest.mark.parametrize("n_out,d_in,rows", [(14336, 4096, 5), (1024, 2048, 3), (512, 1024, 1)])
+def test_matvec_bitwise_equals_exact_rows_oracle(n_out, d_in, rows):
+    # the streaming matvec takes the oracle's exact-rows order (runs of 16
+    # blocks folded with fmaf, runs added in order): every output bit equal
+    codes, scales, x = _matvec_inputs(n_out, d_in, rows, 2)
+    packed = m.moe_pack_mxfp4(codes, scales, 0)
+    q, qs = m.moe_quant_act_q8(torch.from_numpy(x).to(DEV))
+    y = m.moe_matvec_mxfp4(packed, n_out, d_in, q, qs)
+    _sync()
+    q_o, qs_o = oracle.quant_q8(x)
+    with oracle.exact_rows():
+        y_o = oracle.matvec(codes.cpu().numpy(), scales.cpu().numpy(), q_o, qs_o)
+    np.testing.assert_array_equal(y.cpu().numpy(), y_o)
+
+
 def test_matvec_k_rows_share_one_pass_bitwise():
     # a row's result does not depend on which other rows share the weight pass
     n_out, d_in = 14336, 4096
