@@ -178,7 +178,14 @@ typedef struct moe_layer {
   int64_t down_stride;
   const void* shared_gate_up;
   const void* shared_down;
+  int flags;      /* MOE_LAYER_* bits; 0 = the default arithmetic */
 } moe_layer_t;
+
+/* Layer flag: round the SwiGLU intermediate to BF16 (to nearest, ties to even)
+ * before its group-32 INT8 requant, as the gfx90a report's down chain reads
+ * an already-rounded BF16 intermediate ([gfx90a] §8.2).  Without it the fp32
+ * intermediate is requantised directly.  Other flag bits are rejected. */
+#define MOE_LAYER_BF16_INTERMEDIATE 1
 
 /* Workspace of one FFN call with `rows` tokens (same for decode/prefill).
  * With A' = rows*top_k + (has_shared ? rows : 0) hidden rows, it holds, in

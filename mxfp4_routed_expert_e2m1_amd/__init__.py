@@ -42,7 +42,10 @@ class moe_layer_t(C.Structure):
                 ("top_k", C.c_int), ("has_shared", C.c_int),
                 ("gate_up", C.c_void_p), ("gate_up_stride", C.c_int64),
                 ("down", C.c_void_p), ("down_stride", C.c_int64),
-                ("shared_gate_up", C.c_void_p), ("shared_down", C.c_void_p)]
+                ("shared_gate_up", C.c_void_p), ("shared_down", C.c_void_p),
+                ("flags", C.c_int)]
+
+MOE_LAYER_BF16_INTERMEDIATE = 1
 
 
 _lib = None
@@ -212,9 +215,17 @@ class Layer:
                              gate_up.data_ptr(), gate_up.stride(0) if gate_up.dim() == 2 else 0,
                              down.data_ptr(), down.stride(0) if down.dim() == 2 else 0,
                              shared_gate_up.data_ptr() if has_shared else None,
-                             shared_down.data_ptr() if has_shared else None)
+                             shared_down.data_ptr() if has_shared else None, 0)
         self.d_model, self.d_ff, self.n_experts, self.top_k = d_model, d_ff, n_experts, top_k
         self.has_shared = has_shared
+
+    def variant(self, bf16_intermediate=False):
+        """The same packed weights with other layer flags (moe_layer_t.flags)."""
+        v = Layer.__new__(Layer)
+        v.__dict__.update(self.__dict__)
+        v.c = moe_layer_t.from_buffer_copy(self.c)
+        v.c.flags = MOE_LAYER_BF16_INTERMEDIATE if bf16_intermediate else 0
+        return v
 
 
 def moe_ffn_workspace_bytes(layer: Layer, rows: int) -> int:

@@ -143,6 +143,14 @@ __device__ inline float exp_rows(float x) {
 __device__ inline float swiglu(float gate, float up) {
   return gate / (1.0f + exp_rows(-gate)) * up;
 }
+// BF16 rounding of the intermediate (layer flag MOE_LAYER_BF16_INTERMEDIATE):
+// to nearest, ties to even, on the fp32 bits; infinities and NaN unchanged.
+__device__ inline float round_bf16(float x) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7F800000u) == 0x7F800000u) return x;
+  return __uint_as_float((b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u);
+}
+__device__ inline float mid_round(float h, int bf16_mid) { return bf16_mid ? round_bf16(h) : h; }
 __device__ inline float q8_code(float v, float d) {
   return d != 0.f ? fminf(fmaxf(rintf(v / d), -127.f), 127.f) : 0.f;
 }

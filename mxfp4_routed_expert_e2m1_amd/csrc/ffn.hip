@@ -223,7 +223,7 @@ __global__ __launch_bounds__(W * 64, 4) void proj_kernel(ProjArgs p) {
       const int l = 16 * ((f & 15) >> 2) + n;
       const float gv = red[0][gsel * 4 + (f & 3)][l];
       const float uv = red[0][(gsel + 1) * 4 + (f & 3)][l];
-      const float hv = swiglu(gv, uv);
+      const float hv = mid_round(swiglu(gv, uv), p.bf16_mid);
       const float d = max32(fabsf(hv)) / 127.0f;
       const float qf = q8_code(hv, d);
       if (n < t.count) {
@@ -326,6 +326,7 @@ static int check_layer(const moe_layer_t* L) {
   if (L->top_k < 1 || L->top_k > L->n_experts || L->top_k > MOE_MAX_TOP_K) return MOE_ERR_SHAPE;
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (!L->gate_up || !L->down) return MOE_ERR_INVALID_ARG;
+  if (L->flags & ~MOE_LAYER_BF16_INTERMEDIATE) return MOE_ERR_INVALID_ARG;
   if (L->has_shared && (!L->shared_gate_up || !L->shared_down)) return MOE_ERR_INVALID_ARG;
   const int64_t gu = PackedDims(2 * L->d_ff, L->d_model).total();
   const int64_t dn = PackedDims(L->d_model, L->d_ff).total();
@@ -384,6 +385,7 @@ static ProjArgs gateup_args(const moe_layer_t* L, const int8_t* q, int64_t ld_q,
   g.hs = (float*)(base + lay.hidden_scales);
   g.ld_h = L->d_ff;
   g.ld_hs = L->d_ff / kBlock;
+  g.bf16_mid = (L->flags & MOE_LAYER_BF16_INTERMEDIATE) != 0;
   return g;
 }
 

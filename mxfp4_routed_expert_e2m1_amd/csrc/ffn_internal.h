@@ -57,6 +57,7 @@ struct ProjArgs {
   uint16_t* h;              // GATEUP: requantised hidden codes (bf16 bits) and scales
   float* hs;
   int64_t ld_h, ld_hs;
+  int bf16_mid;             // GATEUP: round the intermediate to bf16 before its requant
 };
 
 // K/128 in {8, 16, 32} and whole 4-group items

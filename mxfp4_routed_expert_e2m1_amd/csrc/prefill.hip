@@ -63,6 +63,7 @@ struct GemmArgs {
   int64_t ld_h, ld_hs;
   float* y;  // down partials
   int64_t ld_y;
+  int bf16_mid;  // gate/up: round the intermediate to bf16 before its requant
 };
 
 // One LDS stage = one 128-element K chunk of the workgroup's operands, each
@@ -241,8 +242,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
         for (int i = 0; i < 4; ++i) {
           const float g0 = acc[0][q4][i], u0 = acc[1][q4][i];
           const float g1 = acc[2][q4][i], u1 = acc[3][q4][i];
-          hv[i] = swiglu(g0, u0);
-          hv[4 + i] = swiglu(g1, u1);
+          hv[i] = mid_round(swiglu(g0, u0), p.bf16_mid);
+          hv[4 + i] = mid_round(swiglu(g1, u1), p.bf16_mid);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(hv[i]));
@@ -369,6 +370,7 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     g.hs = (float*)(base + lay.hidden_scales);
     g.ld_h = L->d_ff;
     g.ld_hs = L->d_ff / kBlock;
+    g.bf16_mid = (L->flags & MOE_LAYER_BF16_INTERMEDIATE) != 0;
     g.n_items = tiles * (g.rg_total / kBNGroups);
     const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
     if (short_tiles)

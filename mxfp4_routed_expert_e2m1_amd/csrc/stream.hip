@@ -323,7 +323,7 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
         for (int w2 = 0; w2 < W; ++w2) gv += red[buf][w2][8 * gp + i][lane];
 #pragma unroll
         for (int w2 = 0; w2 < W; ++w2) uv += red[buf][w2][8 * gp + 4 + i][lane];
-        hv[s2] = swiglu(gv, uv);
+        hv[s2] = mid_round(swiglu(gv, uv), p.bf16_mid);
         mq = fmaxf(mq, fabsf(hv[s2]));
       }
       mq = fmaxf(mq, __shfl_xor(mq, 16, 64));

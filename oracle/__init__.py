@@ -44,6 +44,10 @@ def _declare(L):
     L.oracle_get_threads.restype = I
     L.oracle_set_exact_rows.argtypes = [I]
     L.oracle_set_exact_rows.restype = I
+    L.oracle_set_bf16_intermediate.argtypes = [I]
+    L.oracle_set_bf16_intermediate.restype = I
+    L.oracle_round_bf16.argtypes = [P, I, P]
+    L.oracle_round_bf16.restype = None
     L.oracle_exp_rows.argtypes = [P, I, P]
     L.oracle_exp_rows.restype = None
     L.oracle_e2m1_x2.argtypes = [I]
@@ -106,6 +110,30 @@ class exact_rows:
 
     def __exit__(self, *exc):
         set_exact_rows(self.old)
+
+
+def set_bf16_intermediate(on: bool) -> bool:
+    """BF16-intermediate mode (SwiGLU output rounded to BF16 before its
+    requantisation) on or off; returns the previous setting."""
+    return bool(lib().oracle_set_bf16_intermediate(int(bool(on))))
+
+
+class bf16_intermediate:
+    """with oracle.bf16_intermediate(): ... runs its body in that mode."""
+
+    def __enter__(self):
+        self.old = set_bf16_intermediate(True)
+
+    def __exit__(self, *exc):
+        set_bf16_intermediate(self.old)
+
+
+def round_bf16(x):
+    """The oracle's BF16 rounding (to nearest, ties to even), as fp32."""
+    x = _c(x, np.float32)
+    y = np.empty_like(x)
+    lib().oracle_round_bf16(_p(x), x.size, _p(y))
+    return y
 
 
 def exp_rows(x):

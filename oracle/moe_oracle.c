@@ -18,6 +18,7 @@
 
 static int g_threads = 1;
 static int g_exact = 0;
+static int g_bf16_mid = 0;
 
 void oracle_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
 int oracle_get_threads(void) { return g_threads; }
@@ -25,6 +26,40 @@ int oracle_set_exact_rows(int on) {
   const int old = g_exact;
   g_exact = on ? 1 : 0;
   return old;
+}
+
+int oracle_set_bf16_intermediate(int on) {
+  const int old = g_bf16_mid;
+  g_bf16_mid = on ? 1 : 0;
+  return old;
+}
+
+/* ------------------------------------------------------------ round_bf16 */
+
+/* From the format's definition: a BF16 number has 8 significant bits and the
+ * fp32 exponent range, so for |x| in [2^(e-1), 2^e) its spacing is 2^(e-8),
+ * and below 2^-126 the spacing stays at the subnormal step 2^-133.  x / spacing
+ * is taken to the nearest integer (ties to the even one) and scaled back; all
+ * of it is exact in double. */
+static float round_bf16_1(float x) {
+  if (x != x || isinf(x) || x == 0.0f) return x;
+  int e;
+  (void)frexp((double)x, &e);
+  if (e < -125) e = -125;
+  const double step = ldexp(1.0, e - 8);
+  const double q = (double)x / step;
+  double n = floor(q);
+  const double frac = q - n;
+  if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0)) n += 1.0;
+  const double v = n * step;
+  const double max_bf16 = ldexp(255.0, 127 - 7); /* (2 - 2^-7) * 2^127 */
+  if (fabs(v) > max_bf16) return x < 0 ? -INFINITY : INFINITY;
+  if (v == 0.0) return x < 0 ? -0.0f : 0.0f;
+  return (float)v;
+}
+
+void oracle_round_bf16(const float* x, int n, float* y) {
+  for (int i = 0; i < n; ++i) y[i] = round_bf16_1(x[i]);
 }
 
 /* ------------------------------------------------------------ exp_rows */
@@ -331,7 +366,11 @@ int oracle_expert_hidden(const uint8_t* gu_codes, const uint8_t* gu_scales,
       rc = matvec_impl(gu_codes + (int64_t)d_ff * ldc, ldc,
                        gu_scales + (int64_t)d_ff * lds, lds, d_ff, d_model, qt,
                        ld_q, st, ld_qs, 1, u, d_ff, 1);
-    if (rc == ORACLE_OK) oracle_swiglu(g, u, d_ff, h + (int64_t)t * ld_h);
+    if (rc == ORACLE_OK) {
+      float* ht = h + (int64_t)t * ld_h;
+      oracle_swiglu(g, u, d_ff, ht);
+      if (g_bf16_mid) oracle_round_bf16(ht, d_ff, ht); /* [gfx90a] §8.2 */
+    }
   }
   free(g);
   free(u);

@@ -36,6 +36,11 @@
  * the router's sigmoid use exp_rows (below) in fp32; router weights sum in
  * pick order; the combine folds the slots with fused multiply-adds in slot
  * order and adds the shared expert last.
+ *
+ * BF16-intermediate mode ([gfx90a] §8.2: the down chain reads an
+ * already-rounded BF16 intermediate), off by default and independent of the
+ * exact-rows mode: each SwiGLU output is rounded to the nearest BF16 value,
+ * ties to even, before its group-32 requantisation.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -55,6 +60,14 @@ int oracle_get_threads(void);
 
 /* exact-rows mode on (1) or off (0, the fp64 reference); returns the old one */
 int oracle_set_exact_rows(int on);
+
+/* BF16-intermediate mode on (1) or off (0); returns the old one */
+int oracle_set_bf16_intermediate(int on);
+
+/* y[i] = the BF16 value nearest x[i] (8 significant bits, BF16's exponent
+ * range with its subnormals, ties to even; beyond the largest finite BF16
+ * plus half its spacing -> infinity; infinities and NaN unchanged), as fp32 */
+void oracle_round_bf16(const float* x, int n, float* y);
 
 /* exp in fp32 by a named sequence: Cody-Waite reduction x = k ln2 + r (ln2 as
  * a 16-bit high part plus a low part), the degree-7 Taylor polynomial of exp
@@ -98,7 +111,8 @@ int oracle_block_dots(const uint8_t* codes, int64_t ld_c, int n_out, int d_in,
 /* h = (float)(silu(g) * u), silu(z) = z / (1 + exp(-z)), in fp64 */
 void oracle_swiglu(const float* g, const float* u, int n, float* h);
 
-/* gate/up projection + SwiGLU for one expert: h[t][f], f < d_ff */
+/* gate/up projection + SwiGLU for one expert: h[t][f], f < d_ff (rounded
+ * to BF16 in the BF16-intermediate mode) */
 int oracle_expert_hidden(const uint8_t* gu_codes, const uint8_t* gu_scales,
                          int d_model, int d_ff, const int8_t* q, int64_t ld_q,
                          const float* qs, int64_t ld_qs, int rows, float* h,

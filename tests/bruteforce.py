@@ -86,9 +86,15 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def ffn(experts, n_experts, top_k, has_shared, q, qs, ids, w):
-    """float64 end-to-end: dequantised projections, fp64 SwiGLU rounded to fp32,
-    numpy requant, dequantised down, fp64 combine."""
+def bf16(x):
+    """Round fp32 values to BF16 (to nearest, ties to even) with torch's CPU cast."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def ffn(experts, n_experts, top_k, has_shared, q, qs, ids, w, bf16_mid=False):
+    """float64 end-to-end: dequantised projections, fp64 SwiGLU rounded to fp32
+    (then to BF16 with bf16_mid), numpy requant, dequantised down, fp64 combine."""
     rows = q.shape[0]
     d_model = experts[next(iter(experts))]["down_codes"].shape[0]
     y = np.zeros((rows, d_model), np.float64)
@@ -102,6 +108,8 @@ def ffn(experts, n_experts, top_k, has_shared, q, qs, ids, w):
             f = gu.size // 2
             h = (silu(np.float32(gu[:f]).astype(np.float64)) *
                  np.float32(gu[f:]).astype(np.float64)).astype(np.float32)
+            if bf16_mid:
+                h = bf16(h)
             hq, hs = quant(h[None, :])
             Y = matvec(ex["down_codes"], ex["down_scales"], hq, hs)[0]
             y[t] += wt * np.float32(Y).astype(np.float64)

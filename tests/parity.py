@@ -74,6 +74,56 @@ def check_hidden(hq_gpu, hs_gpu, hq_o, hs_o, h_o):
     return flips
 
 
+def bf16_tie_mask(h_pre, hs):
+    """Elements whose oracle value before the BF16 rounding lies within
+    FLIP_EPS * d of a BF16 rounding midpoint (either neighbour): there the GPU,
+    from projections a few ulp away, may round to the other BF16 value."""
+    h = np.ascontiguousarray(h_pre, np.float32)
+    mag = h.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    base = mag & np.uint32(0xFFFF0000)
+    up = (base | np.uint32(0x8000)).view(np.float32).astype(np.float64)
+    dn = np.where(base > 0, base - np.uint32(0x8000), np.uint32(0)).astype(np.uint32)
+    dn = dn.view(np.float32).astype(np.float64)
+    a = np.abs(h.astype(np.float64))
+    d = np.repeat(np.asarray(hs, np.float64), 32, axis=1)
+    eps = FLIP_EPS * d
+    return (np.abs(a - up) <= eps) | ((base > 0) & (np.abs(a - dn) <= eps))
+
+
+def check_hidden_bf16(hq_gpu, hs_gpu, hq_o, hs_o, h_o, h_pre):
+    """check_hidden for the BF16-intermediate mode.  A code may also move where
+    the oracle's pre-rounding value sits at a BF16 midpoint (one BF16 step is at
+    most 2^-7 |h| <= d, so at most 2 code units), and a group scale may move only
+    when its largest element sits there; such a group's codes may then all move
+    by up to 2.  Returns per-element flip weights in units of d * |W_down|."""
+    hq_gpu = np.asarray(hq_gpu, np.int32)
+    hq_o = np.asarray(hq_o, np.int32)
+    hs_gpu = np.asarray(hs_gpu, np.float64)
+    hs_o64 = np.asarray(hs_o, np.float64)
+    tie = bf16_tie_mask(h_pre, hs_o)
+    n, F = hq_o.shape
+    G = F // 32
+    a = np.abs(np.asarray(h_o, np.float64)).reshape(n, G, 32)
+    top = a >= a.max(axis=2, keepdims=True) * (1 - 2.0 ** -6)
+    tie_top = (tie.reshape(n, G, 32) & top).any(axis=2)
+    same = np.isclose(hs_gpu, hs_o64, rtol=1e-5, atol=0)
+    moved = ~same
+    assert np.all(tie_top[moved]), "hidden scale moved without a BF16 midpoint at its max"
+    assert np.all(np.abs(hs_gpu[moved] / hs_o64[moved] - 1) <= 2.0 ** -6), "hidden scale"
+    diff = hq_gpu - hq_o
+    weights = np.zeros((n, F), np.float64)
+    g_moved = np.repeat(moved, 32, axis=1)
+    weights[g_moved] = 3.0
+    flips = (diff != 0) & ~g_moved
+    if flips.any():
+        near = boundary_mask(h_o, hs_o) | tie
+        assert np.all(np.abs(diff[flips]) <= 2), "hidden code off by more than 2"
+        assert np.all(near[flips]), "hidden code flipped away from a rounding boundary"
+        weights[flips] = np.abs(diff[flips])
+    assert np.all(np.abs(diff[g_moved]) <= 2), "hidden code off by more than 2"
+    return weights
+
+
 def flip_bound(flips, slot_weight, hs_o, down_col_absmax):
     """Per-token widening of the y tolerance for legitimate requant flips.
 
@@ -81,13 +131,15 @@ def flip_bound(flips, slot_weight, hs_o, down_col_absmax):
     slot_weight:    f32  [rows*(k+1)] oracle combine weight of each hidden row
     hs_o:           f32  [rows*(k+1)][F/32] oracle hidden scales
     down_col_absmax: callable(row) -> f64 [F], max_n |W_down[n][f]| of that row's expert
+    A numeric `flips` weights each element (code units it may have moved by).
     """
     n_rows, F = flips.shape
     out = np.zeros(n_rows, np.float64)
     for r in np.nonzero(flips.any(axis=1))[0]:
         f = np.nonzero(flips[r])[0]
+        m = np.asarray(flips[r, f], np.float64)
         out[r] = np.sum(abs(float(slot_weight[r])) * hs_o[r, f // 32].astype(np.float64) *
-                        down_col_absmax(r)[f]) * (1 + 1e-6)
+                        down_col_absmax(r)[f] * m) * (1 + 1e-6)
     return out
 
 

@@ -144,7 +144,7 @@ def test_decode_step_validation():
 def _layer(**kw):
     d = dict(d_model=4096, d_ff=2048, n_experts=256, top_k=6, has_shared=1,
              gate_up=0x1000000, gate_up_stride=8912896, down=0x2000000, down_stride=4456448,
-             shared_gate_up=0x3000000, shared_down=0x4000000)
+             shared_gate_up=0x3000000, shared_down=0x4000000, flags=0)
     d.update(kw)
     return m.moe_layer_t(*[d[k] for k, _ in m.moe_layer_t._fields_])
 
@@ -165,6 +165,8 @@ def test_ffn_validation(name):
     assert _ffn(f, _layer(n_experts=600)) == SHAPE
     assert _ffn(f, _layer(has_shared=2)) == INVALID
     assert _ffn(f, _layer(shared_down=0)) == INVALID
+    assert _ffn(f, _layer(flags=2)) == INVALID           # unknown layer flag bits
+    assert _ffn(f, _layer(flags=-1)) == INVALID
     assert _ffn(f, _layer(gate_up_stride=8912896 - 256)) == STRIDE
     assert _ffn(f, _layer(down_stride=4456448 + 16)) == ALIGN
     assert _ffn(f, _layer(gate_up=0x1000010)) == ALIGN

@@ -1,12 +1,15 @@
 """GPU parity of the whole routed-expert layer (decode and prefill) through the
 C ABI, stage by stage, against the oracle, at the workloads' real shapes."""
+from contextlib import nullcontext
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from parity import (assert_rows_close, check_hidden, down_col_absmax, flip_bound)
+from parity import (assert_rows_close, check_hidden, check_hidden_bf16, down_col_absmax,
+                    flip_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,10 +39,14 @@ def canonical_experts(L, seed, set_idx, experts):
 
 
 def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
-             ids_override=None, pads=(0, 0, 0)):
-    """Run the GPU layer and check it against the oracle on rows `sample`."""
+             ids_override=None, pads=(0, 0, 0), bf16_mid=False):
+    """Run the GPU layer and check it against the oracle on rows `sample`
+    (bf16_mid: the layer flag and the oracle mode that round the SwiGLU output
+    to BF16 before its requant)."""
     T = x.shape[0]
     layer = layer_for(L, seed, set_idx)
+    if bf16_mid:
+        layer = layer.variant(bf16_intermediate=True)
     pad_x, pad_q, pad_y = pads
     xw = torch.zeros((T, L.d_model + pad_x), device=DEV)
     xw[:, : L.d_model] = torch.from_numpy(x).to(DEV)
@@ -95,8 +102,13 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
         need.add(L.n_experts)
     ex = canonical_experts(L, seed, set_idx, need)
     k, slots = L.top_k, L.top_k + 1
-    y_o, mid = oracle.ffn(ex, L.n_experts, k, L.has_shared, q_o[rows], qs_o[rows], ids_o[rows],
-                          w_o[rows], want_intermediates=True)
+    o_args = (ex, L.n_experts, k, L.has_shared, q_o[rows], qs_o[rows], ids_o[rows], w_o[rows])
+    if bf16_mid:
+        with oracle.bf16_intermediate():
+            y_o, mid = oracle.ffn(*o_args, want_intermediates=True)
+        h_pre = oracle.ffn(*o_args, want_intermediates=True)[1]["h"]
+    else:
+        y_o, mid = oracle.ffn(*o_args, want_intermediates=True)
 
     # stage 3: requantised intermediate read back from the documented workspace
     A = T * k
@@ -118,9 +130,13 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
             o_rows.append(j * slots + i)
             wts.append(w_o[t, i] if i < k else 1.0)
     gpu_rows, o_rows = np.array(gpu_rows), np.array(o_rows)
-    flips = np.zeros((len(rows) * slots, L.d_ff), bool)
-    flips[o_rows] = check_hidden(hb[gpu_rows], hs[gpu_rows], mid["hq"][o_rows],
-                                 mid["hs"][o_rows], mid["h"][o_rows])
+    flips = np.zeros((len(rows) * slots, L.d_ff), np.float64)
+    if bf16_mid:
+        flips[o_rows] = check_hidden_bf16(hb[gpu_rows], hs[gpu_rows], mid["hq"][o_rows],
+                                          mid["hs"][o_rows], mid["h"][o_rows], h_pre[o_rows])
+    else:
+        flips[o_rows] = check_hidden(hb[gpu_rows], hs[gpu_rows], mid["hq"][o_rows],
+                                     mid["hs"][o_rows], mid["h"][o_rows])
     weight = np.zeros(len(rows) * slots)
     weight[o_rows] = wts
     col_max = {}
@@ -135,7 +151,7 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
     extra_slot = flip_bound(flips, weight, mid["hs"], colmax)
     extra = extra_slot.reshape(len(rows), slots).sum(axis=1)
     worst = assert_rows_close(y.cpu().numpy()[rows], y_o, extra=extra, what=entry)
-    return dict(worst=worst, flips=int(flips.sum()), y=y)
+    return dict(worst=worst, flips=int(np.count_nonzero(flips)), y=y)
 
 
 TINY = synth.TINY["layer"]
@@ -487,16 +503,21 @@ def test_decode_exact_rows_across_batch_sizes():
     assert torch.equal(y, y_all[7:8])
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("rows", [1, 3, 16])
-def test_decode_bitwise_equals_exact_rows_oracle(rows):
+def test_decode_bitwise_equals_exact_rows_oracle(rows, bf16):
     # Exact rows, second half: the oracle's exact-rows mode takes the same fp32
     # steps in the same named order (runs of 16 blocks, fmaf, exp_rows, slot
     # order), so every output of a decode step -- codes, scales, routes,
     # weights, hidden codes and scales, y -- must have the oracle's bits.
     # 1 row: the one-row step kernel; 3: down by rows; 16: streaming down.
+    # bf16: the layer flag and the oracle mode that round the SwiGLU output to
+    # BF16 before its requant.
     c = synth.DECODE_BATCH
     L = DSV4
     layer = layer_for(L, c["seed"])
+    if bf16:
+        layer = layer.variant(bf16_intermediate=True)
     x = synth.activations(c["seed"], 950 + rows, rows, L.d_model)
     lg = synth.router_logits(c["seed"], 950 + rows, rows, L.n_experts)
     ws = torch.full((m.moe_ffn_workspace_bytes(layer, rows),), 0x7F, dtype=torch.uint8,
@@ -504,7 +525,7 @@ def test_decode_bitwise_equals_exact_rows_oracle(rows):
     q, qs, ids, w, counts, offsets, srt, y = m.moe_ffn_decode_step(
         layer, torch.from_numpy(x).to(DEV), torch.from_numpy(lg).to(DEV), ws=ws)
     torch.cuda.synchronize()
-    with oracle.exact_rows():
+    with oracle.exact_rows(), (oracle.bf16_intermediate() if bf16 else nullcontext()):
         q_o, qs_o = oracle.quant_q8(x)
         ids_o, w_o = oracle.route(lg, L.top_k)
         need = set(int(e) for e in ids_o.reshape(-1)) | {L.n_experts}
@@ -539,3 +560,51 @@ def test_decode_one_row_tiny_and_odd():
         x = synth.activations(seed, 1, 1, L.d_model)
         lg = synth.router_logits(seed, 1, 1, L.n_experts)
         run_case(L, seed, x, lg)
+
+
+@pytest.mark.parametrize("case", ["tiny-decode", "odd-decode", "odd-prefill-tiles",
+                                  "dsv4-prefill-33", "dsv4-decode-12"])
+def test_bf16_intermediate_other_paths(case):
+    # the BF16-intermediate flag on every gate/up epilogue: the one-pass
+    # projection kernel (shapes the streaming kernel does not take), the
+    # streaming kernel with streaming down, and both prefill tile heights;
+    # against the fp64 oracle in its BF16 mode
+    L, rows, entry = {"tiny-decode": (TINY, synth.TINY["rows"], "moe_ffn_decode"),
+                      "odd-decode": (ODD, 5, "moe_ffn_decode"),
+                      "odd-prefill-tiles": (ODD, 100, "moe_ffn_prefill"),
+                      "dsv4-prefill-33": (DSV4, 33, "moe_ffn_prefill"),
+                      "dsv4-decode-12": (DSV4, 12, "moe_ffn_decode")}[case]
+    seed = 77
+    x = synth.activations(seed, rows, rows, L.d_model)
+    lg = synth.router_logits(seed, rows, rows, L.n_experts)
+    r = run_case(L, seed, x, lg, entry=entry, bf16_mid=True)
+    print(f"{case}: worst err/tol {r['worst']:.3f}, moved codes {r['flips']}")
+
+
+@pytest.mark.parametrize("rows", [512, 4096])
+def test_prefill_bf16_intermediate_sampled(rows):
+    # 512 rows: 32-row tiles; 4096 rows: 128-row tiles
+    c = synth.PREFILL
+    x = synth.activations(c["seed"], rows, rows, DSV4.d_model)
+    lg = synth.router_logits(c["seed"], rows, rows, DSV4.n_experts)
+    sample = np.sort(np.random.default_rng(rows + 1).choice(rows, 16, replace=False))
+    sample[-1] = rows - 1
+    r = run_case(DSV4, c["seed"], x, lg, sample=sample, entry="moe_ffn_prefill", bf16_mid=True)
+    print(f"prefill {rows} bf16: worst err/tol {r['worst']:.3f}, moved codes {r['flips']}")
+
+
+def test_bf16_flag_is_per_layer_struct():
+    # one set of packed weights, flag off and on: the flag is read per call, a
+    # flagged copy leaves the original untouched, and it changes the output
+    c = synth.DECODE_BATCH
+    layer = layer_for(DSV4, c["seed"])
+    lay_b = layer.variant(bf16_intermediate=True)
+    x = torch.from_numpy(synth.activations(c["seed"], 990, 4, DSV4.d_model)).to(DEV)
+    lg = torch.from_numpy(synth.router_logits(c["seed"], 990, 4, DSV4.n_experts)).to(DEV)
+    y0 = m.moe_ffn_decode_step(layer, x, lg)[-1].clone()
+    y1 = m.moe_ffn_decode_step(lay_b, x, lg)[-1].clone()
+    y2 = m.moe_ffn_decode_step(layer, x, lg)[-1].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y2)
+    assert not torch.equal(y0, y1)
+    assert layer.c.flags == 0 and lay_b.c.flags == m.MOE_LAYER_BF16_INTERMEDIATE
