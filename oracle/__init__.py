@@ -61,6 +61,8 @@ def _declare(L):
     L.oracle_quant_q8.argtypes = [P, I64, I, I, P, I64, P, I64]
     L.oracle_route.argtypes = [P, I64, I, I, I, P, P]
     L.oracle_group.argtypes = [P, I, I, P, P, P]
+    L.oracle_router_logits.argtypes = [P, I64, I, I, P, I64, I, P, I64]
+    L.oracle_router_logits.restype = I
     L.oracle_matvec.argtypes = [P, I64, P, I64, I, I, P, I64, P, I64, I, P, I64]
     L.oracle_block_dots.argtypes = [P, I64, I, I, P, I64, I, P]
     L.oracle_swiglu.argtypes = [P, P, I, P]
@@ -180,6 +182,20 @@ def route(logits, top_k: int):
     w = np.zeros((rows, top_k), np.float32)
     _check(lib().oracle_route(_p(lg), E, rows, E, top_k, _p(ids), _p(w)), "route")
     return ids, w
+
+
+def router_logits(x, wr_bits):
+    """logits [rows][E] from x fp32 [rows][D] and BF16 router weights given as
+    their uint16 bit patterns [E][D]."""
+    x = _c(x, np.float32)
+    wr = _c(wr_bits, np.uint16)
+    rows, D = x.shape
+    E = wr.shape[0]
+    assert wr.shape[1] == D
+    lg = np.zeros((rows, E), np.float32)
+    _check(lib().oracle_router_logits(_p(x), D, rows, D, _p(wr), D, E, _p(lg), E),
+           "router_logits")
+    return lg
 
 
 def group(ids, n_experts: int):

@@ -170,6 +170,59 @@ int oracle_quant_q8(const float* x, int64_t ld_x, int rows, int cols,
 
 /* --------------------------------------------------------------- router */
 
+static float bf16_bits_value(uint16_t b) {
+  /* BF16 is the top half of an fp32: sign, 8 exponent bits, 7 fraction bits */
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+int oracle_router_logits(const float* x, int64_t ld_x, int rows, int d_model,
+                         const uint16_t* wr, int64_t ld_w, int n_experts,
+                         float* logits, int64_t ld_l) {
+  if (rows < 0 || d_model < 32 || d_model % 32 || n_experts < 1 ||
+      ld_x < d_model || ld_w < d_model || ld_l < n_experts)
+    return ORACLE_EINVAL;
+  int rc = ORACLE_OK;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int t = 0; t < rows; ++t) {
+    float* xb = (float*)malloc(sizeof(float) * (size_t)d_model);
+    if (!xb) {
+      rc = ORACLE_EINVAL;
+      continue;
+    }
+    oracle_round_bf16(x + (int64_t)t * ld_x, d_model, xb);
+    for (int e = 0; e < n_experts; ++e) {
+      const uint16_t* we = wr + (int64_t)e * ld_w;
+      if (g_exact) {
+        float p[64];
+        for (int l = 0; l < 64; ++l) {
+          p[l] = 0.0f;
+          for (int j = 0; 512 * j < d_model; ++j)
+            for (int i = 0; i < 8; ++i) {
+              const int k = 512 * j + 8 * l + i;
+              if (k < d_model) p[l] = fmaf(xb[k], bf16_bits_value(we[k]), p[l]);
+            }
+        }
+        for (int m = 32; m >= 1; m >>= 1) {
+          float q[64];
+          for (int l = 0; l < 64; ++l) q[l] = p[l] + p[l ^ m];
+          memcpy(p, q, sizeof p);
+        }
+        logits[(int64_t)t * ld_l + e] = p[0];
+      } else {
+        double s = 0.0;
+        for (int k = 0; k < d_model; ++k)
+          s += (double)xb[k] * (double)bf16_bits_value(we[k]);
+        logits[(int64_t)t * ld_l + e] = (float)s;
+      }
+    }
+    free(xb);
+  }
+  return rc;
+}
+
 /* [gfx90a] §3.2 (Execution structure): 256 routed experts, top-6 per token.
  * [gfx90a] §5.3: membership ties are broken by logical expert id and the
  * selected positions come out in a fixed order.  Reading used: experts are

@@ -94,6 +94,18 @@ int oracle_quant_q8(const float* x, int64_t ld_x, int rows, int cols,
 int oracle_route(const float* logits, int64_t ld_l, int rows, int n_experts,
                  int top_k, int32_t* ids, float* w);
 
+/* router projection ([gfx90a] Fig. 1 "Router Top-6"; Table 4: a BF16 router
+ * GEMM): logits[t][e] = sum_k bf16(x[t][k]) * wr[e][k], x fp32 [rows][ld_x]
+ * rounded to BF16 (oracle_round_bf16), wr BF16 bits [n_experts][ld_w].  Every
+ * product is exact in fp32.  Default: fp64 sum rounded once to fp32.
+ * Exact-rows mode: 64 partial sums, partial l taking k = 512 j + 8 l + i
+ * (j ascending, then i = 0..7) with fused multiply-adds from zero, then
+ * p[l] += p[l ^ m] for m = 32, 16, 8, 4, 2, 1; the logit is p[0].
+ * d_model % 32 == 0. */
+int oracle_router_logits(const float* x, int64_t ld_x, int rows, int d_model,
+                         const uint16_t* wr, int64_t ld_w, int n_experts,
+                         float* logits, int64_t ld_l);
+
 /* per-expert histogram, exclusive prefix, stable permutation */
 int oracle_group(const int32_t* ids, int n_assign, int n_experts,
                  int32_t* counts, int32_t* offsets, int32_t* sorted);

@@ -9,7 +9,8 @@ is the one piece shared by the oracle-side tests and the GPU-side callers.
   GPU and gives identical bytes.  Codes are uniform over all 16 E2M1 patterns
   (so -0 occurs); exponents are uniform in [-8, 0], stored as 127 + e.
 * Activations and router logits are N(0,1) from numpy's PCG64 on the host,
-  drawn in fp64 and cast to fp32.
+  drawn in fp64 and cast to fp32; BF16 router weights are such draws scaled
+  by 1/sqrt(d_model) with their low 16 bits cut off.
 """
 from __future__ import annotations
 
@@ -120,6 +121,14 @@ def router_logits(seed: int, step: int, rows: int, n_experts: int, hot_bias=0.0,
 
 def activations(seed: int, step: int, rows: int, d_model: int) -> np.ndarray:
     return normal(seed, 0x20000 + step, (rows, d_model))
+
+
+def router_weights(seed: int, layer: int, n_experts: int, d_model: int) -> np.ndarray:
+    """BF16 router weights as uint16 bit patterns [n_experts][d_model]:
+    N(0, 1/d_model) drawn in fp64, cast to fp32 and cut to its top 16 bits, so
+    that N(0,1) activations give logits of about unit spread."""
+    v = normal(seed, 0x30000 + layer, (n_experts, d_model)) * np.float32(1.0 / np.sqrt(d_model))
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 @dataclass(frozen=True)
