@@ -43,6 +43,9 @@ def parse():
                     choices=["decode", "decode-batch", "prefill", "matvec", "copy"])
     ap.add_argument("--rows", type=int, default=None)
     ap.add_argument("--hot", action="store_true")
+    ap.add_argument("--router", action="store_true",
+                    help="start each step from the hidden state: the router projection "
+                         "(BF16 weights) computes the logits inside the step")
     ap.add_argument("--sets", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None)
@@ -100,6 +103,12 @@ def main():
     for s in range(sets):
         fn = lambda e, s=s: synth.expert_weights(seed, s, e, L.d_model, L.d_ff, device=dev)
         layers.append(m.pack_layer(L.d_model, L.d_ff, L.n_experts, L.top_k, fn, True, dev))
+    base_layers = layers
+    wrs = []
+    if args.router:
+        wrs = [torch.from_numpy(synth.router_weights(seed, s, L.n_experts, L.d_model)
+                                .view(np.int16)).to(dev) for s in range(sets)]
+        layers = [lay.variant(router=wr) for lay, wr in zip(base_layers, wrs)]
     torch.cuda.synchronize()
     print(f"[bench] packed {sets} layer sets in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
@@ -108,6 +117,9 @@ def main():
           for i in range(n_inputs)]
     lgs = [torch.from_numpy(synth.router_logits(seed, i, T, L.n_experts, hot_bias=hot)).to(dev)
            for i in range(n_inputs)]
+    lg_out = torch.empty((T, L.n_experts), dtype=torch.float32, device=dev)
+    if args.router:   # the logits come from the router instead; routes from those
+        lgs = [m.moe_router_logits(xs[i], wrs[i % sets]) for i in range(n_inputs)]
     q = torch.empty((T, L.d_model), dtype=torch.int8, device=dev)
     qs = torch.empty((T, L.d_model // 32), dtype=torch.float32, device=dev)
     route_out = (torch.empty((T, L.top_k), dtype=torch.int32, device=dev),
@@ -120,14 +132,18 @@ def main():
     ffn = m.moe_ffn_prefill if prefill else m.moe_ffn_decode
 
     def step(i):
+        lg = lgs[i % n_inputs]
         if prefill:
             m.moe_quant_act_q8(xs[i % n_inputs], q=q, scales=qs)
-            m.moe_route_group(lgs[i % n_inputs], L.top_k, out=route_out)
+            if args.router:
+                lg = m.moe_router_logits(xs[i % n_inputs], wrs[i % sets], logits=lg_out)
+            m.moe_route_group(lg, L.top_k, out=route_out)
             ids, w, counts, offsets, srt = route_out
             ffn(layers[i % sets], q, qs, ids, w, offsets, srt, y=y, ws=ws)
         else:  # decode: the whole step from the layer input in one call
-            m.moe_ffn_decode_step(layers[i % sets], xs[i % n_inputs], lgs[i % n_inputs], q=q,
-                                  scales=qs, route_out=route_out, y=y, ws=ws)
+            m.moe_ffn_decode_step(layers[i % sets], xs[i % n_inputs],
+                                  lg_out if args.router else lg, q=q, scales=qs,
+                                  route_out=route_out, y=y, ws=ws)
 
     # touched experts per input (bytes are counted from the actual routes)
     touched = []
@@ -178,6 +194,8 @@ def main():
     act_bytes = T * (L.d_model * 4 + L.d_model + L.d_model // 8)  # x read, q + scales written
     mean_touched = float(np.mean(touched))
     step_bytes = mean_touched * (gu_bytes + dn_bytes) + act_bytes + T * L.d_model * 4
+    if args.router:
+        step_bytes += L.n_experts * L.d_model * 2 + T * L.n_experts * 4
 
     # dominant kernel, alone over the rotated sets in a graph: the gate/up
     # projection (decode) or the gate/up GEMM (prefill)
@@ -186,10 +204,10 @@ def main():
     fused1 = not prefill and T == 1   # one row: quantiser + router + gate/up, one kernel
     if fused1:
         kcall = lambda i: m.moe_ffn_decode_step(
-            layers[i % sets], xs[last % n_inputs], lgs[last % n_inputs], q=q, scales=qs,
+            base_layers[i % sets], xs[last % n_inputs], lgs[last % n_inputs], q=q, scales=qs,
             route_out=route_out, y=y, ws=ws, stage_mask=m.MOE_STAGE_GATE_UP)
     else:
-        kcall = lambda i: m.moe_ffn_stages(layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
+        kcall = lambda i: m.moe_ffn_stages(base_layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
                                            q, qs, ids, w, offsets, srt, y, ws)
     g_k = capture(torch, lambda: [kcall(i) for i in range(n_k)])
     g_k.replay()
@@ -227,6 +245,24 @@ def main():
                     kernel=kname, avg_us=round(k_us, 3),
                     bytes_per_launch=int(k_bytes), experts_touched=last_touched)
 
+    router = None
+    if args.router:   # the router projection alone, over the rotated weights
+        rcall = lambda i: m.moe_router_logits(xs[last % n_inputs], wrs[i % sets], logits=lg_out)
+        g_r = capture(torch, lambda: [rcall(i) for i in range(n_k)])
+        g_r.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(kreps):
+            g_r.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        r_us = ev0.elapsed_time(ev1) * 1e3 / (kreps * n_k)
+        r_bytes = L.n_experts * L.d_model * 2 + T * L.d_model * 4 + T * L.n_experts * 4
+        r_flops = 2.0 * T * L.n_experts * L.d_model
+        router = dict(kernel="router_kernel", avg_us=round(r_us, 3), bytes_per_launch=r_bytes,
+                      hbm_gbs=round(r_bytes / (r_us * 1e-6) / 1e9, 1),
+                      fp32_fma_tflops=round(r_flops / (r_us * 1e-6) / 1e12, 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill)
@@ -239,7 +275,9 @@ def main():
         "data": "synthetic (seeded counter-hash weights, N(0,1) activations/logits)",
         "config": {"workload": f"{wl}: E256 top-6 + shared, d_model 4096, d_ff 2048, "
                                f"{T} token(s)/step, {sets} rotated layer sets"
-                               + (", hot-16 +2.0 bias" if hot else ""),
+                               + (", hot-16 +2.0 bias" if hot else "")
+                               + (", router projection in the step (BF16 weights)"
+                                  if args.router else ""),
                    "rows": T, "layer_sets": sets, "seed": seed},
         "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "eager_ms_per_step": round(eager_ms, 4),
@@ -247,6 +285,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if router is not None:
+        line["router"] = router
     emit(line, args)
 
 

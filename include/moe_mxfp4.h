@@ -140,6 +140,28 @@ int moe_route_group(const float* logits, int64_t ld_l, int rows, int n_experts,
                     int top_k, int32_t* ids, float* w, int32_t* counts,
                     int32_t* offsets, int32_t* sorted, void* stream);
 
+/* Router projection ([gfx90a] Fig. 1 "Router Top-6": the router reads the
+ * layer input; Table 4: the router GEMM runs in BF16):
+ *   logits[t][e] = sum_k bf16(x[t][k]) * w_router[e][k]   (fp32)
+ *   x, ld_x        f32 [rows][ld_x] (device) layer input; each element is
+ *                  rounded to BF16 (nearest, ties to even) first
+ *   w_router, ld_w BF16 [n_experts][ld_w] (device) router weights
+ *   logits, ld_l   f32 [rows][ld_l] (device) out, the input of moe_route_group
+ * Every product is exact in fp32; the sum runs in one fixed order, so a
+ * logit has the same bits for any rows and tiling: 64 partial sums, partial l
+ * folding the elements k = 512 j + 8 l + i (j ascending, then i = 0..7) with
+ * fused multiply-adds from zero, then p[l] += p[l ^ m] for m = 32, 16, 8, 4,
+ * 2, 1; the logit is p[0].
+ * rows >= 0 (0: nothing is read, written or enqueued, and the pointers may
+ * be null); d_model % 32 == 0 and <= 8192;
+ * 1 <= n_experts <= 4096; ld_x >= d_model, ld_w >= d_model, ld_l >= n_experts
+ * (MOE_ERR_STRIDE); x 16-byte aligned with ld_x % 4 == 0, w_router 16-byte
+ * aligned with ld_w % 8 == 0 (MOE_ERR_ALIGNMENT).  The caller owns every
+ * buffer. */
+int moe_router_logits(const float* x, int64_t ld_x, int rows, int d_model,
+                      const void* w_router, int64_t ld_w, int n_experts, float* logits,
+                      int64_t ld_l, void* stream);
+
 /* Decode-step inputs in one launch: moe_quant_act_q8 of x and
  * moe_route_group of logits for the same rows, which depend on nothing from
  * each other ([gfx90a] Fig. 1: the router and the activation quantisation
@@ -179,6 +201,12 @@ typedef struct moe_layer {
   const void* shared_gate_up;
   const void* shared_down;
   int flags;      /* MOE_LAYER_* bits; 0 = the default arithmetic */
+  /* optional BF16 router weights [n_experts][router_ld] (device; NULL: none).
+   * When set, moe_ffn_decode_step computes the logits from x itself
+   * (moe_router_logits) into its logits buffer.  16-byte aligned,
+   * router_ld >= d_model and % 8 == 0, d_model <= 8192. */
+  const void* router;
+  int64_t router_ld;
 } moe_layer_t;
 
 /* Layer flag: round the SwiGLU intermediate to BF16 (to nearest, ties to even)
@@ -232,16 +260,19 @@ int moe_ffn_decode(const moe_layer_t* L, const int8_t* q, int64_t ld_q,
  * moe_ffn_decode in one call, every output written as those calls write it
  * (same bits).
  *   x, ld_x      f32 [rows][ld_x] (device) layer input, as for moe_quant_act_q8
- *   logits, ld_l f32 [rows][ld_l] (device) router logits, as for moe_route_group
+ *   logits, ld_l f32 [rows][ld_l] (device) router logits, as for
+ *                moe_route_group; with L->router set, an output instead: the
+ *                step first writes moe_router_logits of x there
  *   q .. qs      out, as moe_quant_act_q8's (and as moe_ffn_decode requires)
  *   ids .. sorted out, as moe_route_group's
  *   y, ws        as for moe_ffn_decode
  * 1 <= rows <= MOE_MAX_DECODE_ROWS; every check of the three calls applies
  * and runs before anything is enqueued.  With one row (and d_model of 1024,
  * 2048 or 4096) the gate/up kernel quantises and routes the row itself, so
- * the step is two launches; otherwise it is the three calls in order. */
+ * the step is two launches; otherwise it is the three calls in order (one
+ * more launch, first, with L->router set). */
 int moe_ffn_decode_step(const moe_layer_t* L, const float* x, int64_t ld_x,
-                        const float* logits, int64_t ld_l, int rows, int8_t* q,
+                        float* logits, int64_t ld_l, int rows, int8_t* q,
                         int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids, float* w,
                         int32_t* counts, int32_t* offsets, int32_t* sorted, float* y,
                         int64_t ld_y, void* ws, size_t ws_bytes, void* stream);
@@ -277,12 +308,13 @@ int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask, const int8
                    size_t ws_bytes, void* stream);
 
 /* The same two stages for moe_ffn_decode_step: MOE_STAGE_GATE_UP covers the
- * quantiser, the router and the gate/up stage (one launch with one row),
+ * router projection (with L->router), the quantiser, the routing and the
+ * gate/up stage (one launch with one row),
  * MOE_STAGE_DOWN the down stage and the combine, which read what a GATE_UP
  * stage of the same inputs left in the outputs and the workspace.  Arguments
  * and errors as moe_ffn_decode_step; stage_mask as for moe_ffn_stages. */
 int moe_ffn_decode_step_stages(const moe_layer_t* L, int stage_mask, const float* x,
-                               int64_t ld_x, const float* logits, int64_t ld_l, int rows,
+                               int64_t ld_x, float* logits, int64_t ld_l, int rows,
                                int8_t* q, int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids,
                                float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
                                float* y, int64_t ld_y, void* ws, size_t ws_bytes, void* stream);

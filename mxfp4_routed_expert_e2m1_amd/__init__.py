@@ -21,7 +21,7 @@ MOE_MAX_DECODE_ROWS = 16
 
 EXPORTS = [
     "moe_packed_bytes", "moe_pack_mxfp4", "moe_unpack_mxfp4", "moe_quant_act_q8",
-    "moe_route_group", "moe_decode_prep", "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout",
+    "moe_route_group", "moe_router_logits", "moe_decode_prep", "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout",
     "moe_ffn_decode", "moe_ffn_decode_step", "moe_ffn_decode_step_stages", "moe_ffn_prefill",
     "moe_ffn_stages",
     "moe_matvec_mxfp4",
@@ -43,7 +43,7 @@ class moe_layer_t(C.Structure):
                 ("gate_up", C.c_void_p), ("gate_up_stride", C.c_int64),
                 ("down", C.c_void_p), ("down_stride", C.c_int64),
                 ("shared_gate_up", C.c_void_p), ("shared_down", C.c_void_p),
-                ("flags", C.c_int)]
+                ("flags", C.c_int), ("router", C.c_void_p), ("router_ld", C.c_int64)]
 
 MOE_LAYER_BF16_INTERMEDIATE = 1
 
@@ -66,6 +66,7 @@ def lib():
         L.moe_unpack_mxfp4.argtypes = [P, I, I, I, P, I64, P, I64, P]
         L.moe_quant_act_q8.argtypes = [P, I64, I, I, P, I64, P, I64, P]
         L.moe_route_group.argtypes = [P, I64, I, I, I, P, P, P, P, P, P]
+        L.moe_router_logits.argtypes = [P, I64, I, I, P, I64, I, P, I64, P]
         L.moe_decode_prep.argtypes = [P, I64, I, P, I64, P, I64, P, I64, I, I, I, P, P, P, P, P,
                                       P]
         L.moe_ffn_workspace_bytes.argtypes = [C.POINTER(moe_layer_t), I]
@@ -176,6 +177,18 @@ def moe_route_group(logits, top_k, n_experts=None, out=None, stream=None):
     return out
 
 
+def moe_router_logits(x, w_router, logits=None, stream=None):
+    """logits [rows][E] (f32) of x [rows][D] (f32) under BF16 router weights
+    w_router [E][D] (torch.bfloat16, or their uint16/int16 bits)."""
+    rows, D = x.shape
+    E = w_router.shape[0]
+    if logits is None:
+        logits = torch.empty((rows, E), dtype=torch.float32, device=x.device)
+    _call("moe_router_logits", _ptr(x), _ld(x), rows, D, _ptr(w_router), _ld(w_router), E,
+          _ptr(logits), _ld(logits), _stream(stream))
+    return logits
+
+
 def moe_decode_prep(x, logits, top_k, n_experts=None, q=None, scales=None, out=None,
                     stream=None):
     """moe_quant_act_q8(x) and moe_route_group(logits, top_k) in one launch
@@ -208,23 +221,29 @@ class Layer:
     [E][stride_dn]; shared_gate_up / shared_down: packed blobs or None."""
 
     def __init__(self, d_model, d_ff, n_experts, top_k, gate_up, down, shared_gate_up=None,
-                 shared_down=None):
-        self.tensors = (gate_up, down, shared_gate_up, shared_down)  # keep alive
+                 shared_down=None, router=None):
+        self.tensors = (gate_up, down, shared_gate_up, shared_down, router)  # keep alive
         has_shared = shared_gate_up is not None
         self.c = moe_layer_t(d_model, d_ff, n_experts, top_k, int(has_shared),
                              gate_up.data_ptr(), gate_up.stride(0) if gate_up.dim() == 2 else 0,
                              down.data_ptr(), down.stride(0) if down.dim() == 2 else 0,
                              shared_gate_up.data_ptr() if has_shared else None,
-                             shared_down.data_ptr() if has_shared else None, 0)
+                             shared_down.data_ptr() if has_shared else None, 0,
+                             router.data_ptr() if router is not None else None,
+                             _ld(router) if router is not None else 0)
         self.d_model, self.d_ff, self.n_experts, self.top_k = d_model, d_ff, n_experts, top_k
         self.has_shared = has_shared
 
-    def variant(self, bf16_intermediate=False):
-        """The same packed weights with other layer flags (moe_layer_t.flags)."""
+    def variant(self, bf16_intermediate=False, router=None):
+        """The same packed weights with other layer flags (moe_layer_t.flags)
+        and, if given, BF16 router weights [E][D] (moe_layer_t.router)."""
         v = Layer.__new__(Layer)
         v.__dict__.update(self.__dict__)
         v.c = moe_layer_t.from_buffer_copy(self.c)
         v.c.flags = MOE_LAYER_BF16_INTERMEDIATE if bf16_intermediate else 0
+        if router is not None:
+            v.tensors = self.tensors[:4] + (router,)
+            v.c.router, v.c.router_ld = router.data_ptr(), _ld(router)
         return v
 
 
@@ -255,15 +274,19 @@ def moe_ffn_decode(layer, q, qs, ids, w, offsets, srt, y=None, ws=None, stream=N
     return _ffn("moe_ffn_decode", layer, q, qs, ids, w, offsets, srt, y, ws, stream)
 
 
-def moe_ffn_decode_step(layer, x, logits, q=None, scales=None, route_out=None, y=None, ws=None,
-                        stream=None, stage_mask=None):
+def moe_ffn_decode_step(layer, x, logits=None, q=None, scales=None, route_out=None, y=None,
+                        ws=None, stream=None, stage_mask=None):
     """One decode step from the layer input: quantise x, route and group the
     logits, run the FFN.  Returns (q, scales, ids, w, counts, offsets, sorted, y),
     every output the separate calls would produce.  stage_mask selects stages
-    (moe_ffn_decode_step_stages)."""
+    (moe_ffn_decode_step_stages).  With router weights in the layer, logits is
+    where the step writes the router's logits (allocated when None)."""
     rows, D = x.shape[0], layer.d_model
     dev = x.device
     E, k = layer.c.n_experts, layer.c.top_k
+    if logits is None:
+        assert layer.c.router, "logits are needed when the layer has no router weights"
+        logits = torch.empty((rows, E), dtype=torch.float32, device=dev)
     if q is None:
         q = torch.empty((rows, D), dtype=torch.int8, device=dev)
     if scales is None:

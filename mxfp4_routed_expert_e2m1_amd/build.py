@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libmoe_mxfp4.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["status.cpp", "pack.hip", "quant.hip", "route.hip", "ffn.hip", "stream.hip",
-           "prefill.hip", "down_rows.hip"]
+           "prefill.hip", "down_rows.hip", "router.hip"]
 # Packed-fp32 VALU ops are disabled: only scalar fp32 FMAs are emitted.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -335,6 +335,11 @@ static int check_layer(const moe_layer_t* L) {
   if (!aligned(L->gate_up, 256) || !aligned(L->down, 256)) return MOE_ERR_ALIGNMENT;
   if (L->has_shared && (!aligned(L->shared_gate_up, 256) || !aligned(L->shared_down, 256)))
     return MOE_ERR_ALIGNMENT;
+  if (L->router) {
+    if (L->d_model > 8192) return MOE_ERR_SHAPE;
+    if (L->router_ld < L->d_model) return MOE_ERR_STRIDE;
+    if (!aligned(L->router, 16) || L->router_ld % 8) return MOE_ERR_ALIGNMENT;
+  }
   return MOE_OK;
 }
 
@@ -502,7 +507,7 @@ extern "C" int moe_decode_prep(const float* x, int64_t ld_x, int cols, int8_t* q
                                int32_t* counts, int32_t* offsets, int32_t* sorted, void* stream);
 
 extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, const float* x,
-                                          int64_t ld_x, const float* logits, int64_t ld_l,
+                                          int64_t ld_x, float* logits, int64_t ld_l,
                                           int rows, int8_t* q, int64_t ld_q, float* qs,
                                           int64_t ld_qs, int32_t* ids, float* w, int32_t* counts,
                                           int32_t* offsets, int32_t* sorted, float* y,
@@ -516,6 +521,11 @@ extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, cons
   rc = route_args_check(logits, ld_l, rows, L->n_experts, L->top_k, ids, w, counts, offsets,
                         sorted);
   if (rc != MOE_OK) return rc;
+  if (L->router) {
+    rc = router_args_check(x, ld_x, rows, L->d_model, L->router, L->router_ld, L->n_experts,
+                           logits, ld_l);
+    if (rc != MOE_OK) return rc;
+  }
   rc = check_acts(q, ld_q, qs, ld_qs, L->d_model, y, ld_y, L->d_model);
   if (rc != MOE_OK) return rc;
   if (!ws) return MOE_ERR_INVALID_ARG;
@@ -523,6 +533,12 @@ extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, cons
   if (ws_bytes < ws_layout(L, rows).total) return MOE_ERR_WORKSPACE;
   if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
   hipStream_t s = (hipStream_t)stream;
+  if (L->router && (stages & MOE_STAGE_GATE_UP)) {
+    // the router projection writes the logits the routing below reads
+    rc = launch_router(x, ld_x, rows, L->d_model, L->router, L->router_ld, L->n_experts, logits,
+                       ld_l, s);
+    if (rc != MOE_OK) return rc;
+  }
   const ProjArgs g = gateup_args(L, q, ld_q, qs, ld_qs, rows, offsets, sorted, ws);
   if (rows == 1 && stream_supported(g.kc_total, g.rg_total)) {
     // one launch quantises, routes and runs gate/up; then the down stage
@@ -544,7 +560,7 @@ extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, cons
 }
 
 extern "C" int moe_ffn_decode_step(const moe_layer_t* L, const float* x, int64_t ld_x,
-                                   const float* logits, int64_t ld_l, int rows, int8_t* q,
+                                   float* logits, int64_t ld_l, int rows, int8_t* q,
                                    int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids, float* w,
                                    int32_t* counts, int32_t* offsets, int32_t* sorted, float* y,
                                    int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {

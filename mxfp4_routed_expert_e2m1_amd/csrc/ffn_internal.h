@@ -61,6 +61,12 @@ struct ProjArgs {
 };
 
 // K/128 in {8, 16, 32} and whole 4-group items
+// router projection (router.hip)
+int router_args_check(const float* x, int64_t ld_x, int rows, int d_model, const void* w_router,
+                      int64_t ld_w, int n_experts, const float* logits, int64_t ld_l);
+int launch_router(const float* x, int64_t ld_x, int rows, int d_model, const void* w_router,
+                  int64_t ld_w, int n_experts, float* logits, int64_t ld_l, hipStream_t s);
+
 bool stream_supported(int kc_total, int rg_total);
 // tiles_bound: an upper bound on the call's tiles (1 for MATVEC)
 void launch_stream(int pass, const ProjArgs& a, int tiles_bound, hipStream_t s);

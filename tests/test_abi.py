@@ -98,6 +98,30 @@ def test_route_validation():
     assert f(*args(1 << 22, 256, 6)) == SHAPE
 
 
+def test_router_validation():
+    f = m.lib().moe_router_logits
+    args = lambda rows=4, D=4096, ldx=4096, w=A, ldw=4096, E=256, ldl=256, x=A, lg=A: (
+        x, ldx, rows, D, w, ldw, E, lg, ldl, None)
+    assert f(*args(rows=-1)) == INVALID
+    assert f(*args(rows=0, x=None, w=None, lg=None)) == OK   # nothing to do
+    assert f(*args(rows=0, ldl=255)) == STRIDE
+    assert f(*args(x=None)) == INVALID
+    assert f(*args(w=None)) == INVALID
+    assert f(*args(lg=None)) == INVALID
+    assert f(*args(D=4016, ldx=4016, ldw=4016)) == SHAPE     # d_model % 32
+    assert f(*args(D=8224, ldx=8224, ldw=8224)) == SHAPE     # d_model > 8192
+    assert f(*args(E=0)) == SHAPE
+    assert f(*args(E=4097, ldl=4097)) == SHAPE
+    assert f(*args(ldx=4092)) == STRIDE
+    assert f(*args(ldw=4064)) == STRIDE
+    assert f(*args(ldl=255)) == STRIDE
+    assert f(*args(x=MIS)) == ALIGN
+    assert f(*args(ldx=4098)) == ALIGN
+    assert f(*args(w=C.c_void_p(0x100008))) == ALIGN
+    assert f(*args(ldw=4100)) == ALIGN
+    assert f(*args(lg=MIS)) == ALIGN
+
+
 def test_decode_prep_validation():
     f = m.lib().moe_decode_prep
 
@@ -139,12 +163,19 @@ def test_decode_step_validation():
     assert f(*args(ws=MIS)) == ALIGN
     assert f(*args(wsb=1000)) == WORKSPACE
     assert f(C.byref(_layer(top_k=0)), *args()[1:]) == SHAPE
+    # router weights in the layer: checked with the layer, then against x/logits
+    assert f(C.byref(_layer(router=0x5000000, router_ld=4092)), *args()[1:]) == STRIDE
+    assert f(C.byref(_layer(router=0x5000008, router_ld=4096)), *args()[1:]) == ALIGN
+    assert f(C.byref(_layer(router=0x5000000, router_ld=4100)), *args()[1:]) == ALIGN
+    lr = _layer(router=0x5000000, router_ld=4096)
+    assert f(C.byref(lr), *args(ldx=4098)[1:]) == ALIGN       # the router's 16-byte rows of x
 
 
 def _layer(**kw):
     d = dict(d_model=4096, d_ff=2048, n_experts=256, top_k=6, has_shared=1,
              gate_up=0x1000000, gate_up_stride=8912896, down=0x2000000, down_stride=4456448,
-             shared_gate_up=0x3000000, shared_down=0x4000000, flags=0)
+             shared_gate_up=0x3000000, shared_down=0x4000000, flags=0, router=0,
+             router_ld=0)
     d.update(kw)
     return m.moe_layer_t(*[d[k] for k, _ in m.moe_layer_t._fields_])
 
