@@ -344,7 +344,7 @@ extern "C" int moe_router_logits(const float* x, int64_t ld_x, int rows, int d_m
                                  const void* w_router, int64_t ld_w, int n_experts, float* logits,
                                  int64_t ld_l, void* stream) {
   int rc = router_args_check(x, ld_x, rows, d_model, w_router, ld_w, n_experts, logits, ld_l);
-  if (rc != MOE_OK) return rc;
+  if (rc != MOE_OK || rows == 0) return rc;
   if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
   return launch_router(x, ld_x, rows, d_model, w_router, ld_w, n_experts, logits, ld_l,
                        (hipStream_t)stream);
