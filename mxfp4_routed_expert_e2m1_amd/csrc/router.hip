@@ -141,23 +141,25 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
 }
 
-// Many rows: the same sums, organised for reuse.  A workgroup stages RT rows
-// of x as BF16 in LDS and gives each wave 16 experts, 4 at a time; the wave
+// Many rows: the same sums, organised for reuse.  A workgroup of 8 waves
+// stages RT rows of x as BF16 in LDS and gives each wave 16 experts, 4 at a
+// time; the wave
 // walks d_model one 512-wide piece at a time (a lane's 8 elements of it), so
 // one read of a row's piece feeds 4 experts and one weight piece feeds RT
 // rows.  Weight pieces are loaded two pieces ahead.  A lane still folds its
 // elements in ascending order, so the bits are those of router_kernel.
 constexpr int kTileExperts = 4;   // experts folded together by a wave
 constexpr int kTileNe = 16;       // experts per wave
+constexpr int kTileWaves = 8;     // waves per workgroup (128 experts share a staged x tile)
 
 template <int RT, int NJ>
-__global__ __launch_bounds__(256, 2) void router_tile_kernel(RouterArgs a) {
+__global__ __launch_bounds__(kTileWaves * 64, 2) void router_tile_kernel(RouterArgs a) {
   extern __shared__ __align__(16) uint16_t xb[];  // [RT][d_model] BF16
   constexpr int EB = kTileExperts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = a.d_model;
   const int t0 = blockIdx.y * RT;
-  const int e0 = (blockIdx.x * 4 + wave) * kTileNe;
+  const int e0 = (blockIdx.x * kTileWaves + wave) * kTileNe;
   const int e_end = min(e0 + kTileNe, a.n_experts);
 
   // weight piece j of experts e .. e+EB (rows past the end re-read the last)
@@ -177,11 +179,11 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(RouterArgs a) {
   if (n_steps > 1) load_piece(e0 + EB * (1 / NJ), 1 % NJ, w1);
 
   const int q4 = D / 4, total = RT * q4;
-  for (int base = tid; base < total; base += 256 * kStageBatch) {
+  for (int base = tid; base < total; base += kTileWaves * 64 * kStageBatch) {
     f32x4 v[kStageBatch];
 #pragma unroll
     for (int u = 0; u < kStageBatch; ++u) {
-      const int idx = base + 256 * u;
+      const int idx = base + kTileWaves * 64 * u;
       const int t = idx / q4, c = idx - t * q4;
       v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (idx < total && t0 + t < a.rows)
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(RouterArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kStageBatch; ++u) {
-      const int idx = base + 256 * u;
+      const int idx = base + kTileWaves * 64 * u;
       if (idx < total) {
         const uint32_t b0 = __float_as_uint(round_bf16(v[u][0])) >> 16;
         const uint32_t b1 = __float_as_uint(round_bf16(v[u][1])) & 0xFFFF0000u;
@@ -287,23 +289,23 @@ template <int RT>
 static void launch_router_tile(const RouterArgs& a, dim3 grid, size_t lds, hipStream_t s) {
   const int nj = (a.d_model + 511) / 512;
   if (nj <= 1)
-    hipLaunchKernelGGL((router_tile_kernel<RT, 1>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_tile_kernel<RT, 1>), grid, dim3(kTileWaves * 64), lds, s, a);
   else if (nj <= 2)
-    hipLaunchKernelGGL((router_tile_kernel<RT, 2>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_tile_kernel<RT, 2>), grid, dim3(kTileWaves * 64), lds, s, a);
   else if (nj <= 4)
-    hipLaunchKernelGGL((router_tile_kernel<RT, 4>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_tile_kernel<RT, 4>), grid, dim3(kTileWaves * 64), lds, s, a);
   else if (nj <= 8)
-    hipLaunchKernelGGL((router_tile_kernel<RT, 8>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_tile_kernel<RT, 8>), grid, dim3(kTileWaves * 64), lds, s, a);
   else
-    hipLaunchKernelGGL((router_tile_kernel<RT, 16>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_tile_kernel<RT, 16>), grid, dim3(kTileWaves * 64), lds, s, a);
 }
 
 // Enqueues the projection; arguments already checked by router_args_check.
 // MOE_ERR_SHAPE, with nothing enqueued, past 65535 row tiles.  Decode rows
 // (router_kernel): tiles of at most 8192 elements of x, one batch of loads
 // per thread, every weight row of a wave loaded at once.  More rows
-// (router_tile_kernel): 8-row tiles (BF16 x, at most 64 KiB), 64 experts per
-// workgroup.
+// (router_tile_kernel): 8-row tiles (BF16 x, at most 64 KiB), 8 waves and
+// 128 experts per workgroup.
 int launch_router(const float* x, int64_t ld_x, int rows, int d_model, const void* w_router,
                   int64_t ld_w, int n_experts, float* logits, int64_t ld_l, hipStream_t s) {
   if (rows == 0) return MOE_OK;
@@ -315,7 +317,8 @@ int launch_router(const float* x, int64_t ld_x, int rows, int d_model, const voi
                decode ? 1 : kTileNe};
   const int64_t gy = ((int64_t)rows + rt - 1) / rt;
   if (gy > 65535) return MOE_ERR_SHAPE;
-  const dim3 grid((n_experts + 4 * a.ne - 1) / (4 * a.ne), (unsigned)gy);
+  const int wpg = decode ? 4 : kTileWaves;  // waves per workgroup
+  const dim3 grid((n_experts + wpg * a.ne - 1) / (wpg * a.ne), (unsigned)gy);
   if (!decode) {
     const size_t lds = (size_t)rt * d_model * sizeof(uint16_t);
     switch (rt) {
