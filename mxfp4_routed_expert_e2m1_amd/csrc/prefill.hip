@@ -35,7 +35,12 @@ namespace moe {
 constexpr int kBMFull = 128;
 constexpr int kBMShort = 32;
 constexpr int kBNGroups = 16;     // 16-row weight groups per workgroup (256 rows)
-constexpr int kGemmThreads = 512; // 8 waves: 4 row quarters x 2 token halves
+// Waves per workgroup: 4 row quarters x TH token parts.  128-row tiles take
+// 16 waves (each 2 of the 8 token groups; 4 waves per SIMD hide the MFMA and
+// load latencies), 32-row tiles 8 (each 1 of 2).  Waves 0-7 issue the ring's
+// loads.
+template <int BM> constexpr int gemm_waves() { return BM == kBMFull ? 16 : 8; }
+template <int BM> constexpr int gemm_th() { return gemm_waves<BM>() / 4; }
 // LDS ring depth (prefetch distance: stages - 1 chunks); 3 x 25.5 KB lets
 // two short-tile workgroups share a CU (a 5-deep ring for one workgroup
 // measured 0.921 ms)
@@ -135,6 +140,7 @@ template <int BM>
 __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>& S, int kc,
                                   int wave, int lane, bool b_live) {
   const int n = lane & 15, g4 = lane >> 4, rq = wave & 3;
+  if (wave >= 8) return;  // waves 8-15 (16-wave workgroups) issue nothing
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rg = 2 * wave + i;
@@ -156,16 +162,17 @@ __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>
 }
 
 // K loop + epilogue of one wave owning row groups prb+4*rq .. +3 and token
-// groups th, th+2, .. (NQ of them live).  Branch-free inner loop.
+// groups th, th+TH, .. (NQ of them live).  Branch-free inner loop.
 template <int PASS, int NQ, int BM>
 __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring) {
   constexpr int NST = ring_stages<BM>();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g4 = lane >> 4;
+  constexpr int TH = gemm_th<BM>();
   const int rq = wave & 3, th = wave >> 2;
   const int nnt = (c.t.count + 15) >> 4;
-  const bool b_live = wave < nnt;  // this wave stages token group `wave`
+  const bool b_live = wave < nnt;  // this wave stages token group `wave` (< 8)
 
   f32x4 acc[4][NQ > 0 ? NQ : 1];
 #pragma unroll
@@ -197,7 +204,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dxv[q4][j] = S.d[th + 2 * q4][j][n];
+        for (int j = 0; j < 4; ++j) dxv[q4][j] = S.d[th + TH * q4][j][n];
       uint32_t sw[4];
       u32x4 aw[4];
 #pragma unroll
@@ -210,7 +217,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
         bf16x8 bfr[NQ];
 #pragma unroll
         for (int q4 = 0; q4 < NQ; ++q4)
-          bfr[q4] = __builtin_bit_cast(bf16x8, S.b[th + 2 * q4][j][lane]);
+          bfr[q4] = __builtin_bit_cast(bf16x8, S.b[th + TH * q4][j][lane]);
         f32x4 r[4][NQ];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -235,7 +242,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
       const int f0 = pr0 * 8;
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4) {
-        const int nt = th + 2 * q4;
+        const int nt = th + TH * q4;
         float hv[8];
         float m = 0.f;
 #pragma unroll
@@ -268,7 +275,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
     } else {
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4) {
-        const int col = (th + 2 * q4) * 16 + n;
+        const int col = (th + TH * q4) * 16 + n;
         if (col >= c.t.count) continue;
         const int64_t orow = c.shared ? (int64_t)c.A + c.t.start + col : p.sorted[c.t.start + col];
 #pragma unroll
@@ -280,7 +287,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
 }
 
 template <int PASS, int BM>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(gemm_waves<BM>() * 64, 1) void gemm_kernel(GemmArgs p) {
   __shared__ Stage<BM> ring[ring_stages<BM>()];
 
   // Block b runs on XCD b % 8 (round-robin dispatch).  XCD x walks tiles
@@ -304,17 +311,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs p) {
   c.A = p.rows * p.top_k;
   c.row0 = c.shared ? (int64_t)c.A + c.t.start : c.t.start;
 
-  // live token groups of this wave's half: th, th+2, th+4, th+6 below nnt
+  // live token groups of this wave's part: th, th+TH, ... below nnt
+  constexpr int TH = gemm_th<BM>();
   const int nnt = (c.t.count + 15) >> 4;
   const int th = (threadIdx.x >> 6) >> 2;
-  const int nq = min(BM / 32, max(0, (nnt - th + 1) / 2));
+  const int nq = min(BM / 16 / TH, max(0, (nnt - th + TH - 1) / TH));
   if constexpr (BM == kBMShort) {
     if (nq == 1) gemm_body<PASS, 1, BM>(p, c, ring);  // wave-uniform
     else gemm_body<PASS, 0, BM>(p, c, ring);
   } else {
     switch (nq) {  // wave-uniform
-      case 4: gemm_body<PASS, 4, BM>(p, c, ring); break;
-      case 3: gemm_body<PASS, 3, BM>(p, c, ring); break;
       case 2: gemm_body<PASS, 2, BM>(p, c, ring); break;
       case 1: gemm_body<PASS, 1, BM>(p, c, ring); break;
       default: gemm_body<PASS, 0, BM>(p, c, ring); break;
@@ -374,9 +380,9 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     g.n_items = tiles * (g.rg_total / kBNGroups);
     const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
     if (short_tiles)
-      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), dim3(kGemmThreads), 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), dim3(gemm_waves<kBMShort>() * 64), 0, s, g);
     else
-      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMFull>), dim3(grid), dim3(kGemmThreads), 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMFull>), dim3(grid), dim3(gemm_waves<kBMFull>() * 64), 0, s, g);
   }
   if (stages & MOE_STAGE_DOWN) {
     const PackedDims pd(L->d_model, L->d_ff);
@@ -397,9 +403,9 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     d.n_items = tiles * (d.rg_total / kBNGroups);
     const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (d.rg_total / kBNGroups));
     if (short_tiles)
-      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMShort>), dim3(grid), dim3(kGemmThreads), 0, s, d);
+      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMShort>), dim3(grid), dim3(gemm_waves<kBMShort>() * 64), 0, s, d);
     else
-      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMFull>), dim3(grid), dim3(kGemmThreads), 0, s, d);
+      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMFull>), dim3(grid), dim3(gemm_waves<kBMFull>() * 64), 0, s, d);
     launch_combine((const float*)(base + lay.partials), ids, w, rows, L->top_k, L->has_shared,
                    L->d_model, y, ld_y, s);
   }
