@@ -31,6 +31,41 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-FFN tokens/s + achieved HBM GB/s (decode 1-16 rows), TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+# HBM bytes per launch of each workload's dominant kernel, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) on the native counters driver
+# replaying this benchmark's own inputs (profiles/hbm_traffic_counters.md),
+# scaled by the plain-copy calibration: read = 2 x FETCH_SIZE, written =
+# WRITE_SIZE.  Valid only for the kernel sources they were taken with (hash
+# below): after any change to csrc/ the benchmark reports traffic as null.
+TRAFFIC_SRC = "ffec2f3cd6651ca1"
+TRAFFIC = {  # (workload, rows): (read bytes, written bytes)
+    ("decode", 1): (2 * 30775.1 * 1024, 48.6 * 1024),
+    ("decode-batch", 16): (2 * 349729.5 * 1024, 688.0 * 1024),
+    ("prefill", 4096): (2 * 1346273.0 * 1024, 146336.0 * 1024),
+    ("matvec", 5): (2 * 15404.7 * 1024, 280.0 * 1024),
+}
+
+
+def kernel_sources_hash():
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mxfp4_routed_expert_e2m1_amd",
+                     "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(key):
+    """Counted HBM bytes per launch for this workload, or None (not counted,
+    or the kernels changed since)."""
+    if key not in TRAFFIC or kernel_sources_hash() != TRAFFIC_SRC:
+        return None
+    r, w = TRAFFIC[key]
+    return int(r + w)
 I8_MFMA_PEAK_TOPS = 5000.0
 
 
@@ -50,6 +85,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None)
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--dump-inputs", default=None, metavar="DIR",
+                    help="write the input of the kernel-timing step (x.f32, logits.f32) "
+                         "for the native counters driver, then exit")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step eagerly instead of replaying HIP graphs (for "
                          "counter profilers that cannot follow graph launches); the timings "
@@ -156,6 +194,13 @@ def main():
     cycle = int(np.lcm(sets, n_inputs))
     reps, rem = divmod(steps, cycle)
     last = (steps - 1) % cycle
+    if args.dump_inputs:
+        os.makedirs(args.dump_inputs, exist_ok=True)
+        xs[last % n_inputs].cpu().numpy().tofile(os.path.join(args.dump_inputs, "x.f32"))
+        lgs[last % n_inputs].cpu().numpy().tofile(os.path.join(args.dump_inputs, "logits.f32"))
+        print(json.dumps({"dumped": args.dump_inputs, "workload": wl, "rows": T,
+                          "experts_touched": touched[last % n_inputs]}))
+        return
     for i in range(max(warmup, cycle)):
         step(i)
     torch.cuda.synchronize()
@@ -223,25 +268,32 @@ def main():
     if prefill:
         k_flops = 2.0 * A * (2 * L.d_ff) * L.d_model
         achieved = k_flops / (k_us * 1e-6) / 1e12
-        hidden_bytes = A * (L.d_ff + L.d_ff // 32 * 4)
-        k_bytes = last_touched * gu_bytes + T * (L.d_model + L.d_model // 8) + hidden_bytes
+        # hidden codes are written as bf16 (2 bytes) with fp32 scales; the GEMM
+        # reads every hidden row's activations as gathered bf16 codes + scales
+        hidden_bytes = A * (2 * L.d_ff + L.d_ff // 32 * 4)
+        k_bytes = last_touched * gu_bytes + A * (2 * L.d_model + L.d_model // 8) + hidden_bytes
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                    traffic=None, kernel="gemm_kernel<gate/up>", avg_us=round(k_us, 3),
+                    traffic=traffic_for((wl, T) if not args.router else None),
+                    kernel="gemm_kernel<gate/up>",
+                    avg_us=round(k_us, 3),
                     i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
                     hbm_gbs=round(k_bytes / (k_us * 1e-6) / 1e9, 1))
     else:
         # gate/up weights of the touched experts, activations, hidden codes out
         # (one row: the fp32 row and the logits in, its codes and routes out)
         k_bytes = (last_touched * gu_bytes + T * (L.d_model + L.d_model // 8)
-                   + A * (L.d_ff + L.d_ff // 32 * 4))
+                   + A * (2 * L.d_ff + L.d_ff // 32 * 4))
         kname = "stream_kernel<gate/up>"
         if fused1:
             k_bytes += T * (L.d_model * 4 + L.n_experts * 4)
             kname = "stream_step1_kernel<quantise + route + gate/up>"
         achieved = k_bytes / (k_us * 1e-6) / 1e9
+        # the counted routes are the benchmark's own (hot-expert and router runs
+        # route differently, except for the one-row step's 7 experts)
+        tkey = (wl, T) if not hot and (not args.router or T == 1) else None
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(tkey),
                     kernel=kname, avg_us=round(k_us, 3),
                     bytes_per_launch=int(k_bytes), experts_touched=last_touched)
 
@@ -406,7 +458,7 @@ def bench_matvec(args, m, synth, np, torch, dev):
         "data": "synthetic", "config": {"workload": f"matvec {N}x{D}, {K} rows, {copies} copies",
                                         "rows": K},
         "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic_for(("matvec", K)),
                          kernel="stream_kernel<matvec>", avg_us=round(us, 3)),
         "cpu_baseline": cpu,
     }

@@ -36,7 +36,23 @@ def build_library(jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    _build_counters()
     return LIB
+
+
+COUNTERS = os.path.join(HERE, "moe_counters")
+
+
+def _build_counters() -> None:
+    """The native counters driver (tools/moe_counters.cpp), linked to the library."""
+    src = os.path.join(HERE, "tools", "moe_counters.cpp")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17",
+           "-I", os.path.join(os.path.dirname(HERE), "include"), src, "-L", HERE,
+           "-lmoe_mxfp4", "-Wl,-rpath,$ORIGIN", "-o", COUNTERS + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for moe_counters:\n{r.stderr}")
+    os.replace(COUNTERS + ".tmp", COUNTERS)
 
 
 if __name__ == "__main__":
