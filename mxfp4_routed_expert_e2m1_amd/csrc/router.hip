@@ -11,13 +11,11 @@
 // m = 32, 16, 8, 4, 2, 1.  Partial l is lane l of one wave, so a logit has
 // the same bits whatever the number of rows or their tiling.
 //
-// Work split: a workgroup of 4 waves takes RT rows, whose x it stages once in
-// LDS (the BF16 values held as fp32, RT * d_model <= 16384), and 4 * ne
-// experts; a wave runs its ne experts EB at a time, a lane holding its NJ
-// 16-byte pieces of each weight row, the next rows loaded while the current
-// ones are folded.  Decode rows: ne = EB = 1, so 64 workgroups per row tile
-// read the 2 MiB of weights of 256 experts once, the first row in flight
-// while x is staged.
+// Work split, decode rows (router_kernel): a workgroup of 4 waves takes RT
+// rows, whose x it stages once in LDS (the BF16 values held as fp32, at most
+// 8192 elements), and 4 experts, one per wave, a lane holding its NJ 16-byte
+// pieces of the expert's weight row: 64 workgroups per row tile read the
+// 2 MiB of weights of 256 experts once, every row in flight while x is staged.
 #include "common.h"
 
 namespace moe {
@@ -29,10 +27,13 @@ struct RouterArgs {
   int64_t ld_w;
   float* logits;
   int64_t ld_l;
-  int rows, d_model, n_experts, ne;
+  int rows, d_model, n_experts;
 };
 
-constexpr int kRouterMaxLds = 16384;  // fp32 elements of staged x per workgroup (64 KiB)
+// staged x per workgroup, in elements: decode tiles as fp32 (32 KiB, one
+// batch of loads per thread), many-row tiles as BF16 (64 KiB)
+constexpr int kDecodeXMax = 8192;
+constexpr int kTileXMax = 32768;
 constexpr int kStageBatch = 8;        // float4 loads a thread has in flight while staging
 
 __device__ inline void bf16x8_unpack(const u32x4 v, float (&f)[8]) {
@@ -43,33 +44,29 @@ __device__ inline void bf16x8_unpack(const u32x4 v, float (&f)[8]) {
   }
 }
 
-template <int NJ, int EB>
-__device__ inline void router_load_rows(const RouterArgs& a, int e, int lane,
-                                        u32x4 (&wv)[EB][NJ]) {
+template <int NJ>
+__device__ inline void router_load_row(const RouterArgs& a, int e, int lane, u32x4 (&wv)[NJ]) {
+  const uint16_t* row = a.w + (int64_t)e * a.ld_w;
 #pragma unroll
-  for (int b = 0; b < EB; ++b) {
-    const uint16_t* row = a.w + (int64_t)min(e + b, a.n_experts - 1) * a.ld_w;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int k = 512 * j + 8 * lane;
-      wv[b][j] = k < a.d_model ? *(const u32x4*)(row + k) : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < NJ; ++j) {
+    const int k = 512 * j + 8 * lane;
+    wv[j] = k < a.d_model ? *(const u32x4*)(row + k) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-// RT rows per workgroup, NJ 512-wide pieces of d_model per lane, EB experts
-// folded together by a wave (their weights share each read of x).
-template <int RT, int NJ, int EB>
+// Decode rows: RT rows per workgroup (x staged in LDS, the BF16 values held
+// as fp32), one expert per wave, NJ 512-wide pieces of d_model per lane; the
+// expert's whole weight row is in flight while x is staged.
+template <int RT, int NJ>
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  extern __shared__ __align__(16) float xs[];  // [RT][d_model], BF16 values in fp32
+  extern __shared__ __align__(16) float xs[];  // [RT][d_model]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = a.d_model;
   const int t0 = blockIdx.y * RT;
-  const int e0 = (blockIdx.x * 4 + wave) * a.ne;
-  const int e_end = min(e0 + a.ne, a.n_experts);
+  const int e = blockIdx.x * 4 + wave;
 
-  u32x4 wv[EB][NJ], wn[EB][NJ];
-  if (e0 < e_end) router_load_rows<NJ, EB>(a, e0, lane, wv);
+  u32x4 wv[NJ];
+  if (e < a.n_experts) router_load_row<NJ>(a, e, lane, wv);
 
   // x rows t0 .. t0+RT rounded to BF16 (nearest, ties to even), kStageBatch
   // loads in flight per thread; rows past the end are zeros, never written
@@ -93,51 +90,35 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     }
   }
   __syncthreads();
+  if (e >= a.n_experts) return;  // past the only barrier
 
-  for (int e = e0; e < e_end; e += EB) {
-    if (e + EB < e_end) router_load_rows<NJ, EB>(a, e + EB, lane, wn);
-    float acc[EB][RT];
+  float acc[RT];
 #pragma unroll
-    for (int b = 0; b < EB; ++b)
+  for (int t = 0; t < RT; ++t) acc[t] = 0.f;
 #pragma unroll
-      for (int t = 0; t < RT; ++t) acc[b][t] = 0.f;
+  for (int j = 0; j < NJ; ++j) {
+    const int k = 512 * j + 8 * lane;
+    if (k < D) {
+      float wf[8];
+      bf16x8_unpack(wv[j], wf);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int k = 512 * j + 8 * lane;
-      if (k < D) {
-        float wf[EB][8];
+      for (int t = 0; t < RT; ++t) {
+        const f32x4 x0 = *(const f32x4*)(xs + t * D + k);
+        const f32x4 x1 = *(const f32x4*)(xs + t * D + k + 4);
+        const float xf[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
-        for (int b = 0; b < EB; ++b) bf16x8_unpack(wv[b][j], wf[b]);
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          const f32x4 x0 = *(const f32x4*)(xs + t * D + k);
-          const f32x4 x1 = *(const f32x4*)(xs + t * D + k + 4);
-          const float xf[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-#pragma unroll
-          for (int b = 0; b < EB; ++b)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[b][t] = fmaf(xf[i], wf[b][i], acc[b][t]);
-        }
+        for (int i = 0; i < 8; ++i) acc[t] = fmaf(xf[i], wf[i], acc[t]);
       }
     }
+  }
 #pragma unroll
-    for (int b = 0; b < EB; ++b)
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
+    for (int m = 32; m >= 1; m >>= 1) acc[t] = acc[t] + __shfl_xor(acc[t], m, 64);
+  if (lane == 0) {
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) acc[b][t] = acc[b][t] + __shfl_xor(acc[b][t], m, 64);
-    if (lane == 0) {
-#pragma unroll
-      for (int b = 0; b < EB; ++b)
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-          if (t0 + t < a.rows && e + b < e_end)
-            a.logits[(int64_t)(t0 + t) * a.ld_l + e + b] = acc[b][t];
-    }
-#pragma unroll
-    for (int b = 0; b < EB; ++b)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) wv[b][j] = wn[b][j];
+    for (int t = 0; t < RT; ++t)
+      if (t0 + t < a.rows) a.logits[(int64_t)(t0 + t) * a.ld_l + e] = acc[t];
   }
 }
 
@@ -270,19 +251,19 @@ int router_args_check(const float* x, int64_t ld_x, int rows, int d_model, const
   return MOE_OK;
 }
 
-template <int RT, int EB>
+template <int RT>
 static void launch_router_rt(const RouterArgs& a, dim3 grid, size_t lds, hipStream_t s) {
   const int nj = (a.d_model + 511) / 512;
   if (nj <= 1)
-    hipLaunchKernelGGL((router_kernel<RT, 1, EB>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_kernel<RT, 1>), grid, dim3(256), lds, s, a);
   else if (nj <= 2)
-    hipLaunchKernelGGL((router_kernel<RT, 2, EB>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_kernel<RT, 2>), grid, dim3(256), lds, s, a);
   else if (nj <= 4)
-    hipLaunchKernelGGL((router_kernel<RT, 4, EB>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_kernel<RT, 4>), grid, dim3(256), lds, s, a);
   else if (nj <= 8)
-    hipLaunchKernelGGL((router_kernel<RT, 8, EB>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_kernel<RT, 8>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((router_kernel<RT, 16, EB>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((router_kernel<RT, 16>), grid, dim3(256), lds, s, a);
 }
 
 template <int RT>
@@ -311,14 +292,14 @@ int launch_router(const float* x, int64_t ld_x, int rows, int d_model, const voi
   if (rows == 0) return MOE_OK;
   const bool decode = rows <= MOE_MAX_DECODE_ROWS;
   int rt = decode ? (rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8) : 8;
-  const int cap = decode ? 8192 : 32768;
+  const int cap = decode ? kDecodeXMax : kTileXMax;
   while (rt > 1 && rt * d_model > cap) rt >>= 1;
-  RouterArgs a{x, ld_x, (const uint16_t*)w_router, ld_w, logits, ld_l, rows, d_model, n_experts,
-               decode ? 1 : kTileNe};
+  const RouterArgs a{x, ld_x, (const uint16_t*)w_router, ld_w, logits, ld_l, rows, d_model,
+                     n_experts};
   const int64_t gy = ((int64_t)rows + rt - 1) / rt;
   if (gy > 65535) return MOE_ERR_SHAPE;
-  const int wpg = decode ? 4 : kTileWaves;  // waves per workgroup
-  const dim3 grid((n_experts + wpg * a.ne - 1) / (wpg * a.ne), (unsigned)gy);
+  const int per_wg = decode ? 4 : kTileWaves * kTileNe;  // experts per workgroup
+  const dim3 grid((n_experts + per_wg - 1) / per_wg, (unsigned)gy);
   if (!decode) {
     const size_t lds = (size_t)rt * d_model * sizeof(uint16_t);
     switch (rt) {
@@ -330,10 +311,10 @@ int launch_router(const float* x, int64_t ld_x, int rows, int d_model, const voi
   } else {
     const size_t lds = (size_t)rt * d_model * sizeof(float);
     switch (rt) {
-      case 1: launch_router_rt<1, 1>(a, grid, lds, s); break;
-      case 2: launch_router_rt<2, 1>(a, grid, lds, s); break;
-      case 4: launch_router_rt<4, 1>(a, grid, lds, s); break;
-      default: launch_router_rt<8, 1>(a, grid, lds, s); break;
+      case 1: launch_router_rt<1>(a, grid, lds, s); break;
+      case 2: launch_router_rt<2>(a, grid, lds, s); break;
+      case 4: launch_router_rt<4>(a, grid, lds, s); break;
+      default: launch_router_rt<8>(a, grid, lds, s); break;
     }
   }
   return launch_status();
