@@ -37,8 +37,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # replaying this benchmark's own inputs (profiles/hbm_traffic_counters.md),
 # scaled by the plain-copy calibration: read = 2 x FETCH_SIZE, written =
 # WRITE_SIZE.  Valid only for the kernel sources they were taken with (hash
-# below): after any change to csrc/ the benchmark reports traffic as null.
-TRAFFIC_SRC = "fb08344cf2ab4d0c"
+# below, over the device code in csrc/): after any change to it the benchmark
+# reports traffic as null.
+TRAFFIC_SRC = "2d236613a72e4058"
 TRAFFIC = {  # (workload, rows): (read bytes, written bytes)
     ("decode", 1): (2 * 30777.0 * 1024, 48.6 * 1024),
     ("decode-batch", 16): (2 * 349734.1 * 1024, 687.7 * 1024),
@@ -48,11 +49,14 @@ TRAFFIC = {  # (workload, rows): (read bytes, written bytes)
 
 
 def kernel_sources_hash():
+    """Hash of the device code (csrc/*.hip and *.h; host-only .cpp excluded)."""
     import hashlib
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mxfp4_routed_expert_e2m1_amd",
                      "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
+        if not f.endswith((".hip", ".h")):
+            continue
         h.update(f.encode())
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())

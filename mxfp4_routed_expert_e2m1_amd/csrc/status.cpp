@@ -2,37 +2,44 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/moe_mxfp4.h"
 
 namespace moe {
 
-// -1 unknown, 0 no, 1 yes; indexed by device ordinal.
-static int g_arch_ok[64] = {
-    -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1,
-    -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1,
-    -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+// Per-device caches, indexed by device ordinal (< 64), shared by every host
+// thread that calls the library: atomics, so concurrent first calls on one
+// device race benignly (both store the same value).
+// g_arch: 0 unknown, 1 not gfx950, 2 gfx950.  g_cus: 0 unknown, else the count.
+static std::atomic<int> g_arch[64];
+static std::atomic<int> g_cus[64];
 
 bool device_is_gfx950() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
-  if (dev < 64 && g_arch_ok[dev] >= 0) return g_arch_ok[dev] == 1;
+  if (dev < 64) {
+    const int c = g_arch[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c == 2;
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
   const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) g_arch_ok[dev] = ok ? 1 : 0;
+  if (dev < 64) g_arch[dev].store(ok ? 2 : 1, std::memory_order_relaxed);
   return ok;
 }
 
 // Compute units of the current device (0 if unknown), cached per device.
-static int g_cus[64] = {0};
-
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && g_cus[dev] > 0) return g_cus[dev];
+  if (dev < 64) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) g_cus[dev] = n;
+  if (dev < 64 && n > 0) g_cus[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
