@@ -44,6 +44,7 @@ TRAFFIC = {  # (workload, rows): (read bytes, written bytes)
     ("decode", 1): (2 * 30777.0 * 1024, 48.6 * 1024),
     ("decode-batch", 16): (2 * 349734.1 * 1024, 687.7 * 1024),
     ("prefill", 4096): (2 * 1346555.0 * 1024, 146336.0 * 1024),
+    ("prefill", 512): (2 * 1179207.25 * 1024, 15348.6 * 1024),
     ("matvec", 5): (2 * 15404.8 * 1024, 280.0 * 1024),
 }
 
@@ -276,13 +277,24 @@ def main():
         # reads every hidden row's activations as gathered bf16 codes + scales
         hidden_bytes = A * (2 * L.d_ff + L.d_ff // 32 * 4)
         k_bytes = last_touched * gu_bytes + A * (2 * L.d_model + L.d_model // 8) + hidden_bytes
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                    traffic=traffic_for((wl, T) if not args.router else None),
-                    kernel="gemm_kernel<gate/up>",
-                    avg_us=round(k_us, 3),
-                    i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
-                    hbm_gbs=round(k_bytes / (k_us * 1e-6) / 1e9, 1))
+        hbm_gbs = k_bytes / (k_us * 1e-6) / 1e9
+        # the bound is the one the kernel's arithmetic intensity selects: below
+        # the ridge (peak flops / peak bytes) the weights' stream bounds it
+        ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        intensity = k_flops / k_bytes
+        common = dict(traffic=traffic_for((wl, T) if not args.router else None),
+                      kernel="gemm_kernel<gate/up>", avg_us=round(k_us, 3),
+                      flop_per_byte=round(intensity, 1), ridge_flop_per_byte=round(ridge, 1))
+        if intensity >= ridge:
+            roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), **common,
+                        i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
+                        hbm_gbs=round(hbm_gbs, 1))
+        else:
+            roof = dict(bound="hbm", achieved=round(hbm_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(hbm_gbs / HBM_PEAK_GBS, 4), **common,
+                        tflops=round(achieved, 2),
+                        mfma_frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4))
     else:
         # gate/up weights of the touched experts, activations, hidden codes out
         # (one row: the fp32 row and the logits in, its codes and routes out)
