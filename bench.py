@@ -83,6 +83,9 @@ def parse():
                     choices=["decode", "decode-batch", "prefill", "matvec", "copy"])
     ap.add_argument("--rows", type=int, default=None)
     ap.add_argument("--hot", action="store_true")
+    ap.add_argument("--shard", choices=["tp8"], default=None,
+                    help="one GPU's share of a tensor-parallel layer: d_ff split 8 ways "
+                         "(256 features per expert), the same experts and routes")
     ap.add_argument("--router", action="store_true",
                     help="start each step from the hidden state: the router projection "
                          "(BF16 weights) computes the logits inside the step")
@@ -128,6 +131,9 @@ def main():
         return bench_copy(args, torch, dev)
 
     L = synth.DSV4_LAYER
+    if args.shard == "tp8":
+        L = synth.Layer(n_experts=L.n_experts, top_k=L.top_k, d_model=L.d_model,
+                        d_ff=L.d_ff // 8, has_shared=L.has_shared)
     if wl == "decode":
         T, seed, sets = 1, synth.DECODE["seed"], 8
     elif wl == "decode-batch":
@@ -282,7 +288,7 @@ def main():
         # the ridge (peak flops / peak bytes) the weights' stream bounds it
         ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         intensity = k_flops / k_bytes
-        common = dict(traffic=traffic_for((wl, T) if not args.router else None),
+        common = dict(traffic=traffic_for((wl, T) if not args.router and not args.shard else None),
                       kernel="gemm_kernel<gate/up>", avg_us=round(k_us, 3),
                       flop_per_byte=round(intensity, 1), ridge_flop_per_byte=round(ridge, 1))
         if intensity >= ridge:
@@ -307,7 +313,7 @@ def main():
         achieved = k_bytes / (k_us * 1e-6) / 1e9
         # the counted routes are the benchmark's own (hot-expert and router runs
         # route differently, except for the one-row step's 7 experts)
-        tkey = (wl, T) if not hot and (not args.router or T == 1) else None
+        tkey = (wl, T) if not hot and not args.shard and (not args.router or T == 1) else None
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(tkey),
                     kernel=kname, avg_us=round(k_us, 3),
@@ -341,7 +347,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4(e2m1+e8m0) x int8 -> exact block dots, f32 accumulate",
         "data": "synthetic (seeded counter-hash weights, N(0,1) activations/logits)",
-        "config": {"workload": f"{wl}: E256 top-6 + shared, d_model 4096, d_ff 2048, "
+        "config": {"workload": f"{wl}: E256 top-6 + shared, d_model 4096, d_ff {L.d_ff}"
+                               + (" (TP8 shard of d_ff 2048)" if args.shard else "") + ", "
                                f"{T} token(s)/step, {sets} rotated layer sets"
                                + (", hot-16 +2.0 bias" if hot else "")
                                + (", router projection in the step (BF16 weights)"

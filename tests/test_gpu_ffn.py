@@ -608,3 +608,45 @@ def test_bf16_flag_is_per_layer_struct():
     assert torch.equal(y0, y2)
     assert not torch.equal(y0, y1)
     assert layer.c.flags == 0 and lay_b.c.flags == m.MOE_LAYER_BF16_INTERMEDIATE
+
+
+# What one GPU of a sharded layer runs, at its real shape.  TP8: every expert
+# with d_ff split 8 ways (2048 / 8 = 256 features per GPU).  EP8: 32 of the
+# 256 experts live on this GPU (plus the shared expert); the global top-6
+# routes to other GPUs' experts are -1 sentinels and the local ones are
+# renumbered 0..31.
+TP8 = synth.Layer(n_experts=256, top_k=6, d_model=4096, d_ff=256, has_shared=True)
+EP8 = synth.Layer(n_experts=32, top_k=6, d_model=4096, d_ff=2048, has_shared=True)
+
+
+def ep8_routes(seed, step, rows, share=3):
+    """Global top-6 over 256 experts, kept only where this GPU's 32 own them."""
+    lg = synth.router_logits(seed, step, rows, 256)
+    ids, _ = oracle.route(lg, 6)
+    lo = 32 * share
+    local = np.where((ids >= lo) & (ids < lo + 32), ids - lo, -1).astype(np.int32)
+    return lg[:, lo:lo + 32].copy(), local
+
+
+@pytest.mark.parametrize("rows,entry", [(1, "moe_ffn_decode"), (16, "moe_ffn_decode"),
+                                        (16, "step"), (512, "moe_ffn_prefill")])
+def test_tp8_shard_shape(rows, entry):
+    seed = 61
+    x = synth.activations(seed, rows, rows, TP8.d_model)
+    lg = synth.router_logits(seed, rows, rows, TP8.n_experts)
+    sample = None if rows <= 16 else np.array([0, 1, 100, 255, 256, 400, 510, 511])
+    r = run_case(TP8, seed, x, lg, entry=entry, sample=sample)
+    print(f"TP8 {rows} {entry}: worst err/tol {r['worst']:.3f}, flips {r['flips']}")
+
+
+@pytest.mark.parametrize("rows,entry", [(1, "moe_ffn_decode"), (16, "moe_ffn_decode"),
+                                        (4096, "moe_ffn_prefill")])
+def test_ep8_share_shape(rows, entry):
+    seed = 62
+    x = synth.activations(seed, rows, rows, EP8.d_model)
+    lg_local, ids_local = ep8_routes(seed, rows, rows)
+    sample = None if rows <= 16 else np.array([0, 7, 1000, 2047, 3000, 4095])
+    r = run_case(EP8, seed, x, lg_local, entry=entry, sample=sample, ids_override=ids_local)
+    owned = int((ids_local >= 0).sum())
+    print(f"EP8 {rows} {entry}: {owned} of {rows * 6} routes local, worst err/tol "
+          f"{r['worst']:.3f}, flips {r['flips']}")
