@@ -231,15 +231,22 @@ def main():
     g_step.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event between replays (no synchronisation) gives each cycle's time
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev0.record(stream)
-    for _ in range(reps):
+    for i in range(reps):
+        marks[i].record(stream)
         g_step.replay()
+    marks[reps].record(stream)
     if g_rem is not None:
         g_rem.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     if not torch.equal(y, y_eager):
         raise SystemExit("graph replay differs from the eager step")
+    cycle_ms = [marks[i].elapsed_time(marks[i + 1]) / cycle for i in range(reps)]
+    step_pct = ([round(float(v), 5) for v in np.percentile(cycle_ms, [10, 50, 90])]
+                if cycle_ms else None)
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / steps
     tok_s = T * steps / (ms_total / 1e3)
@@ -356,6 +363,8 @@ def main():
                    "rows": T, "layer_sets": sets, "seed": seed},
         "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "eager_ms_per_step": round(eager_ms, 4),
+        # per-step ms of each replayed rotation cycle: p10, median, p90
+        "ms_per_step_p10_p50_p90": step_pct, "cycles": len(cycle_ms), "steps_per_cycle": cycle,
         "step_bytes": int(step_bytes),
         "roofline": roof,
         "cpu_baseline": cpu,
