@@ -426,9 +426,21 @@ def cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill):
     oracle.group(ido, L.n_experts)
     oracle.ffn(ex, L.n_experts, L.top_k, True, qo, qso, ido, wo)
     dt = time.perf_counter() - t0
+    # the same steps on one thread, over the first S1 rows of the sample
+    S1 = min(S, 8)
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    qo, qso = oracle.quant_q8(x[:S1])
+    ido, wo = oracle.route(lg[:S1], L.top_k)
+    oracle.group(ido, L.n_experts)
+    oracle.ffn(ex, L.n_experts, L.top_k, True, qo, qso, ido, wo)
+    dt1 = time.perf_counter() - t1
+    oracle.set_threads(threads)
     return {"value": round(S / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{S} rows drawn like the workload's (layer set 0, {len(need)} experts): "
-                      f"quant, route, group, FFN in fp64; {dt:.1f}s wall on {threads} threads"}
+                      f"quant, route, group, FFN in fp64; {dt:.1f}s wall on {threads} threads",
+            "value_1_thread": round(S1 / dt1, 4),
+            "sample_1_thread": f"the first {S1} of those rows on 1 thread, {dt1:.1f}s wall"}
 
 
 def bench_matvec(args, m, synth, np, torch, dev):
