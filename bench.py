@@ -40,9 +40,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # below, over the device code in csrc/): after any change to it the benchmark
 # reports traffic as null.
 TRAFFIC_SRC = "2d236613a72e4058"
-TRAFFIC = {  # (workload, rows): (read bytes, written bytes)
+TRAFFIC = {  # (workload, rows[, variant]): (read bytes, written bytes)
     ("decode", 1): (2 * 30777.0 * 1024, 48.6 * 1024),
     ("decode-batch", 16): (2 * 349734.1 * 1024, 687.7 * 1024),
+    ("decode-batch", 16, "hot"): (2 * 171023.99 * 1024, 676.9 * 1024),
     ("prefill", 4096): (2 * 1346555.0 * 1024, 146336.0 * 1024),
     ("prefill", 512): (2 * 1179207.25 * 1024, 15348.6 * 1024),
     ("matvec", 5): (2 * 15404.8 * 1024, 280.0 * 1024),
@@ -320,7 +321,8 @@ def main():
         achieved = k_bytes / (k_us * 1e-6) / 1e9
         # the counted routes are the benchmark's own (hot-expert and router runs
         # route differently, except for the one-row step's 7 experts)
-        tkey = (wl, T) if not hot and not args.shard and (not args.router or T == 1) else None
+        tkey = ((wl, T) + (("hot",) if hot else ())
+                if not args.shard and (not args.router or (T == 1 and not hot)) else None)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(tkey),
                     kernel=kname, avg_us=round(k_us, 3),
