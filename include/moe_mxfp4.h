@@ -72,8 +72,14 @@ extern "C" {
  *   scales uint8 [n_out][ld_scales] (device): E8M0 exponent byte of each run
  *          of 32 consecutive elements of a row; ld_scales >= d_in/32.
  * Supported shapes: n_out % 16 == 0, d_in % 128 == 0.  codes and ld_codes
- * must be 4-byte aligned.  E8M0 bytes 2..252 are represented exactly by the
- * kernels; other values are outside the contract.
+ * must be 4-byte aligned.  E8M0 bytes 2..240 are within the contract: every
+ * block term (the exact integer block dot times 2^(u-128)) is then an exact,
+ * finite fp32 value.  From 241 up a block term whose |dot| nears its
+ * maximum of 48768 (32 x 127 x 12, in half E2M1 steps) overflows fp32 before
+ * the activation scale is applied, so an output can be infinite where the
+ * exact result is finite; bytes 0, 1 and above 240 are outside the contract.
+ * Outputs are fp32 sums: a row whose exact partial sums exceed fp32's range
+ * overflows like any fp32 accumulation.
  *
  * gate_up_interleave = 1 declares a gate/up matrix (n_out = 2F, the F gate
  * rows first, then the F up rows; F % 16 == 0): the packer interleaves

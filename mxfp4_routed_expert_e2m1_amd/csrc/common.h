@@ -73,7 +73,11 @@ __host__ __device__ inline int packed_group_src_row(int pr, int n_out, int inter
 }
 
 // ------------------------------------------------------ device primitives
-// E8M0 byte -> fp32 2^(u-127) (exact for u in 1..254).
+// E8M0 byte -> fp32 2^(u-127) (exact for u in 1..254).  Folded into the
+// bf16 A fragment (value x 2^(u-127), E2M1 magnitudes up to 6) it stays
+// finite up to u = 252, but the matrix-core result, the block dot times
+// 2^(u-128), needs |dot| x 2^(u-128) < 2^128: with |dot| up to 48768
+// (32 x 127 x 12, in units of half an E2M1 step) that holds for u <= 240.
 __device__ inline float e8m0_to_f32(uint32_t u) { return __uint_as_float(u << 23); }
 
 // One A fragment: the 8 E2M1 codes of a dword (element 2i in the low nibble of
@@ -118,8 +122,9 @@ __device__ inline int lane_id() { return threadIdx.x & 63; }
 // can repeat it bit for bit (exact rows): Cody-Waite reduction x = k ln2 + r
 // with ln2 split in two (the high part exact in 16 bits), the degree-7 Taylor
 // polynomial of exp on |r| <= ln2/2 in Horner form with fused multiply-adds
-// (coefficients 1/n! rounded to fp32), then scaling by 2^k.  Within 2 ulp
-// of exp; 0 below -104, infinity above 89.
+// (coefficients 1/n! rounded to fp32), then scaling by 2^k.  Within 1 ulp
+// of exp over the normal range (0.92 ulp at most); 0 below -104, infinity
+// above 89.
 __device__ inline float exp_rows(float x) {
   if (!(x >= -104.0f)) return x != x ? x : 0.0f;
   if (x > 89.0f) return __builtin_inff();

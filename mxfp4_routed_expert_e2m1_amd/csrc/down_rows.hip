@@ -17,6 +17,8 @@
 // Same exact block dots as every other projection here (FP4 converter with
 // the E8M0 scale folded in, one 16x16x32 bf16 matrix-core op per 32-element
 // block, fp32 FMA with the hidden scale).
+#include <atomic>
+
 #include "ffn_internal.h"
 
 namespace moe {
@@ -319,8 +321,10 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
   int nc = copy_pieces(L, rows);
   if (nc < 1 || nc > 16) return MOE_ERR_SHAPE;
   if (nc > 8) nc = nc <= 12 ? 12 : 16;
-  // allow more than 64 KiB of dynamic LDS: once per device and variant
-  static bool lds_raised[64][17] = {};
+  // allow more than 64 KiB of dynamic LDS: once per device and variant (an
+  // atomic flag: concurrent first calls from several host threads both set
+  // the attribute, which is harmless)
+  static std::atomic<bool> lds_raised[64][17];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
   const void* fn = nullptr;
@@ -336,11 +340,11 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
     case 12: fn = (const void*)down_rows_kernel<12>; break;
     default: fn = (const void*)down_rows_kernel<16>; break;
   }
-  if (!lds_raised[dev][nc]) {
+  if (!lds_raised[dev][nc].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDownRowsMaxLds) !=
         hipSuccess)
       return MOE_ERR_HIP;
-    lds_raised[dev][nc] = true;
+    lds_raised[dev][nc].store(true, std::memory_order_release);
   }
   const int cap = tiles_bound(L, rows);
   const dim3 grid((unsigned)pd.rg), block(kDRThreads);

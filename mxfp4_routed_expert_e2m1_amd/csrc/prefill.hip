@@ -13,10 +13,11 @@
 //
 //   * A prep kernel gathers every hidden row's activation codes once into
 //     bf16 rows in tile order (so a tile's token rows are contiguous).
-//   * A workgroup owns 128 token rows x 256 weight rows; 8 waves = 4 row
-//     quarters x 2 token halves (token groups interleaved for balance); wave
-//     tile = 4 row groups x up to 4 token groups, the live count being a
-//     template parameter so the inner loop is branch-free.
+//   * A workgroup owns 128 token rows x 256 weight rows; 16 waves = 4 row
+//     quarters x 4 token parts (token groups interleaved for balance); wave
+//     tile = 4 row groups x up to 2 token groups, the live count being a
+//     template parameter so the inner loop is branch-free.  32-row tiles
+//     take 8 waves (4 row quarters x 2 token parts, one token group each).
 //   * Weights, scales, token fragments and activation scales stream through
 //     a 3-stage LDS ring filled by direct global->LDS loads (no registers),
 //     each piece in the lane order its reader uses.

@@ -308,6 +308,35 @@ def test_block_dots_extremes():
     np.testing.assert_array_equal(dots.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("u", [240, 241])
+def test_block_term_overflow_bound(u):
+    # The contract's top E8M0 byte.  Every block holds the largest dot
+    # (codes +6 -> 12 in half steps, q = 127: 32 * 127 * 12 = 48768) and the
+    # activation scale is 2^-10, so the exact output 4 * 48768 * 2^(u-128-10)
+    # is finite at both bytes.  The matrix core forms the block term
+    # 48768 * 2^(u-128) before the activation scale: finite and exact at 240
+    # (the output equals the oracle's bit for bit), above fp32's range at 241,
+    # where the output overflows although the exact value does not -- the
+    # reason the header stops the contract at 240.
+    n_out, d_in = 16, 128
+    codes = torch.full((n_out, d_in // 2), 0x77, dtype=torch.uint8, device=DEV)
+    scales = torch.full((n_out, d_in // 32), u, dtype=torch.uint8, device=DEV)
+    x = np.full((1, d_in), 127.0 * 2.0 ** -10, np.float32)
+    packed = m.moe_pack_mxfp4(codes, scales, 0)
+    q, qs = m.moe_quant_act_q8(torch.from_numpy(x).to(DEV))
+    y = m.moe_matvec_mxfp4(packed, n_out, d_in, q, qs)
+    _sync()
+    q_o, qs_o = oracle.quant_q8(x)
+    assert np.all(qs_o == np.float32(2.0 ** -10)) and np.all(q_o == 127)
+    y_o = oracle.matvec(codes.cpu().numpy(), scales.cpu().numpy(), q_o, qs_o)
+    exact = 4 * 48768 * 2.0 ** (u - 128 - 10)
+    assert np.all(y_o == np.float32(exact)) and np.all(np.isfinite(y_o))
+    if u <= 240:
+        np.testing.assert_array_equal(y.cpu().numpy(), y_o)
+    else:
+        assert torch.all(torch.isinf(y))
+
+
 def test_generator_cpu_gpu_identical():
     # the input generator gives the same bytes on both sides
     key = synth.stream_key(2, 0, 17, synth.GATE_UP_CODES)
