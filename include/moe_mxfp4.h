@@ -283,6 +283,26 @@ int moe_ffn_decode_step(const moe_layer_t* L, const float* x, int64_t ld_x,
                         int32_t* counts, int32_t* offsets, int32_t* sorted, float* y,
                         int64_t ld_y, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_ffn_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace lives in a file-scope
+ * device array of the library, MOE_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU,
+ * held from the first call on that GPU until the process ends; the call
+ * itself allocates and frees nothing.  Its address is looked up once per
+ * device, on the first call with that device current.  Arguments, checks and
+ * results are those of moe_ffn_decode_step (same kernels, same bits), and a
+ * layer whose workspace (moe_ffn_workspace_bytes(L, rows)) exceeds the array
+ * is rejected with MOE_ERR_WORKSPACE before anything is enqueued (the
+ * DeepSeek-V4 layer at 16 rows needs 3.3 MB).  Every call on one GPU shares
+ * that GPU's array and nothing in it needs clearing, but calls that overlap
+ * on one GPU (several streams, several host threads) race on it: order them
+ * on one stream. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_ffn_decode_step_noalloc(const moe_layer_t* L, const float* x, int64_t ld_x,
+                                float* logits, int64_t ld_l, int rows, int8_t* q,
+                                int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids, float* w,
+                                int32_t* counts, int32_t* offsets, int32_t* sorted, float* y,
+                                int64_t ld_y, void* stream);
 
 /* Prefill chunk: same arguments and results as moe_ffn_decode for any
  * rows >= 1 (tuned for 512..4096).  Grid sizes derive from host-known bounds

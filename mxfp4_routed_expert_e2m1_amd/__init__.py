@@ -22,7 +22,8 @@ MOE_MAX_DECODE_ROWS = 16
 EXPORTS = [
     "moe_packed_bytes", "moe_pack_mxfp4", "moe_unpack_mxfp4", "moe_quant_act_q8",
     "moe_route_group", "moe_router_logits", "moe_decode_prep", "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout",
-    "moe_ffn_decode", "moe_ffn_decode_step", "moe_ffn_decode_step_stages", "moe_ffn_prefill",
+    "moe_ffn_decode", "moe_ffn_decode_step", "moe_ffn_decode_step_stages",
+    "moe_ffn_decode_step_noalloc", "moe_ffn_prefill",
     "moe_ffn_stages",
     "moe_matvec_mxfp4",
     "moe_debug_block_dots", "moe_status_string",
@@ -81,6 +82,7 @@ def lib():
                      I64, P, SZ, P]
         L.moe_ffn_decode_step.argtypes = step_args
         L.moe_ffn_decode_step_stages.argtypes = [step_args[0], I] + step_args[1:]
+        L.moe_ffn_decode_step_noalloc.argtypes = step_args[:17] + [P]
         L.moe_matvec_mxfp4.argtypes = [P, I, I, P, I64, P, I64, I, P, I64, P]
         L.moe_debug_block_dots.argtypes = [P, I, I, P, I64, I, P, P]
         L.moe_status_string.argtypes = [I]
@@ -274,13 +276,7 @@ def moe_ffn_decode(layer, q, qs, ids, w, offsets, srt, y=None, ws=None, stream=N
     return _ffn("moe_ffn_decode", layer, q, qs, ids, w, offsets, srt, y, ws, stream)
 
 
-def moe_ffn_decode_step(layer, x, logits=None, q=None, scales=None, route_out=None, y=None,
-                        ws=None, stream=None, stage_mask=None):
-    """One decode step from the layer input: quantise x, route and group the
-    logits, run the FFN.  Returns (q, scales, ids, w, counts, offsets, sorted, y),
-    every output the separate calls would produce.  stage_mask selects stages
-    (moe_ffn_decode_step_stages).  With router weights in the layer, logits is
-    where the step writes the router's logits (allocated when None)."""
+def _step_outputs(layer, x, logits, q, scales, route_out, y):
     rows, D = x.shape[0], layer.d_model
     dev = x.device
     E, k = layer.c.n_experts, layer.c.top_k
@@ -299,14 +295,41 @@ def moe_ffn_decode_step(layer, x, logits=None, q=None, scales=None, route_out=No
                      torch.empty(rows * k, dtype=torch.int32, device=dev))
     if y is None:
         y = torch.empty((rows, D), dtype=torch.float32, device=dev)
+    return logits, q, scales, route_out, y
+
+
+def moe_ffn_decode_step(layer, x, logits=None, q=None, scales=None, route_out=None, y=None,
+                        ws=None, stream=None, stage_mask=None):
+    """One decode step from the layer input: quantise x, route and group the
+    logits, run the FFN.  Returns (q, scales, ids, w, counts, offsets, sorted, y),
+    every output the separate calls would produce.  stage_mask selects stages
+    (moe_ffn_decode_step_stages).  With router weights in the layer, logits is
+    where the step writes the router's logits (allocated when None)."""
+    rows = x.shape[0]
+    logits, q, scales, route_out, y = _step_outputs(layer, x, logits, q, scales, route_out, y)
     if ws is None:
-        ws = torch.empty(moe_ffn_workspace_bytes(layer, rows), dtype=torch.uint8, device=dev)
+        ws = torch.empty(moe_ffn_workspace_bytes(layer, rows), dtype=torch.uint8,
+                         device=x.device)
     ids, w, counts, offsets, srt = route_out
     fn, pre = (("moe_ffn_decode_step", ()) if stage_mask is None else
                ("moe_ffn_decode_step_stages", (int(stage_mask),)))
     _call(fn, C.byref(layer.c), *pre, _ptr(x), _ld(x), _ptr(logits), _ld(logits), rows,
           _ptr(q), _ld(q), _ptr(scales), _ld(scales), _ptr(ids), _ptr(w), _ptr(counts),
           _ptr(offsets), _ptr(srt), _ptr(y), _ld(y), _ptr(ws), ws.numel(), _stream(stream))
+    return (q, scales) + tuple(route_out) + (y,)
+
+
+def moe_ffn_decode_step_noalloc(layer, x, logits=None, q=None, scales=None, route_out=None,
+                                y=None, stream=None):
+    """moe_ffn_decode_step with the library's own per-GPU scratch as workspace
+    (no workspace argument; the C call allocates nothing).  Outputs that are
+    None are allocated here, by torch, before the call."""
+    rows = x.shape[0]
+    logits, q, scales, route_out, y = _step_outputs(layer, x, logits, q, scales, route_out, y)
+    ids, w, counts, offsets, srt = route_out
+    _call("moe_ffn_decode_step_noalloc", C.byref(layer.c), _ptr(x), _ld(x), _ptr(logits),
+          _ld(logits), rows, _ptr(q), _ld(q), _ptr(scales), _ld(scales), _ptr(ids), _ptr(w),
+          _ptr(counts), _ptr(offsets), _ptr(srt), _ptr(y), _ld(y), _stream(stream))
     return (q, scales) + tuple(route_out) + (y,)
 
 

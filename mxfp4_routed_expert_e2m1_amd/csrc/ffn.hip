@@ -22,6 +22,7 @@
 // The combine adds the per-slot fp32 partials in slot order, shared expert
 // last (gfx90a report §8.2 and Table 4: fp32 partials, fixed reduction).
 #include <algorithm>
+#include <atomic>
 
 #include "ffn_internal.h"
 
@@ -506,13 +507,13 @@ extern "C" int moe_decode_prep(const float* x, int64_t ld_x, int cols, int8_t* q
                                int rows, int n_experts, int top_k, int32_t* ids, float* w,
                                int32_t* counts, int32_t* offsets, int32_t* sorted, void* stream);
 
-extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, const float* x,
-                                          int64_t ld_x, float* logits, int64_t ld_l,
-                                          int rows, int8_t* q, int64_t ld_q, float* qs,
-                                          int64_t ld_qs, int32_t* ids, float* w, int32_t* counts,
-                                          int32_t* offsets, int32_t* sorted, float* y,
-                                          int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
-  if (stages <= 0 || stages > MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
+// Checks of a decode step from the layer input that do not involve the
+// workspace or the device (MOE_OK or the first error).
+static int step_args_check(const moe_layer_t* L, const float* x, int64_t ld_x,
+                           const float* logits, int64_t ld_l, int rows, const int8_t* q,
+                           int64_t ld_q, const float* qs, int64_t ld_qs, const int32_t* ids,
+                           const float* w, const int32_t* counts, const int32_t* offsets,
+                           const int32_t* sorted, float* y, int64_t ld_y) {
   int rc = check_layer(L);
   if (rc != MOE_OK) return rc;
   if (rows < 1 || rows > MOE_MAX_DECODE_ROWS) return MOE_ERR_SHAPE;
@@ -526,12 +527,16 @@ extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, cons
                            logits, ld_l);
     if (rc != MOE_OK) return rc;
   }
-  rc = check_acts(q, ld_q, qs, ld_qs, L->d_model, y, ld_y, L->d_model);
-  if (rc != MOE_OK) return rc;
-  if (!ws) return MOE_ERR_INVALID_ARG;
-  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  if (ws_bytes < ws_layout(L, rows).total) return MOE_ERR_WORKSPACE;
-  if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
+  return check_acts(q, ld_q, qs, ld_qs, L->d_model, y, ld_y, L->d_model);
+}
+
+// The launches of a validated decode step (ws: a workspace of at least
+// ws_layout(L, rows).total bytes).
+static int step_launch(const moe_layer_t* L, int stages, const float* x, int64_t ld_x,
+                       float* logits, int64_t ld_l, int rows, int8_t* q, int64_t ld_q, float* qs,
+                       int64_t ld_qs, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted, float* y, int64_t ld_y, void* ws, void* stream) {
+  int rc = MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   if (L->router && (stages & MOE_STAGE_GATE_UP)) {
     // the router projection writes the logits the routing below reads
@@ -559,6 +564,24 @@ extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, cons
                  s);
 }
 
+extern "C" int moe_ffn_decode_step_stages(const moe_layer_t* L, int stages, const float* x,
+                                          int64_t ld_x, float* logits, int64_t ld_l,
+                                          int rows, int8_t* q, int64_t ld_q, float* qs,
+                                          int64_t ld_qs, int32_t* ids, float* w, int32_t* counts,
+                                          int32_t* offsets, int32_t* sorted, float* y,
+                                          int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
+  if (stages <= 0 || stages > MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
+  const int rc = step_args_check(L, x, ld_x, logits, ld_l, rows, q, ld_q, qs, ld_qs, ids, w,
+                                 counts, offsets, sorted, y, ld_y);
+  if (rc != MOE_OK) return rc;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < ws_layout(L, rows).total) return MOE_ERR_WORKSPACE;
+  if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
+  return step_launch(L, stages, x, ld_x, logits, ld_l, rows, q, ld_q, qs, ld_qs, ids, w, counts,
+                     offsets, sorted, y, ld_y, ws, stream);
+}
+
 extern "C" int moe_ffn_decode_step(const moe_layer_t* L, const float* x, int64_t ld_x,
                                    float* logits, int64_t ld_l, int rows, int8_t* q,
                                    int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids, float* w,
@@ -567,6 +590,51 @@ extern "C" int moe_ffn_decode_step(const moe_layer_t* L, const float* x, int64_t
   return moe_ffn_decode_step_stages(L, MOE_STAGE_ALL, x, ld_x, logits, ld_l, rows, q, ld_q, qs,
                                     ld_qs, ids, w, counts, offsets, sorted, y, ld_y, ws, ws_bytes,
                                     stream);
+}
+
+// ------------------------------------------------- allocation-free entry
+// Scratch memory of moe_ffn_decode_step_noalloc: the workspace of one decode
+// step lives in this file-scope device array instead of a caller buffer.
+// Every GPU holds its own copy at its own address until the process ends; in
+// host code the array's name is not a device address, so the address is
+// taken once per device (with that device current) and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static std::atomic<uintptr_t> g_scratch[64];  // device ordinal -> scratch address
+
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  uintptr_t p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MOE_ERR_HIP;
+    p = (uintptr_t)ptr;
+    g_scratch[dev].store(p, std::memory_order_release);  // racing first calls store the same
+  }
+  *out = (void*)p;
+  return MOE_OK;
+}
+
+extern "C" int moe_ffn_decode_step_noalloc(const moe_layer_t* L, const float* x, int64_t ld_x,
+                                           float* logits, int64_t ld_l, int rows, int8_t* q,
+                                           int64_t ld_q, float* qs, int64_t ld_qs, int32_t* ids,
+                                           float* w, int32_t* counts, int32_t* offsets,
+                                           int32_t* sorted, float* y, int64_t ld_y,
+                                           void* stream) {
+  // the checks of moe_ffn_decode_step, the scratch size in place of the
+  // workspace's, all before anything is enqueued
+  int rc = step_args_check(L, x, ld_x, logits, ld_l, rows, q, ld_q, qs, ld_qs, ids, w, counts,
+                           offsets, sorted, y, ld_y);
+  if (rc != MOE_OK) return rc;
+  if (ws_layout(L, rows).total > kScratchBytes) return MOE_ERR_WORKSPACE;
+  if (!device_is_gfx950()) return MOE_ERR_UNSUPPORTED_ARCH;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != MOE_OK) return rc;
+  return step_launch(L, MOE_STAGE_ALL, x, ld_x, logits, ld_l, rows, q, ld_q, qs, ld_qs, ids, w,
+                     counts, offsets, sorted, y, ld_y, ws, stream);
 }
 
 extern "C" int moe_matvec_mxfp4(const void* w_packed, int n_out, int d_in, const int8_t* q,

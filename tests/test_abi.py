@@ -171,6 +171,34 @@ def test_decode_step_validation():
     assert f(C.byref(lr), *args(ldx=4098)[1:]) == ALIGN       # the router's 16-byte rows of x
 
 
+def test_decode_step_noalloc_validation():
+    # the step's own checks, then the scratch limit (8 MiB), before the device
+    f = m.lib().moe_ffn_decode_step_noalloc
+    lay = _layer()
+
+    def args(rows=1, x=A, ldx=4096, ldl=256, counts=A, y=A, ldy=4096):
+        return (C.byref(lay), x, ldx, A, ldl, rows, A, 4096, A, 128, A, A, counts, A, A, y, ldy,
+                None)
+    assert f(*args(rows=0)) == SHAPE
+    assert f(*args(rows=17)) == SHAPE
+    assert f(*args(x=None)) == INVALID
+    assert f(*args(ldx=4000)) == STRIDE
+    assert f(*args(ldl=255)) == STRIDE
+    assert f(*args(counts=None)) == INVALID
+    assert f(*args(y=None)) == INVALID
+    assert f(*args(ldy=4095)) == STRIDE
+    assert f(C.byref(_layer(top_k=0)), *args()[1:]) == SHAPE
+    # d_model 8192, d_ff 4096, top-16 + shared at 16 rows: 272 hidden rows,
+    # more workspace than the scratch array holds
+    gu = (m.moe_packed_bytes(8192, 8192) + 255) // 256 * 256
+    dn = (m.moe_packed_bytes(8192, 4096) + 255) // 256 * 256
+    big = _layer(d_model=8192, d_ff=4096, n_experts=32, top_k=16, gate_up_stride=gu,
+                 down_stride=dn)
+    assert m.lib().moe_ffn_workspace_bytes(C.byref(big), 16) > 8 << 20
+    assert f(C.byref(big), A, 8192, A, 32, 16, A, 8192, A, 256, A, A, A, A, A, A, 8192,
+             None) == WORKSPACE
+
+
 def _layer(**kw):
     d = dict(d_model=4096, d_ff=2048, n_experts=256, top_k=6, has_shared=1,
              gate_up=0x1000000, gate_up_stride=8912896, down=0x2000000, down_stride=4456448,
