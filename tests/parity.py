@@ -12,6 +12,8 @@ neighbouring integer.  `check_hidden` accepts exactly those, and
 can cause, computed from the oracle's own quantities (its w, its d_h and the
 dequantised down-projection column) -- never from GPU values.
 """
+import os
+
 import numpy as np
 
 import oracle
@@ -22,6 +24,17 @@ TOL_REL, TOL_ABS = 1e-3, 1e-6
 FLIP_EPS = 1e-3
 
 _E2M1 = None
+
+
+def host_threads():
+    """Oracle threads for the parity tests: the host cores this process may
+    use, at most 16 (a GPU machine's share).  The oracle splits work over rows and
+    assignments only, so its results do not depend on the count."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def use_host_threads():
+    oracle.set_threads(host_threads())
 
 
 def e2m1_values():
@@ -152,3 +165,35 @@ def down_col_absmax(down_codes, down_scales):
     vals = np.abs(e2m1_values()[nib])
     sc = np.power(2.0, np.asarray(down_scales, np.float64) - 127.0)
     return (vals * np.repeat(sc, 32, axis=1)).max(axis=0)
+
+
+def covering_rows(ids, n_experts, top_k, rows, tile, base, seed):
+    """A seeded sample of prefill rows for the parity check that still touches
+    every part of the grouped GEMM: `base` random rows and the last row, plus
+    rows so that every routed expert's last sorted assignment (the last row of
+    its ragged last tile) is in, every row offset (sorted position - expert
+    offset) mod `tile` of a routed tile occurs, and every token offset mod
+    `tile` of the shared expert's tiles occurs.  ids: the oracle's routes
+    (negative = not owned), grouped here by the oracle."""
+    counts, offsets, srt = oracle.group(ids, n_experts)
+    rng = np.random.default_rng(seed)
+    pick = {rows - 1}
+    pick.update(int(t) for t in rng.choice(rows, min(base, rows), replace=False))
+    n_valid = int(offsets[-1])
+    expert_of = np.repeat(np.arange(n_experts), counts)
+    r_off = (np.arange(n_valid) - offsets[expert_of]) % tile
+    tok = srt[:n_valid] // top_k
+    for e in range(n_experts):
+        if counts[e]:
+            pick.add(int(tok[offsets[e + 1] - 1]))
+    have = set(int(v) for v in r_off[np.isin(tok, sorted(pick))])
+    for v in np.unique(r_off):
+        if int(v) not in have:
+            t = int(tok[rng.choice(np.nonzero(r_off == v)[0])])
+            pick.add(t)
+            have.update(int(x) for x in r_off[tok == t])
+    shared = set(t % tile for t in pick)
+    for v in range(min(tile, rows)):
+        if v not in shared:
+            pick.add(int(rng.choice(np.arange(v, rows, tile))))
+    return np.array(sorted(pick))
