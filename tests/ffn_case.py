@@ -4,15 +4,13 @@ the layer through the C ABI, then check it against the oracle stage by stage
 codes read back from the documented workspace, with the rounding-boundary
 allowance; y within the tolerance, widened only by what legitimate hidden-code
 flips can move).  Shared by the GPU test modules."""
-from contextlib import nullcontext  # noqa: F401  (kept for callers' symmetry)
-
 import numpy as np
 import torch
 
 import oracle
 import synth
 from parity import (assert_rows_close, check_hidden, check_hidden_bf16, down_col_absmax,
-                    flip_bound, use_host_threads)
+                    flip_bound, hidden_error_bound, use_host_threads)
 
 import mxfp4_routed_expert_e2m1_amd as m
 
@@ -142,8 +140,14 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
         flips[o_rows] = check_hidden_bf16(hb[gpu_rows], hs[gpu_rows], mid["hq"][o_rows],
                                           mid["hs"][o_rows], mid["h"][o_rows], h_pre[o_rows])
     else:
+        def dh_fn(i):  # error bound of the i-th checked hidden row
+            j, sl = divmod(int(o_rows[i]), slots)
+            e = L.n_experts if sl == k else int(ids_o[rows[j], sl])
+            return hidden_error_bound(ex[e]["gate_up_codes"], ex[e]["gate_up_scales"],
+                                      q_o[rows[j]], qs_o[rows[j]])
+
         flips[o_rows] = check_hidden(hb[gpu_rows], hs[gpu_rows], mid["hq"][o_rows],
-                                     mid["hs"][o_rows], mid["h"][o_rows])
+                                     mid["hs"][o_rows], mid["h"][o_rows], dh_fn=dh_fn)
     weight = np.zeros(len(rows) * slots)
     weight[o_rows] = wts
     col_max = {}
@@ -158,4 +162,7 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
     extra_slot = flip_bound(flips, weight, mid["hs"], colmax)
     extra = extra_slot.reshape(len(rows), slots).sum(axis=1)
     worst = assert_rows_close(y.cpu().numpy()[rows], y_o, extra=extra, what=entry)
-    return dict(worst=worst, flips=int(np.count_nonzero(flips)), y=y)
+    # what the GPU layer was given, for callers that check more (q_o and qs_o
+    # equal the GPU's codes; ids and w are the routes the layer ran with)
+    return dict(worst=worst, flips=int(np.count_nonzero(flips)), y=y, ex=ex, q_o=q_o,
+                qs_o=qs_o, ids=ids.cpu().numpy(), w=w.cpu().numpy())

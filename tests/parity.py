@@ -73,18 +73,84 @@ def boundary_mask(h, hs):
     return (frac < FLIP_EPS) & (d > 0)
 
 
-def check_hidden(hq_gpu, hs_gpu, hq_o, hs_o, h_o):
-    """GPU requant codes/scales vs the oracle's.  Returns the boolean flip mask."""
+def hidden_error_bound(gu_codes, gu_scales, q_row, qs_row):
+    """Bound on |h_gpu - h_oracle| for every feature of one (token, expert).
+
+    The GPU forms each gate and up value as an fp32 sum of nb = d_model/32
+    block terms t_b = dot_b * 2^(u_b - 128) * d_b (each exact, folded in with
+    one rounding) plus a few run additions, so its error is at most
+    (nb + 8) * 2^-24 * sum_b |t_b|; the oracle's value is the exact sum
+    rounded once.  Through SwiGLU, h = silu(g) * u moves by at most
+    |silu'(g)| |u| dg + (|silu(g)| + |silu'(g)| dg) du, plus the rounding of
+    the SwiGLU arithmetic itself (the exp within 1 ulp, a division and a
+    product: 8 ulp of |h| covers them).  Well-conditioned sums keep this far
+    below FLIP_EPS; block scales spread over many binades make sum_b |t_b|
+    much larger than |g| and the bound grows with it.  sum_b |t_b| comes from
+    the oracle's exact integer block dots, g and u from its matvec."""
+    gu_codes = np.asarray(gu_codes, np.uint8)
+    F = gu_codes.shape[0] // 2
+    q_row = np.asarray(q_row, np.int8)[None, :]
+    qs_row = np.asarray(qs_row, np.float32)[None, :]
+    gu = oracle.matvec(gu_codes, gu_scales, q_row, qs_row)[0].astype(np.float64)
+    dots = oracle.block_dots(gu_codes, q_row)[0].astype(np.float64)     # [2F][nb], dot x 2
+    sc = np.exp2(np.asarray(gu_scales, np.float64) - 128.0) * qs_row.astype(np.float64)
+    a = (np.abs(dots) * sc).sum(axis=1)
+    gamma = (dots.shape[1] + 8) * 2.0 ** -24
+    g, u = gu[:F], gu[F:]
+    dg, du = gamma * a[:F], gamma * a[F:]
+    with np.errstate(over="ignore", invalid="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
+    return (dsilu * np.abs(u) * dg + (np.abs(silu) + dsilu * dg) * du
+            + 8 * 2.0 ** -24 * np.abs(silu * u) + 1e-37)
+
+
+def check_hidden(hq_gpu, hs_gpu, hq_o, hs_o, h_o, dh_fn=None):
+    """GPU requant codes/scales vs the oracle's.  Returns per-element weights:
+    how many code units each GPU code sits from the oracle's (0 where equal).
+
+    First the plain bar: group scales within 1e-5 relative, and a code off by
+    one only where the oracle's h/d lies within FLIP_EPS of a .5 boundary.
+    Rows that miss it are checked again against the bound of their arithmetic
+    (dh_fn(i) -> hidden_error_bound of row i): a group scale may then differ
+    by max(dh)/127 over its group (the amax moves by at most the largest
+    element error) plus 2 ulp, and a code may move by up to floor(e) + 1 where
+    the oracle's h/d lies within e + FLIP_EPS of a boundary, e being the
+    bound of |h_gpu/d_gpu - h_o/d_o| in code units."""
     hq_gpu = np.asarray(hq_gpu, np.int32)
     hq_o = np.asarray(hq_o, np.int32)
-    np.testing.assert_allclose(hs_gpu, hs_o, rtol=1e-5, atol=0, err_msg="hidden scales")
+    hs_gpu = np.asarray(hs_gpu, np.float32)
+    hs_o = np.asarray(hs_o, np.float32)
     diff = hq_gpu - hq_o
     flips = diff != 0
-    if flips.any():
-        near = boundary_mask(h_o, hs_o)
-        assert np.all(np.abs(diff[flips]) == 1), "hidden code off by more than 1"
-        assert np.all(near[flips]), "hidden code flipped away from a rounding boundary"
-    return flips
+    near = boundary_mask(h_o, hs_o) if flips.any() else np.zeros(diff.shape, bool)
+    s_bad = np.abs(hs_gpu.astype(np.float64) - hs_o) > 1e-5 * np.abs(hs_o.astype(np.float64))
+    c_bad = flips & (~near | (np.abs(diff) > 1))
+    bad_rows = np.nonzero(s_bad.any(axis=1) | c_bad.any(axis=1))[0]
+    assert dh_fn is not None or bad_rows.size == 0, (
+        f"hidden codes/scales of {bad_rows.size} rows outside the plain bar "
+        f"(scales {int(s_bad.sum())}, codes {int(c_bad.sum())}) and no error bound given")
+    F = hq_o.shape[1]
+    for r in bad_rows:
+        dh = np.asarray(dh_fn(r), np.float64)
+        d_o = np.repeat(hs_o[r].astype(np.float64), 32)
+        d_g = np.repeat(hs_gpu[r].astype(np.float64), 32)
+        s_tol = (dh.reshape(F // 32, 32).max(axis=1) / 127.0
+                 + 2 * np.spacing(hs_o[r]).astype(np.float64))
+        ds = np.abs(hs_gpu[r].astype(np.float64) - hs_o[r])
+        assert np.all(ds <= np.maximum(s_tol, 1e-5 * np.abs(hs_o[r]))), (
+            f"hidden scale of row {r} beyond its error bound: {ds.max():.3e} "
+            f"> {s_tol[np.argmax(ds - s_tol)]:.3e}")
+        with np.errstate(divide="ignore", invalid="ignore"):
+            x_o = np.where(d_o > 0, np.asarray(h_o[r], np.float64) / d_o, 0.0)
+            e = np.where(d_o > 0, dh / d_o + np.abs(x_o) * np.abs(d_g - d_o) / d_o, 0.0)
+        dist = np.abs(x_o - np.floor(x_o) - 0.5)
+        f = np.nonzero(diff[r])[0]
+        ok = (dist[f] <= e[f] + FLIP_EPS) & (np.abs(diff[r, f]) <= np.floor(e[f]) + 1)
+        assert np.all(ok), (f"hidden code of row {r} beyond its error bound: feature "
+                            f"{f[~ok][0]}, diff {diff[r, f[~ok][0]]}, e {e[f[~ok][0]]:.3e}")
+    return np.abs(diff).astype(np.float64)
 
 
 def bf16_tie_mask(h_pre, hs):
