@@ -224,13 +224,21 @@ typedef struct moe_layer {
 /* Workspace of one FFN call with `rows` tokens (same for decode/prefill).
  * With A' = rows*top_k + (has_shared ? rows : 0) hidden rows, it holds, in
  * order, each region 256-byte aligned:
- *   hidden codes  bf16 [A'][d_ff]     requantised intermediate, the int8
- *                                      codes stored as exact bf16 values
+ *   hidden codes  [A'][2*d_ff bytes]  requantised intermediate.  Decode calls,
+ *                                      and prefill calls off the grouped GEMM
+ *                                      (d_model or 2*d_ff not a multiple of
+ *                                      256), store each int8 code as the exact
+ *                                      bf16 value.  Prefill calls on the GEMM
+ *                                      store each run of 32 codes as four E2M1
+ *                                      digit planes of 16 bytes, plane 0
+ *                                      first: code = d0 + 4 d1 + 16 d2 + 64 d3
+ *                                      with every d in {-2..2}, plane s holding
+ *                                      d_s of the 32 codes (element 2i in the
+ *                                      low nibble of byte i).
  *   hidden scales f32  [A'][d_ff/32]
  *   partials      f32  [A'][d_model]  per-slot down projections
- *   activations   bf16 [A'][d_model]  prefill: activation codes gathered per
- *                                      hidden row, stored as exact bf16 values
- *   act scales    f32  [A'][d_model/32]
+ *   activations   [rows][2*d_model bytes]  prefill GEMM: each token's int8
+ *                                      codes as digit planes, as above
  * Hidden row of routed assignment at sorted position p is p; the shared
  * expert's row for token t is rows*top_k + t.  Partials row of routed
  * assignment a is a; shared: rows*top_k + t.  The byte offsets are returned
@@ -322,11 +330,17 @@ int moe_ffn_prefill(const moe_layer_t* L, const int8_t* q, int64_t ld_q,
  * may be re-run on its own, e.g. to time it, once the workspace has seen a
  * GATE_UP stage of the same rows.  `prefill` = 0 selects the decode limits and
  * kernels (rows <= MOE_MAX_DECODE_ROWS), 1 the prefill ones.  Other arguments
- * and errors as moe_ffn_decode; stage_mask must be non-zero and within
- * MOE_STAGE_ALL. */
+ * and errors as moe_ffn_decode; stage_mask must hold GATE_UP or DOWN and no
+ * bits beyond MOE_STAGE_ALL | MOE_STAGE_REUSE_ACTS. */
 #define MOE_STAGE_GATE_UP 1
 #define MOE_STAGE_DOWN 2
 #define MOE_STAGE_ALL 3
+/* With prefill = 1 and MOE_STAGE_GATE_UP: skip the preparation of the
+ * activations (the digit planes of q in the workspace) and reuse what an
+ * earlier gate/up stage of the same q left there, so the gate/up GEMM can be
+ * timed alone.  Rejected (MOE_ERR_INVALID_ARG) with prefill = 0 or without
+ * MOE_STAGE_GATE_UP; no effect off the grouped GEMM. */
+#define MOE_STAGE_REUSE_ACTS 4
 int moe_ffn_stages(const moe_layer_t* L, int prefill, int stage_mask, const int8_t* q,
                    int64_t ld_q, const float* qs, int64_t ld_qs, int rows,
                    const int32_t* ids, const float* w, const int32_t* offsets,

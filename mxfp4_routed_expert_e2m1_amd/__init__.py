@@ -29,7 +29,7 @@ EXPORTS = [
     "moe_debug_block_dots", "moe_status_string",
 ]
 
-MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_ALL = 1, 2, 3
+MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_ALL, MOE_STAGE_REUSE_ACTS = 1, 2, 3, 4
 
 
 class MoeError(RuntimeError):

@@ -4,11 +4,14 @@
 // A matrix W[N][K] (N % 16 == 0, K % 128 == 0) is cut into 16-row groups
 // ("row groups", RG = N/16) and 128-element K chunks (KC = K/128 = four
 // 32-element blocks).  The unit of one wave load is a (row group, K chunk)
-// tile of 1 KiB nibbles: lane l (l = 16*g + r) holds 16 bytes = for each of
-// the chunk's 4 blocks j, the 4 code bytes of row r, elements 8g..8g+7 of
-// block j.  That is exactly the A-operand fragment of one 16x16x32 matrix
-// core instruction per block, so every wave load is one contiguous 1 KiB
-// burst and every nibble lands in the lane that consumes it.
+// tile of 1 KiB nibbles: lane l = 16*j + r holds the 16 canonical bytes of
+// row r's block j (32 E2M1 codes, element 2i in the low nibble of byte i).
+// That is exactly the operand layout of the scaled FP4 matrix-core
+// instruction (16x16x128: lane l supplies row l%16 and the 32 elements of
+// K-slot l/16), so the prefill GEMM feeds LDS copies of the tiles to it
+// directly; the bf16 16x16x32 instruction of the decode kernels wants lane
+// 16*g + r to hold elements 8g..8g+7 of every block instead, which four
+// lane-group swaps per loaded tile produce (tile_to_bf16_frags).
 //   nibbles: [RG][KC slots][64 lanes][16 B]
 // Within a row group the chunks are stored interleaved by 4 when KC % 4 ==
 // 0: chunk c sits in slot (c % 4) * (KC/4) + c / 4.  The decode streams give
@@ -37,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int v8i32 __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsPerGroup = 16;
 constexpr int kChunkK = 128;     // elements per K chunk (4 blocks)
@@ -80,6 +84,19 @@ __host__ __device__ inline int packed_group_src_row(int pr, int n_out, int inter
 // (32 x 127 x 12, in units of half an E2M1 step) that holds for u <= 240.
 __device__ inline float e8m0_to_f32(uint32_t u) { return __uint_as_float(u << 23); }
 
+// A packed tile as loaded (lane 16*j + r: dword g = bytes 4g..4g+3 of row
+// r's block j) -> the bf16 instruction's fragments (lane 16*g + r: dword j =
+// those same bytes), a 4 x 4 transpose of dwords across the four 16-lane
+// groups: one 32-lane swap between registers (0, 2) and (1, 3), then one
+// 16-lane swap between (0, 1) and (2, 3).  Every lane must be active.
+__device__ inline u32x4 tile_to_bf16_frags(u32x4 t) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(t[0], t[2], false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(t[1], t[3], false, false);
+  const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  return u32x4{s01[0], s01[1], s23[0], s23[1]};
+}
+
 // One A fragment: the 8 E2M1 codes of a dword (element 2i in the low nibble of
 // byte i/2) -> 8 bf16 values value*scale, via the gfx950 FP4 converter.
 // Exact: E2M1 values have 2 significant bits and scale is a power of two.
@@ -114,6 +131,27 @@ __device__ inline bf16x8 i8x8_to_bf16x8(u32x2 v) {
 __device__ inline f32x4 mfma_block(bf16x8 a, bf16x8 b) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero, 0, 0, 0);
+}
+
+// D[16][16] = A[16][128] * B[128][16] on the scaled FP4 matrix core, zero C:
+// A and B are E2M1 codes (lane l supplies row / column l%16 and the 32
+// elements of K slot l/16 in the low 4 dwords, element 2i in the low nibble
+// of byte i), each (row or column, K slot) scaled by 2^(byte - 127) of its
+// lane's scale register -- byte J of sa, byte 0 of sb.  D as for mfma_block.
+template <int J>
+__device__ inline f32x4 mfma_fp4_blk(v8i32 a, v8i32 b, int sa, int sb) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, J, sa, 0, sb);
+}
+// j: a compile-time constant after unrolling (the byte select is part of the
+// instruction)
+__device__ __forceinline__ f32x4 mfma_fp4_block(v8i32 a, v8i32 b, int j, int sa, int sb) {
+  switch (j) {
+    case 0: return mfma_fp4_blk<0>(a, b, sa, sb);
+    case 1: return mfma_fp4_blk<1>(a, b, sa, sb);
+    case 2: return mfma_fp4_blk<2>(a, b, sa, sb);
+    default: return mfma_fp4_blk<3>(a, b, sa, sb);
+  }
 }
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }

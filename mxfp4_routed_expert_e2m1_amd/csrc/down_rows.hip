@@ -214,10 +214,11 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
             run = f32x4{0.f, 0.f, 0.f, 0.f};
           }
           if (kk + 1 < n_in) load_h(kg + kk + 1, b[(kk + 1) & 1], d[(kk + 1) & 1]);
+          const u32x4 af = tile_to_bf16_frags(a[kk]);  // (kk < n_in is wave-uniform)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float sc = e8m0_to_f32((s[kk] >> (8 * j)) & 0xFFu);
-            const f32x4 r = mfma_block(fp4x8_to_bf16x8(a[kk][j], sc),
+            const f32x4 r = mfma_block(fp4x8_to_bf16x8(af[j], sc),
                                        __builtin_bit_cast(bf16x8, b[kk & 1][j]));
 #pragma unroll
             for (int i = 0; i < 4; ++i) run[i] = fmaf(r[i], d[kk & 1][j], run[i]);

@@ -58,7 +58,10 @@ __device__ inline void wave_project(const ProjArgs& p, const uint8_t* blob, int 
     }
     d = *(const f32x4*)(p.bs + (int64_t)brow * p.ld_bs + (int64_t)kc * 4);
   };
-  auto compute = [&](const u32x4* a, const uint32_t* s, const u32x4* b, f32x4 d) {
+  auto compute = [&](const u32x4* a_tile, const uint32_t* s, const u32x4* b, f32x4 d) {
+    u32x4 a[RGW];
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) a[g] = tile_to_bf16_frags(a_tile[g]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 bb;
@@ -275,7 +278,8 @@ __global__ __launch_bounds__(64) void block_dots_kernel(const uint8_t* __restric
   const int lane = threadIdx.x;
   const int col = lane & 15;
   const int brow = col < rows ? col : 0;
-  const u32x4 a = ((const u32x4*)blob)[((int64_t)pr * pd.kc + chunk_slot(kc, (int)pd.kc)) * 64 + lane];
+  const u32x4 a = tile_to_bf16_frags(
+      ((const u32x4*)blob)[((int64_t)pr * pd.kc + chunk_slot(kc, (int)pd.kc)) * 64 + lane]);
   const int nb = d_in / kBlock;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -454,7 +458,10 @@ static int ffn_entry(const moe_layer_t* L, bool decode, int stages, const int8_t
                      const float* w, const int32_t* offsets, const int32_t* sorted, float* y,
                      int64_t ld_y, void* ws, size_t ws_bytes, void* stream) {
   const int max_rows = decode ? MOE_MAX_DECODE_ROWS : kMaxPrefillRows;
-  if (stages <= 0 || stages > MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
+  if ((stages & MOE_STAGE_ALL) == 0 || (stages & ~(MOE_STAGE_ALL | MOE_STAGE_REUSE_ACTS)))
+    return MOE_ERR_INVALID_ARG;
+  if ((stages & MOE_STAGE_REUSE_ACTS) && (decode || !(stages & MOE_STAGE_GATE_UP)))
+    return MOE_ERR_INVALID_ARG;
   int rc = check_layer(L);
   if (rc != MOE_OK) return rc;
   if (rows < 1 || rows > max_rows) return MOE_ERR_SHAPE;

@@ -8,14 +8,16 @@ namespace moe {
 
 // Workspace regions (each 256-byte aligned), for A' = rows*top_k (+ rows when
 // a shared expert is present) hidden rows:
-//   hidden        bf16 [A'][d_ff]      requantised intermediate codes
+//   hidden        [A'][2 d_ff bytes]   requantised intermediate codes: exact
+//                                      bf16 values (decode; prefill off the
+//                                      GEMM path), or E2M1 digit planes
+//                                      [d_ff/32][4][16 B] (prefill GEMM path)
 //   hidden_scales f32  [A'][d_ff/32]
 //   partials      f32  [A'][d_model]   per-slot down projections
-//   act           bf16 [A'][d_model]   prefill: activation codes gathered per
-//                                      hidden row (tile order), exact in bf16
-//   act_scales    f32  [A'][d_model/32]
+//   act           [rows][2 d_model bytes]  prefill GEMM path: each token's
+//                                      activation codes as digit planes
 struct WsLayout {
-  size_t hidden, hidden_scales, partials, act, act_scales, total;
+  size_t hidden, hidden_scales, partials, act, total;
 };
 
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -28,8 +30,7 @@ inline WsLayout ws_layout(const moe_layer_t* L, int rows) {
   w.hidden_scales = w.hidden + round256(hrows * L->d_ff * 2);
   w.partials = w.hidden_scales + round256(hrows * (L->d_ff / kBlock) * 4);
   w.act = w.partials + round256(hrows * L->d_model * 4);
-  w.act_scales = w.act + round256(hrows * L->d_model * 2);
-  w.total = w.act_scales + round256(hrows * (L->d_model / kBlock) * 4);
+  w.total = w.act + round256((size_t)rows * L->d_model * 2);
   return w;
 }
 

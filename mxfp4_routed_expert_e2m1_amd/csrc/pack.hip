@@ -9,20 +9,21 @@
 
 namespace moe {
 
-// One thread per packed nibble dword: (pr, slot, lane, j) -> 4 canonical bytes.
+// One thread per packed nibble dword: (pr, slot, lane = 16 j + r, g) -> bytes
+// 4g..4g+3 of row r's block j of the chunk.
 __global__ void pack_nibbles_kernel(const uint8_t* __restrict__ codes, int64_t ld_codes,
                                     int n_out, int d_in, int interleave, int64_t n_words,
                                     uint32_t* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_words) return;
   const int64_t kcn = d_in / kChunkK;
-  const int j = (int)(i & 3);
+  const int g = (int)(i & 3);
   const int lane = (int)((i >> 2) & 63);
   const int64_t tile = i >> 8;  // pr * KC + storage slot
   const int kc = slot_chunk((int)(tile % kcn), (int)kcn);
   const int pr = (int)(tile / kcn);
   const int row = packed_group_src_row(pr, n_out, interleave) + (lane & 15);
-  const int64_t byte = ((int64_t)kc * kChunkK + j * kBlock + 8 * (lane >> 4)) / 2;
+  const int64_t byte = ((int64_t)kc * kChunkK + (lane >> 4) * kBlock) / 2 + 4 * g;
   dst[i] = *(const uint32_t*)(codes + (int64_t)row * ld_codes + byte);
 }
 
@@ -32,13 +33,13 @@ __global__ void unpack_nibbles_kernel(const uint32_t* __restrict__ src, int n_ou
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_words) return;
   const int64_t kcn = d_in / kChunkK;
-  const int j = (int)(i & 3);
+  const int g = (int)(i & 3);
   const int lane = (int)((i >> 2) & 63);
   const int64_t tile = i >> 8;
   const int kc = slot_chunk((int)(tile % kcn), (int)kcn);
   const int pr = (int)(tile / kcn);
   const int row = packed_group_src_row(pr, n_out, interleave) + (lane & 15);
-  const int64_t byte = ((int64_t)kc * kChunkK + j * kBlock + 8 * (lane >> 4)) / 2;
+  const int64_t byte = ((int64_t)kc * kChunkK + (lane >> 4) * kBlock) / 2 + 4 * g;
   *(uint32_t*)(codes + (int64_t)row * ld_codes + byte) = src[i];
 }
 

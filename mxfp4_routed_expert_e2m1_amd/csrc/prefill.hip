@@ -1,30 +1,45 @@
-// prefill.hip -- grouped matrix-core GEMM for prefill chunks.
+// prefill.hip -- grouped GEMM for prefill chunks on gfx950's scaled FP4
+// matrix core.
 //
 // The gfx90a report (§7.1) moves prefill from a per-assignment dot path to
 // INT8 MFMA routed gate and down kernels with FP4 unpack reused across rows,
 // and (§7.1 item 8) sorts assignments into per-expert row blocks so an expert
 // with ~48 rows scans its packed weights once.  Here a workgroup owns one
 // tile of up to 128 token rows of one expert (rows grouped by
-// moe_route_group) and 256 weight rows, so each expert's weights are streamed
-// once per 128 tokens.  The contraction runs on the bf16 matrix core with the
-// same exact per-block scheme as decode (E2M1 x E8M0 folded into bf16 by the
-// FP4 converter, int8 codes exact in bf16, one 16x16x32 op per 32-element
-// block, fp32 FMA with the activation scale).
+// moe_route_group) and 256 weight rows, so each expert's weights stream once
+// per 128 tokens.  The contraction is exact on the matrix core without any
+// unpacking of the weights:
 //
-//   * A prep kernel gathers every hidden row's activation codes once into
-//     bf16 rows in tile order (so a tile's token rows are contiguous).
-//   * A workgroup owns 128 token rows x 256 weight rows; 16 waves = 4 row
-//     quarters x 4 token parts (token groups interleaved for balance); wave
-//     tile = 4 row groups x up to 2 token groups, the live count being a
-//     template parameter so the inner loop is branch-free.  32-row tiles
-//     take 8 waves (4 row quarters x 2 token parts, one token group each).
-//   * Weights, scales, token fragments and activation scales stream through
-//     a 3-stage LDS ring filled by direct global->LDS loads (no registers),
-//     each piece in the lane order its reader uses.
+//   * gfx950's scaled 16x16x128 FP4 instruction takes the packed E2M1 codes
+//     as they are and applies one E8M0 byte per row and 32-element K slot
+//     (picked from a register by the instruction's byte select), so the
+//     weights go from LDS to the matrix core untouched.
+//   * An int8 activation block has no exact FP4 form, but its code q in
+//     [-127, 127] splits into balanced base-4 digits, q = d0 + 4 d1 + 16 d2 +
+//     64 d3 with every d in {-2..2}, each an exact E2M1 value.  The four
+//     digit planes of one 32-element block fill the instruction's four K
+//     slots, with B scales 2^0, 2^2, 2^4, 2^6, against the same weight block
+//     in every slot: one instruction gives the exact integer block dot times
+//     2^(u-127) (every product and partial sum is a multiple of half an E2M1
+//     step below 2^15 of them, exact in fp32) -- the same fp32 value as the
+//     decode kernels' bf16 route.  The activation scale follows with one fp32
+//     FMA per output and block.
+//   * The sums run as in every decode kernel: runs of 16 blocks (4 chunks),
+//     each folded from zero in block order, added in order -- so a prefill
+//     row has the bits of the same row decoded alone (exact rows).
+//
+// Data movement:
+//   * A prep kernel turns each token's int8 codes into digit planes once
+//     (2 bytes per code); the gate/up GEMM reads the planes of its tile's
+//     tokens through the sorted assignment list.  Its epilogue (SwiGLU +
+//     group-32 requant) writes the hidden codes as digit planes too, in tile
+//     order, which the down GEMM reads directly.
+//   * Weights, scales, digit planes and activation scales stream through a
+//     3-stage LDS ring filled by direct global->LDS loads (no registers).
+//   * 8 waves: 4 row quarters (4 row groups each) x 2 token parts (token
+//     groups tp, tp+2, tp+4, tp+6), a 64 x 64 output block per wave.
 //   * Block ids are remapped so the workgroups that share a token tile run on
 //     the same XCD and share its L2.
-//   * Gate/up epilogue: SwiGLU + group-32 requant in registers (a wave holds
-//     gate and up of the same 32 features); down epilogue: fp32 partials.
 #include "ffn_internal.h"
 
 namespace moe {
@@ -32,21 +47,13 @@ namespace moe {
 // Token rows per tile: 128 (8 groups of 16), or 32 when experts hold few rows
 // each: a short tile's stage takes half the LDS, so two workgroups share a
 // CU and one streams while the other starts (finds its tile, waits for its
-// first chunk).  Measured on MI355X, 512-token step: 0.783 vs 0.920 ms.
+// first chunk).
 constexpr int kBMFull = 128;
 constexpr int kBMShort = 32;
-constexpr int kBNGroups = 16;     // 16-row weight groups per workgroup (256 rows)
-// Waves per workgroup: 4 row quarters x TH token parts.  128-row tiles take
-// 16 waves (each 2 of the 8 token groups; 4 waves per SIMD hide the MFMA and
-// load latencies), 32-row tiles 8 (each 1 of 2).  Waves 0-7 issue the ring's
-// loads.
-template <int BM> constexpr int gemm_waves() { return BM == kBMFull ? 16 : 8; }
-template <int BM> constexpr int gemm_th() { return gemm_waves<BM>() / 4; }
-// LDS ring depth (prefetch distance: stages - 1 chunks); 3 x 25.5 KB lets
-// two short-tile workgroups share a CU (a 5-deep ring for one workgroup
-// measured 0.921 ms)
-template <int BM> constexpr int ring_stages() { return 3; }
-constexpr int kLoadsPerChunk = 8; // direct-to-LDS loads per wave per K chunk
+constexpr int kBNGroups = 16;  // 16-row weight groups per workgroup (256 rows)
+constexpr int kGemmWaves = 8;  // 4 row quarters x 2 token parts
+constexpr int kRing = 3;       // LDS stages (chunks in flight ahead: kRing - 1)
+constexpr int kRunChunks = 4;  // chunks per exact-rows run (16 blocks)
 
 enum GemmPass : int { GEMM_GATEUP = 0, GEMM_DOWN = 1 };
 
@@ -59,179 +66,250 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* sorted;
   int n_experts, top_k, has_shared, rows;
-  const uint16_t* xb;  // B rows (bf16 codes), tile order
-  int64_t ld_xb;
-  const float* xs;
+  const uint8_t* xp;  // B digit planes: tokens (gate/up) or hidden rows (down)
+  int64_t ld_xp;      // bytes per row of planes (2 * K)
+  const float* xs;    // B scales: qs (gate/up) or hidden scales (down)
   int64_t ld_xs;
   int n_items;  // tiles bound x weight-row blocks
-  uint16_t* h;  // gate/up outputs
+  uint8_t* h;   // gate/up: hidden digit planes
   float* hs;
-  int64_t ld_h, ld_hs;
-  float* y;  // down partials
+  int64_t ld_h, ld_hs;  // bytes per hidden row, floats per hidden-scale row
+  float* y;             // down partials
   int64_t ld_y;
   int bf16_mid;  // gate/up: round the intermediate to bf16 before its requant
 };
 
 // One LDS stage = one 128-element K chunk of the workgroup's operands, each
-// piece in the lane order its consumer reads (conflict-free ds_read_b128):
+// piece in the order its reader uses:
 template <int BM>
 struct Stage {
-  u32x4 a[kBNGroups][64];        // weight fragments, [row group][lane]      16 KiB
-  uint32_t s[kBNGroups][16];     // E8M0 bytes of the chunk's 4 blocks, per row 1 KiB
-  u32x4 b[BM / 16][4][64];       // token fragments, [token group][block][lane] BM/4 KiB
-  float d[BM / 16][4][16];       // activation scales, [token group][block][token]
+  static constexpr int NTG = BM / 16;              // token groups
+  static constexpr int NTD = NTG < 4 ? 4 : NTG;    // scale rows, whole loads of 4 groups
+  u32x4 a[kBNGroups][64];  // packed tiles, lane 16 j + r: row r's block j   16 KiB
+  uint32_t s[kBNGroups][16];  // E8M0 bytes of the chunk's 4 blocks, per row  1 KiB
+  u32x4 b[NTG][4][64];     // digit planes, [token group][block][16 s + col]  BM/4 KiB
+  f32x4 d[NTD][16];        // activation scales of the chunk's 4 blocks, per column
 };
 
 // vmcnt <= n (n < 64), no wait on the other counters (gfx9 encoding: vmcnt
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | ((n) & 15) | (((n) >> 4) << 14))
+__device__ inline void wait_vmcnt(int n) {  // n wave-uniform, 0..15
+  switch (n) {
+    case 0: WAIT_VMCNT(0); break;
+    case 1: WAIT_VMCNT(1); break;
+    case 2: WAIT_VMCNT(2); break;
+    case 3: WAIT_VMCNT(3); break;
+    case 4: WAIT_VMCNT(4); break;
+    case 5: WAIT_VMCNT(5); break;
+    case 6: WAIT_VMCNT(6); break;
+    case 7: WAIT_VMCNT(7); break;
+    case 8: WAIT_VMCNT(8); break;
+    case 9: WAIT_VMCNT(9); break;
+    case 10: WAIT_VMCNT(10); break;
+    case 11: WAIT_VMCNT(11); break;
+    case 12: WAIT_VMCNT(12); break;
+    case 13: WAIT_VMCNT(13); break;
+    case 14: WAIT_VMCNT(14); break;
+    default: WAIT_VMCNT(15); break;
+  }
+}
 
 // Workgroup barrier for the LDS ring.  __syncthreads() (and any LDS fence)
 // would wait for every outstanding direct-to-LDS load (vmcnt(0)) and collapse
 // the prefetch to one chunk.  Instead each wave first waits for its own loads
-// of the chunk about to be consumed (WAIT_VMCNT; loads complete in issue
-// order), then all waves meet at s_barrier; every LDS read of the previous
-// chunk has returned (its data was consumed) before a wave reaches it.  The
-// empty asm statements keep the compiler from moving memory accesses across.
+// of the chunk about to be consumed (loads complete in issue order), then
+// all waves meet at s_barrier; every LDS read of the previous chunk has
+// returned (its data was consumed) before a wave reaches it.  The empty asm
+// statements keep the compiler from moving memory accesses across.
 __device__ inline void ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// One thread per 8 activations of a hidden row: q[token] -> bf16 row p.
-__global__ __launch_bounds__(256) void gather_act_kernel(
-    const int8_t* __restrict__ q, int64_t ld_q, const float* __restrict__ qs, int64_t ld_qs,
-    const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets, int n_experts,
-    int rows, int top_k, int has_shared, int d_model, uint16_t* __restrict__ xb, int64_t ld_xb,
-    float* __restrict__ xs, int64_t ld_xs) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int per_row = d_model / 8;
-  const int A = rows * top_k;
-  const int64_t n_rows = (int64_t)A + (has_shared ? rows : 0);
-  if (i >= n_rows * per_row) return;
-  const int p = (int)(i / per_row);
-  const int c = (int)(i % per_row);
-  int token;
-  if (p < A) {
-    if (p >= offsets[n_experts]) return;  // sentinel-only tail: no hidden row
-    token = sorted[p] / top_k;
-  } else {
-    token = p - A;
+// ------------------------------------------------------------ digit planes
+// E2M1 code of a digit in {-2..2}: sign bit 3, |d| = 1 -> 0b010, 2 -> 0b100.
+__device__ inline uint32_t digit_code(int d) {
+  return (d < 0 ? 8u : 0u) | ((uint32_t)(d < 0 ? -d : d) << 1);
+}
+// The four balanced base-4 digits of q in [-127, 127] as E2M1 codes:
+// d_s = ((x + 2) mod 4) - 2, x <- (x - d_s) / 4, the last digit what is left.
+__device__ inline void q8_digit_codes(int q, uint32_t (&c)[4]) {
+  int x = q;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int dg = ((x + 2) & 3) - 2;
+    c[s] = digit_code(dg);
+    x = (x - dg) >> 2;
   }
-  const u32x2 v = *(const u32x2*)(q + (int64_t)token * ld_q + (int64_t)c * 8);
-  *(bf16x8*)(xb + (int64_t)p * ld_xb + (int64_t)c * 8) = i8x8_to_bf16x8(v);
-  if ((c & 3) == 0) xs[(int64_t)p * ld_xs + c / 4] = qs[(int64_t)token * ld_qs + c / 4];
+  c[3] = digit_code(x);
 }
 
+// One thread per 8 codes of a token row: plane s of block b holds the 32
+// digit-s codes of the block (16 bytes, element 2i in the low nibble of byte
+// i); a row is [K/32 blocks][4 planes][16 B].  Threads 4b..4b+3 of a row
+// write the 64 bytes of block b.
+__global__ __launch_bounds__(256) void prep_digits_kernel(const int8_t* __restrict__ q,
+                                                          int64_t ld_q, int rows, int d_model,
+                                                          uint8_t* __restrict__ xp,
+                                                          int64_t ld_xp) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = d_model / 8;
+  if (i >= (int64_t)rows * per_row) return;
+  const int t = (int)(i / per_row);
+  const int c8 = (int)(i % per_row);  // 8-element group: block c8 / 4, quarter c8 % 4
+  const u32x2 v = *(const u32x2*)(q + (int64_t)t * ld_q + (int64_t)c8 * 8);
+  uint32_t plane[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int code = (int)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+    uint32_t c[4];
+    q8_digit_codes(code, c);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) plane[s] |= c[s] << (4 * e);
+  }
+  uint8_t* dst = xp + (int64_t)t * ld_xp + (int64_t)(c8 >> 2) * 64 + (c8 & 3) * 4;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) *(uint32_t*)(dst + 16 * s) = plane[s];
+}
+
+// ------------------------------------------------------------------- GEMM
 // Everything a workgroup knows about its item once the tile is found.
 struct GemmCtx {
   const u32x4* nib;
   const uint8_t* scl;
   int prb;       // first packed row group of the workgroup
-  int64_t row0;  // first B row (hidden row) of the tile
+  int64_t row0;  // first hidden row of the tile (A + start for the shared expert)
   Tile t;
   bool shared;
   int A;
+  int b_row;  // B / scale row of this lane's B loads (token or hidden row)
+  int d_row;  // B / scale row of this lane's scale loads
 };
 
-// Issue wave `wave`'s share of K chunk kc into `S`: 2 weight tiles, 1 scale
-// load, and -- when its token group is live -- 4 token fragments + 1 scale load.
+// B row of tile row r (clamped into the tile): the token for gate/up (through
+// the sorted list for routed experts), the hidden row for down.
+template <int PASS>
+__device__ inline int gemm_brow(const GemmArgs& p, const GemmCtx& c, int r) {
+  r = min(r, c.t.count - 1);
+  if (PASS == GEMM_DOWN) return (int)c.row0 + r;
+  return c.shared ? c.t.start + r : p.sorted[c.t.start + r] / p.top_k;
+}
+
+// Loads this wave issues per chunk.  Every wave: 2 weight tiles; waves 0-3:
+// one E8M0 load (4 row groups), waves 4..4+NTD/4-1: one scale load (4 token
+// groups); B: 128-row tiles: token group `wave`, all 4 blocks, when live;
+// 32-row tiles: token group wave/4, block wave%4, when live.
 template <int BM>
+__device__ inline int gemm_loads_per_chunk(int wave, bool b_live) {
+  constexpr int NTD = Stage<BM>::NTD;
+  int n = 2 + (wave < 4 ? 1 : 0) + (wave >= 4 && wave < 4 + NTD / 4 ? 1 : 0);
+  if (b_live) n += BM == kBMFull ? 4 : 1;
+  return n;
+}
+
+template <int PASS, int BM>
 __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>& S, int kc,
                                   int wave, int lane, bool b_live) {
-  const int n = lane & 15, g4 = lane >> 4, rq = wave & 3;
-  if (wave >= 8) return;  // waves 8-15 (16-wave workgroups) issue nothing
+  const int n = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rg = 2 * wave + i;
     load_to_lds(c.nib + ((int64_t)(c.prb + rg) * p.kc_total + chunk_slot(kc, p.kc_total)) * 64 + lane,
                 &S.a[rg][0], 16);
   }
-  {
-    const int rg = 4 * rq + g4;
+  if (wave < 4) {  // E8M0 bytes of row groups 4 wave .. 4 wave + 3
+    const int rg = 4 * wave + g4;
     load_to_lds(c.scl + (((int64_t)(c.prb + rg) * p.sc_total + (kc >> 2)) * 16 + n) * 16 + (kc & 3) * 4,
-                &S.s[4 * rq][0], 4);
+                &S.s[4 * wave][0], 4);
+  } else if (wave < 4 + Stage<BM>::NTD / 4) {  // scales of token groups 4 q .. 4 q + 3
+    const int qd = wave - 4;
+    load_to_lds(p.xs + (int64_t)c.d_row * p.ld_xs + (int64_t)kc * 4, &S.d[4 * qd][0], 16);
   }
   if (b_live) {
-    const int r = min(wave * 16 + n, c.t.count - 1);
-    const uint16_t* src = p.xb + (c.row0 + r) * p.ld_xb + (int64_t)kc * kChunkK + 8 * g4;
+    const uint8_t* src = p.xp + (int64_t)c.b_row * p.ld_xp + (int64_t)kc * 256 + 16 * g4;
+    if constexpr (BM == kBMFull) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_to_lds(src + j * kBlock, &S.b[wave][j][0], 16);
-    load_to_lds(p.xs + (c.row0 + r) * p.ld_xs + (int64_t)kc * 4 + g4, &S.d[wave][0][0], 4);
+      for (int j = 0; j < 4; ++j) load_to_lds(src + 64 * j, &S.b[wave][j][0], 16);
+    } else {
+      load_to_lds(src + 64 * (wave & 3), &S.b[wave >> 2][wave & 3][0], 16);
+    }
   }
 }
 
 // K loop + epilogue of one wave owning row groups prb+4*rq .. +3 and token
-// groups th, th+TH, .. (NQ of them live).  Branch-free inner loop.
+// groups tp, tp+2, .. (NQ of them live).  Branch-free inner loop.
 template <int PASS, int NQ, int BM>
 __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring) {
-  constexpr int NST = ring_stages<BM>();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g4 = lane >> 4;
-  constexpr int TH = gemm_th<BM>();
-  const int rq = wave & 3, th = wave >> 2;
+  const int rq = wave & 3, tp = wave >> 2;
   const int nnt = (c.t.count + 15) >> 4;
-  const bool b_live = wave < nnt;  // this wave stages token group `wave` (< 8)
+  // token group this wave stages
+  const bool b_live = (BM == kBMFull ? wave : (wave >> 2)) < nnt;
+  const int per_chunk = gemm_loads_per_chunk<BM>(wave, b_live);
+  // B scale of K slot g4 (digit plane g4 carries weight 4^g4)
+  const int sb = 127 + 2 * g4;
 
-  f32x4 acc[4][NQ > 0 ? NQ : 1];
+  f32x4 acc[4][NQ > 0 ? NQ : 1], run[4][NQ > 0 ? NQ : 1];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int q4 = 0; q4 < NQ; ++q4) acc[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q4 = 0; q4 < NQ; ++q4) {
+      acc[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      run[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   const int KC = p.kc_total;
-  // chunks 0 .. NST-2 go out first; chunk kc + NST - 1 after chunk kc lands
+  // chunks 0 .. kRing-2 go out first; chunk kc + kRing - 1 after chunk kc lands
 #pragma unroll
-  for (int k0 = 0; k0 < NST - 1; ++k0)
-    if (k0 < KC) gemm_issue(p, c, ring[k0], k0, wave, lane, b_live);
+  for (int k0 = 0; k0 < kRing - 1; ++k0)
+    if (k0 < KC) gemm_issue<PASS, BM>(p, c, ring[k0], k0, wave, lane, b_live);
   for (int kc = 0; kc < KC; ++kc) {
     // chunk kc has landed when no more than the loads of the chunks issued
     // after it are outstanding (loads complete in issue order)
-    static_assert(NST - 2 <= 3 && 3 * kLoadsPerChunk < 64, "vmcnt range");
-    switch (min(NST - 2, KC - 1 - kc)) {
-      case 0: WAIT_VMCNT(0); break;
-      case 1: if (b_live) WAIT_VMCNT(kLoadsPerChunk); else WAIT_VMCNT(3); break;
-      case 2: if (b_live) WAIT_VMCNT(2 * kLoadsPerChunk); else WAIT_VMCNT(6); break;
-      default: if (b_live) WAIT_VMCNT(3 * kLoadsPerChunk); else WAIT_VMCNT(9); break;
-    }
+    wait_vmcnt(min(kRing - 2, KC - 1 - kc) * per_chunk);
     ring_barrier();  // every wave's loads of chunk kc have landed; chunk kc-1 is consumed
-    if (kc + NST - 1 < KC)
-      gemm_issue(p, c, ring[(kc + NST - 1) % NST], kc + NST - 1, wave, lane, b_live);
+    if (kc + kRing - 1 < KC)
+      gemm_issue<PASS, BM>(p, c, ring[(kc + kRing - 1) % kRing], kc + kRing - 1, wave, lane, b_live);
     if constexpr (NQ > 0) {
-      const Stage<BM>& S = ring[kc % NST];
-      float dxv[NQ][4];
+      const Stage<BM>& S = ring[kc % kRing];
+      f32x4 dx[NQ];
 #pragma unroll
-      for (int q4 = 0; q4 < NQ; ++q4)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dxv[q4][j] = S.d[th + TH * q4][j][n];
+      for (int q4 = 0; q4 < NQ; ++q4) dx[q4] = S.d[tp + 2 * q4][n];
       uint32_t sw[4];
-      u32x4 aw[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        sw[g] = S.s[4 * rq + g][n];
-        aw[g] = S.a[4 * rq + g][lane];
-      }
+      for (int g = 0; g < 4; ++g) sw[g] = S.s[4 * rq + g][n];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x8 bfr[NQ];
+        u32x4 bq[NQ];
 #pragma unroll
-        for (int q4 = 0; q4 < NQ; ++q4)
-          bfr[q4] = __builtin_bit_cast(bf16x8, S.b[th + TH * q4][j][lane]);
-        f32x4 r[4][NQ];
+        for (int q4 = 0; q4 < NQ; ++q4) bq[q4] = S.b[tp + 2 * q4][j][lane];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bf16x8 af = fp4x8_to_bf16x8(aw[g][j], e8m0_to_f32((sw[g] >> (8 * j)) & 0xFFu));
+          // row n's block j, the same 16 bytes in all four K slots
+          const u32x4 a = S.a[4 * rq + g][16 * j + n];
+          const v8i32 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
 #pragma unroll
-          for (int q4 = 0; q4 < NQ; ++q4) r[g][q4] = mfma_block(af, bfr[q4]);
+          for (int q4 = 0; q4 < NQ; ++q4) {
+            const v8i32 bv = {(int)bq[q4][0], (int)bq[q4][1], (int)bq[q4][2], (int)bq[q4][3],
+                              0, 0, 0, 0};
+            const f32x4 r = mfma_fp4_block(av, bv, j, (int)sw[g], sb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) run[g][q4][i] = fmaf(r[i], dx[q4][j], run[g][q4][i]);
+          }
         }
+      }
+      if ((kc % kRunChunks) == kRunChunks - 1 || kc == KC - 1) {  // a run ends: fold it in
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int q4 = 0; q4 < NQ; ++q4)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[g][q4][i] = fmaf(r[g][q4][i], dxv[q4][j], acc[g][q4][i]);
+          for (int q4 = 0; q4 < NQ; ++q4) {
+            acc[g][q4] += run[g][q4];
+            run[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
       }
     }
   }
@@ -239,19 +317,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
   if constexpr (NQ > 0) {
     const int pr0 = c.prb + 4 * rq;
     if (PASS == GEMM_GATEUP) {
-      // rows pr0..pr0+3 = (gate j, up j, gate j+1, up j+1): 32 features from f0
+      // rows pr0..pr0+3 = (gate j, up j, gate j+1, up j+1): 32 features from
+      // f0; this lane holds features f0 + 4 g4 + i and f0 + 16 + 4 g4 + i
       const int f0 = pr0 * 8;
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4) {
-        const int nt = th + TH * q4;
+        const int nt = tp + 2 * q4;
         float hv[8];
         float m = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float g0 = acc[0][q4][i], u0 = acc[1][q4][i];
-          const float g1 = acc[2][q4][i], u1 = acc[3][q4][i];
-          hv[i] = mid_round(swiglu(g0, u0), p.bf16_mid);
-          hv[4 + i] = mid_round(swiglu(g1, u1), p.bf16_mid);
+          hv[i] = mid_round(swiglu(acc[0][q4][i], acc[1][q4][i]), p.bf16_mid);
+          hv[4 + i] = mid_round(swiglu(acc[2][q4][i], acc[3][q4][i]), p.bf16_mid);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(hv[i]));
@@ -260,23 +337,29 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
         const float d = m / 127.0f;
         const int col = nt * 16 + n;
         if (col < c.t.count) {
-          uint32_t packed[4];
+          // the 4 digit planes of this lane's 8 codes: elements 4 g4 .. +3
+          // (bytes 2 g4, 2 g4 + 1) and 16 + 4 g4 .. +3 (bytes 8 + 2 g4, ..)
+          uint32_t half[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            const float q0 = q8_code(hv[i], d);
-            const float q1 = q8_code(hv[i + 1], d);
-            packed[i / 2] = (__float_as_uint(q0) >> 16) | (__float_as_uint(q1) & 0xFFFF0000u);
+          for (int e = 0; e < 8; ++e) {
+            uint32_t cd[4];
+            q8_digit_codes((int)q8_code(hv[e], d), cd);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) half[e >> 2][s] |= cd[s] << (4 * (e & 3));
           }
-          uint16_t* hrow = p.h + (c.row0 + col) * p.ld_h;
-          *(u32x2*)(hrow + f0 + 4 * g4) = u32x2{packed[0], packed[1]};
-          *(u32x2*)(hrow + f0 + 16 + 4 * g4) = u32x2{packed[2], packed[3]};
+          uint8_t* hrow = p.h + (c.row0 + col) * p.ld_h + (int64_t)(f0 >> 5) * 64 + 2 * g4;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            *(uint16_t*)(hrow + 16 * s) = (uint16_t)half[0][s];
+            *(uint16_t*)(hrow + 16 * s + 8) = (uint16_t)half[1][s];
+          }
           if (g4 == 0) p.hs[(c.row0 + col) * p.ld_hs + (f0 >> 5)] = d;
         }
       }
     } else {
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4) {
-        const int col = (th + TH * q4) * 16 + n;
+        const int col = (tp + 2 * q4) * 16 + n;
         if (col >= c.t.count) continue;
         const int64_t orow = c.shared ? (int64_t)c.A + c.t.start + col : p.sorted[c.t.start + col];
 #pragma unroll
@@ -288,8 +371,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
 }
 
 template <int PASS, int BM>
-__global__ __launch_bounds__(gemm_waves<BM>() * 64, 1) void gemm_kernel(GemmArgs p) {
-  __shared__ Stage<BM> ring[ring_stages<BM>()];
+__global__ __launch_bounds__(kGemmWaves * 64, BM == kBMShort ? 4 : 2) void gemm_kernel(GemmArgs p) {
+  __shared__ Stage<BM> ring[kRing];
 
   // Block b runs on XCD b % 8 (round-robin dispatch).  XCD x walks tiles
   // x, x+8, x+16, ... and all weight-row blocks of a tile back to back, so the
@@ -311,17 +394,24 @@ __global__ __launch_bounds__(gemm_waves<BM>() * 64, 1) void gemm_kernel(GemmArgs
   c.prb = nb * kBNGroups;
   c.A = p.rows * p.top_k;
   c.row0 = c.shared ? (int64_t)c.A + c.t.start : c.t.start;
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  // the rows behind this lane's B load (token group of this wave, column
+  // lane % 16) and scale load (token group 4 (wave - 4) + lane / 16)
+  const int b_tg = BM == kBMFull ? wave : (wave >> 2);
+  c.b_row = gemm_brow<PASS>(p, c, 16 * b_tg + (lane & 15));
+  c.d_row = gemm_brow<PASS>(p, c, 16 * (4 * max(wave - 4, 0) + (lane >> 4)) + (lane & 15));
 
-  // live token groups of this wave's part: th, th+TH, ... below nnt
-  constexpr int TH = gemm_th<BM>();
+  // live token groups of this wave's part: tp, tp+2, ... below nnt
   const int nnt = (c.t.count + 15) >> 4;
-  const int th = (threadIdx.x >> 6) >> 2;
-  const int nq = min(BM / 16 / TH, max(0, (nnt - th + TH - 1) / TH));
+  const int tp = wave >> 2;
+  const int nq = min(BM / 32, max(0, (nnt - tp + 1) / 2));
   if constexpr (BM == kBMShort) {
     if (nq == 1) gemm_body<PASS, 1, BM>(p, c, ring);  // wave-uniform
     else gemm_body<PASS, 0, BM>(p, c, ring);
   } else {
     switch (nq) {  // wave-uniform
+      case 4: gemm_body<PASS, 4, BM>(p, c, ring); break;
+      case 3: gemm_body<PASS, 3, BM>(p, c, ring); break;
       case 2: gemm_body<PASS, 2, BM>(p, c, ring); break;
       case 1: gemm_body<PASS, 1, BM>(p, c, ring); break;
       default: gemm_body<PASS, 0, BM>(p, c, ring); break;
@@ -336,7 +426,6 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
   const WsLayout lay = ws_layout(L, rows);
   uint8_t* base = (uint8_t*)ws;
   const int A = rows * L->top_k;
-  const int n_h = A + (L->has_shared ? rows : 0);
   // short tiles when experts average at most 16 rows (then more than 32 in
   // one expert is rare, and a second tile is the only cost)
   const bool short_tiles = (int64_t)A <= 16LL * L->n_experts;
@@ -351,15 +440,32 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
   a.top_k = L->top_k;
   a.has_shared = L->has_shared;
   a.rows = rows;
+  a.h = base + lay.hidden;
+  a.hs = (float*)(base + lay.hidden_scales);
+  a.ld_h = 2 * (int64_t)L->d_ff;
+  a.ld_hs = L->d_ff / kBlock;
+
+  auto launch = [&](int pass, GemmArgs& g) {
+    g.n_items = tiles * (g.rg_total / kBNGroups);
+    const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
+    const dim3 block(kGemmWaves * 64);
+    if (pass == GEMM_GATEUP) {
+      if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), block, 0, s, g);
+      else hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMFull>), dim3(grid), block, 0, s, g);
+    } else {
+      if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMShort>), dim3(grid), block, 0, s, g);
+      else hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMFull>), dim3(grid), block, 0, s, g);
+    }
+  };
 
   if (stages & MOE_STAGE_GATE_UP) {
-    uint16_t* xb = (uint16_t*)(base + lay.act);
-    float* xs = (float*)(base + lay.act_scales);
-    const int64_t threads = (int64_t)n_h * (L->d_model / 8);
-    hipLaunchKernelGGL(gather_act_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       s, q, ld_q, qs, ld_qs, sorted, offsets, L->n_experts, rows, L->top_k,
-                       L->has_shared, L->d_model, xb, (int64_t)L->d_model, xs,
-                       (int64_t)(L->d_model / kBlock));
+    uint8_t* xp = base + lay.act;
+    const int64_t ld_xp = 2 * (int64_t)L->d_model;
+    if (!(stages & MOE_STAGE_REUSE_ACTS)) {
+      const int64_t threads = (int64_t)rows * (L->d_model / 8);
+      hipLaunchKernelGGL(prep_digits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                         0, s, q, ld_q, rows, L->d_model, xp, ld_xp);
+    }
     const PackedDims pd(2 * L->d_ff, L->d_model);
     GemmArgs g = a;
     g.w = (const uint8_t*)L->gate_up;
@@ -369,21 +475,12 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     g.rg_total = (int)pd.rg;
     g.kc_total = (int)pd.kc;
     g.sc_total = (int)pd.sc;
-    g.xb = xb;
-    g.ld_xb = L->d_model;
-    g.xs = xs;
-    g.ld_xs = L->d_model / kBlock;
-    g.h = (uint16_t*)(base + lay.hidden);
-    g.hs = (float*)(base + lay.hidden_scales);
-    g.ld_h = L->d_ff;
-    g.ld_hs = L->d_ff / kBlock;
+    g.xp = xp;
+    g.ld_xp = ld_xp;
+    g.xs = qs;
+    g.ld_xs = ld_qs;
     g.bf16_mid = (L->flags & MOE_LAYER_BF16_INTERMEDIATE) != 0;
-    g.n_items = tiles * (g.rg_total / kBNGroups);
-    const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
-    if (short_tiles)
-      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), dim3(gemm_waves<kBMShort>() * 64), 0, s, g);
-    else
-      hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMFull>), dim3(grid), dim3(gemm_waves<kBMFull>() * 64), 0, s, g);
+    launch(GEMM_GATEUP, g);
   }
   if (stages & MOE_STAGE_DOWN) {
     const PackedDims pd(L->d_model, L->d_ff);
@@ -395,18 +492,13 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     d.rg_total = (int)pd.rg;
     d.kc_total = (int)pd.kc;
     d.sc_total = (int)pd.sc;
-    d.xb = (const uint16_t*)(base + lay.hidden);
-    d.ld_xb = L->d_ff;
-    d.xs = (const float*)(base + lay.hidden_scales);
-    d.ld_xs = L->d_ff / kBlock;
+    d.xp = a.h;
+    d.ld_xp = a.ld_h;
+    d.xs = a.hs;
+    d.ld_xs = a.ld_hs;
     d.y = (float*)(base + lay.partials);
     d.ld_y = L->d_model;
-    d.n_items = tiles * (d.rg_total / kBNGroups);
-    const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (d.rg_total / kBNGroups));
-    if (short_tiles)
-      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMShort>), dim3(grid), dim3(gemm_waves<kBMShort>() * 64), 0, s, d);
-    else
-      hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMFull>), dim3(grid), dim3(gemm_waves<kBMFull>() * 64), 0, s, d);
+    launch(GEMM_DOWN, d);
     launch_combine((const float*)(base + lay.partials), ids, w, rows, L->top_k, L->has_shared,
                    L->d_model, y, ld_y, s);
   }

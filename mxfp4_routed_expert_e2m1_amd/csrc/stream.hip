@@ -286,6 +286,9 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
     }
   };
   auto compute = [&](int kk, const u32x4 (&sc4)[RGW], f32x4 (&acc)[RGW]) {
+    u32x4 af[RGW];
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) af[g] = tile_to_bf16_frags(a[kk][g]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 bb;
@@ -294,7 +297,7 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
 #pragma unroll
       for (int g = 0; g < RGW; ++g) {
         const float sc = e8m0_to_f32((sc4[g][kk] >> (8 * j)) & 0xFFu);
-        const f32x4 r = mfma_block(fp4x8_to_bf16x8(a[kk][g][j], sc), bb);
+        const f32x4 r = mfma_block(fp4x8_to_bf16x8(af[g][j], sc), bb);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[g][i] = fmaf(r[i], d[kk][j], acc[g][i]);
       }

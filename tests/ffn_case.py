@@ -9,8 +9,9 @@ import torch
 
 import oracle
 import synth
-from parity import (assert_rows_close, check_hidden, check_hidden_bf16, down_col_absmax,
-                    flip_bound, hidden_error_bound, use_host_threads)
+from parity import (assert_rows_close, check_hidden, check_hidden_bf16,
+                    codes_from_digit_planes, down_col_absmax, flip_bound, hidden_error_bound,
+                    use_host_threads)
 
 import mxfp4_routed_expert_e2m1_amd as m
 
@@ -36,6 +37,13 @@ def canonical_experts(L, seed, set_idx, experts):
     return {e: {k: v.cpu().numpy() for k, v in
                 synth.expert_weights(seed, set_idx, e, L.d_model, L.d_ff, device=DEV).items()}
             for e in sorted(experts)}
+
+
+def prefill_gemm(L, entry):
+    """Whether a call takes the prefill grouped GEMM, whose workspace holds the
+    hidden codes as digit planes: moe_ffn_prefill with d_model and 2 d_ff
+    multiples of 256 (other prefill shapes use the decode tiles)."""
+    return entry == "moe_ffn_prefill" and L.d_model % 256 == 0 and (2 * L.d_ff) % 256 == 0
 
 
 def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
@@ -118,9 +126,9 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
     # stage 3: requantised intermediate read back from the documented workspace
     A = T * k
     n_h = A + (T if L.has_shared else 0)
-    hb = ws[off_h: off_h + n_h * L.d_ff * 2].view(torch.bfloat16).view(n_h, L.d_ff)
+    hraw = ws[off_h: off_h + n_h * L.d_ff * 2]
     hs = ws[off_hs: off_hs + n_h * (L.d_ff // 32) * 4].view(torch.float32).view(n_h, L.d_ff // 32)
-    hb, hs = hb.float().cpu().numpy(), hs.cpu().numpy()
+    hs = hs.cpu().numpy()
     pos = np.empty(A, np.int64)
     valid = srt_o[: off_o[-1]]
     pos[valid] = np.arange(valid.size)
@@ -135,6 +143,16 @@ def run_case(L, seed, x, logits, sample=None, entry="moe_ffn_decode", set_idx=0,
             o_rows.append(j * slots + i)
             wts.append(w_o[t, i] if i < k else 1.0)
     gpu_rows, o_rows = np.array(gpu_rows), np.array(o_rows)
+    # the hidden codes of the checked rows (rows of sentinel routes are never
+    # written), stored as E2M1 digit planes or as exact bf16 values
+    hb = np.zeros((n_h, L.d_ff), np.float32)
+    if len(gpu_rows):
+        if prefill_gemm(L, entry):
+            raw = hraw.view(n_h, 2 * L.d_ff)[torch.from_numpy(gpu_rows).to(hraw.device)]
+            hb[gpu_rows] = codes_from_digit_planes(raw.cpu().numpy(), L.d_ff)
+        else:
+            hb[gpu_rows] = hraw.view(torch.bfloat16).view(n_h, L.d_ff)[
+                torch.from_numpy(gpu_rows).to(hraw.device)].float().cpu().numpy()
     flips = np.zeros((len(rows) * slots, L.d_ff), np.float64)
     if bf16_mid:
         flips[o_rows] = check_hidden_bf16(hb[gpu_rows], hs[gpu_rows], mid["hq"][o_rows],

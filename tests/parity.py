@@ -263,3 +263,24 @@ def covering_rows(ids, n_experts, top_k, rows, tile, base, seed):
         if v not in shared:
             pick.add(int(rng.choice(np.arange(v, rows, tile))))
     return np.array(sorted(pick))
+
+
+E2M1_DIGIT = {0x0: 0, 0x2: 1, 0x4: 2, 0xA: -1, 0xC: -2}
+
+
+def codes_from_digit_planes(raw, d_ff):
+    """Hidden codes stored as E2M1 digit planes (the prefill GEMM's workspace
+    format): per row, d_ff/32 groups of 4 planes x 16 bytes, plane s holding
+    digit s of the group's 32 codes (element 2i in the low nibble of byte i);
+    code = sum_s 4^s * digit_s.  raw: uint8 [rows][2 * d_ff].  Any nibble
+    outside the five digit codes is an error."""
+    raw = np.asarray(raw, np.uint8).reshape(raw.shape[0], d_ff // 32, 4, 16)
+    nib = np.empty(raw.shape[:3] + (32,), np.uint8)
+    nib[..., 0::2], nib[..., 1::2] = raw & 0xF, raw >> 4
+    lut = np.full(16, 99, np.int32)
+    for c, v in E2M1_DIGIT.items():
+        lut[c] = v
+    dig = lut[nib]
+    assert np.all(dig != 99), "hidden digit plane holds a nibble that is not a digit 0, +-1, +-2"
+    w = np.array([1, 4, 16, 64], np.int32)[None, None, :, None]
+    return (dig * w).sum(axis=2).reshape(raw.shape[0], d_ff)

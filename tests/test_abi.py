@@ -46,11 +46,10 @@ def test_packed_bytes_and_workspace_queries():
     lay = m.moe_layer_t(4096, 2048, 256, 6, 1, 0x100000, 8912896, 0x200000, 4456448, 0x300000,
                         0x400000)
     L = m.lib()
-    # 7 hidden rows: bf16 codes, f32 scales, f32 partials, bf16 gathered activations and
-    # their f32 scales, each region 256-byte aligned
+    # 7 hidden rows: 2-byte codes, f32 scales, f32 partials; 1 token row of
+    # 2-byte activation digit planes; each region 256-byte aligned
     assert L.moe_ffn_workspace_bytes(C.byref(lay), 1) == (7 * 2048 * 2 + 7 * 64 * 4
-                                                          + 7 * 4096 * 4 + 7 * 4096 * 2
-                                                          + 7 * 128 * 4)
+                                                          + 7 * 4096 * 4 + 1 * 4096 * 2)
     a, b, c = C.c_size_t(), C.c_size_t(), C.c_size_t()
     assert L.moe_ffn_workspace_layout(C.byref(lay), 1, C.byref(a), C.byref(b), C.byref(c)) == 0
     assert (a.value, b.value, c.value) == (0, 28672, 28672 + 1792)

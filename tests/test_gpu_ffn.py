@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from ffn_case import canonical_experts, layer_for, run_case
-from parity import covering_rows
+from parity import covering_rows, use_host_threads
 
 pytestmark = pytest.mark.gpu
 
@@ -529,3 +529,38 @@ def test_ep8_share_shape(rows, entry):
     owned = int((ids_local >= 0).sum())
     print(f"EP8 {rows} {entry}: {owned} of {rows * 6} routes local, worst err/tol "
           f"{r['worst']:.3f}, flips {r['flips']}")
+
+
+@pytest.mark.parametrize("rows", [16, 512, 4096])
+def test_prefill_rows_bitwise_equal_decode_and_exact_rows(rows):
+    # Exact rows in prefill ([strix] "The two gates": every kernel keeps each
+    # row's reduction order identical to the one-token path): the grouped
+    # GEMM sums in the decode kernels' runs of 16 blocks, so each prefill row
+    # equals the same row decoded in a step of 16 rows, and the oracle's
+    # exact-rows mode, bit for bit (16 and 512 rows: every row; 4096: the
+    # covering sample).  The fp64 checks of the same path stay in
+    # test_prefill_rows.
+    use_host_threads()
+    c = synth.PREFILL
+    L = DSV4
+    layer = layer_for(L, c["seed"])
+    x = synth.activations(c["seed"], 8000 + rows, rows, L.d_model)
+    lg = synth.router_logits(c["seed"], 8000 + rows, rows, L.n_experts)
+    xt, lt = torch.from_numpy(x).to(DEV), torch.from_numpy(lg).to(DEV)
+    q, qs = m.moe_quant_act_q8(xt)
+    ids, w, counts, offsets, srt = m.moe_route_group(lt, L.top_k)
+    y = m.moe_ffn_prefill(layer, q, qs, ids, w, offsets, srt)
+    sample = prefill_sample(L, lg, rows, seed=rows + 3)
+    sample = np.arange(rows) if sample is None else sample
+    for i in range(0, len(sample), 16):
+        idx = torch.from_numpy(sample[i:i + 16]).to(DEV)
+        y_d = m.moe_ffn_decode_step(layer, xt[idx].contiguous(), lt[idx].contiguous())[-1]
+        torch.cuda.synchronize()
+        assert torch.equal(y_d, y[idx]), f"rows {sample[i:i + 16]}"
+    with oracle.exact_rows():
+        q_o, qs_o = oracle.quant_q8(x[sample])
+        ids_o, w_o = oracle.route(lg[sample], L.top_k)
+        need = set(int(e) for e in ids_o.reshape(-1)) | {L.n_experts}
+        ex = canonical_experts(L, c["seed"], 0, need)
+        y_o = oracle.ffn(ex, L.n_experts, L.top_k, L.has_shared, q_o, qs_o, ids_o, w_o)
+    np.testing.assert_array_equal(y.cpu().numpy()[sample], y_o)
