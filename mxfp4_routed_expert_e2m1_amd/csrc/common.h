@@ -156,6 +156,19 @@ __device__ __forceinline__ f32x4 mfma_fp4_block(v8i32 a, v8i32 b, int j, int sa,
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
+// Uniform (wave-wide) values live in scalar registers: the compiler cannot
+// see that a value read from LDS or a shuffle is the same in every lane, and
+// a buffer resource it cannot prove uniform costs a loop over the lanes at
+// every load.  Pointers stay kernel arguments plus a uniform offset, so the
+// loads keep their global address space (an integer-to-pointer cast would
+// make them flat loads, which also count as LDS traffic).
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // exp in fp32 by a fixed, named sequence of operations, so a CPU reference
 // can repeat it bit for bit (exact rows): Cody-Waite reduction x = k ln2 + r
 // with ln2 split in two (the high part exact in 16 bits), the degree-7 Taylor

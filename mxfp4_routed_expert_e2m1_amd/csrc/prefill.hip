@@ -36,8 +36,9 @@
 //     order, which the down GEMM reads directly.
 //   * Weights, scales, digit planes and activation scales stream through a
 //     3-stage LDS ring filled by direct global->LDS loads (no registers).
-//   * 8 waves: 4 row quarters (4 row groups each) x 2 token parts (token
-//     groups tp, tp+2, tp+4, tp+6), a 64 x 64 output block per wave.
+//   * 16 waves (128-row tiles; 8 for 32-row tiles): 4 row quarters (4 row
+//     groups each) x 4 token parts (token groups tp, tp+4), a 64 x 32 output
+//     block per wave.
 //   * Block ids are remapped so the workgroups that share a token tile run on
 //     the same XCD and share its L2.
 #include "ffn_internal.h"
@@ -51,9 +52,15 @@ namespace moe {
 constexpr int kBMFull = 128;
 constexpr int kBMShort = 32;
 constexpr int kBNGroups = 16;  // 16-row weight groups per workgroup (256 rows)
-constexpr int kGemmWaves = 8;  // 4 row quarters x 2 token parts
 constexpr int kRing = 3;       // LDS stages (chunks in flight ahead: kRing - 1)
 constexpr int kRunChunks = 4;  // chunks per exact-rows run (16 blocks)
+// Waves per workgroup: 4 row quarters x TH token parts, 4 waves per SIMD
+// (<= 128 VGPRs each) so latencies of one wave hide behind the others.
+// 128-row tiles: 16 waves, each 4 row groups x 2 of the 8 token groups;
+// 32-row tiles: 8 waves, each 4 row groups x 1 of the 2 (two workgroups
+// share a CU).
+template <int BM> constexpr int gemm_waves() { return 8; }
+template <int BM> constexpr int gemm_th() { return gemm_waves<BM>() / 4; }
 
 enum GemmPass : int { GEMM_GATEUP = 0, GEMM_DOWN = 1 };
 
@@ -128,6 +135,18 @@ __device__ inline void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Direct buffer -> LDS load: lane l writes `bytes` (4 or 16) at lds_base + l *
+// bytes from the resource at voff (per lane) + soff (uniform).  A resource
+// in scalar registers and one 32-bit lane offset cost fewer vector registers
+// than a 64-bit address per lane.
+__device__ inline void buf_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, int bytes,
+                                  uint32_t voff, uint32_t soff) {
+  if (bytes == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 16, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 4, voff, soff, 0, 0);
+}
+
 // ------------------------------------------------------------ digit planes
 // E2M1 code of a digit in {-2..2}: sign bit 3, |d| = 1 -> 0b010, 2 -> 0b100.
 __device__ inline uint32_t digit_code(int d) {
@@ -177,8 +196,7 @@ __global__ __launch_bounds__(256) void prep_digits_kernel(const int8_t* __restri
 // ------------------------------------------------------------------- GEMM
 // Everything a workgroup knows about its item once the tile is found.
 struct GemmCtx {
-  const u32x4* nib;
-  const uint8_t* scl;
+  __amdgpu_buffer_rsrc_t blob;  // the expert's packed matrix (tiles, then E8M0 bytes)
   int prb;       // first packed row group of the workgroup
   int64_t row0;  // first hidden row of the tile (A + start for the shared expert)
   Tile t;
@@ -197,15 +215,20 @@ __device__ inline int gemm_brow(const GemmArgs& p, const GemmCtx& c, int r) {
   return c.shared ? c.t.start + r : p.sorted[c.t.start + r] / p.top_k;
 }
 
-// Loads this wave issues per chunk.  Every wave: 2 weight tiles; waves 0-3:
-// one E8M0 load (4 row groups), waves 4..4+NTD/4-1: one scale load (4 token
-// groups); B: 128-row tiles: token group `wave`, all 4 blocks, when live;
-// 32-row tiles: token group wave/4, block wave%4, when live.
+// The loads of one K chunk, spread over the waves: the 16 weight tiles
+// (16 / W per wave), the B digit-plane loads (one per token group and block:
+// NTG * 4 / W per wave, all of them in token group (wave * that) / 4), the
+// E8M0 bytes (waves 0-3, 4 row groups each) and the activation scales (waves
+// 4 .. 4 + NTD/4 - 1, 4 token groups each).
+template <int BM> constexpr int gemm_a_per_wave() { return kBNGroups / gemm_waves<BM>(); }
+template <int BM> constexpr int gemm_b_per_wave() { return Stage<BM>::NTG * 4 / gemm_waves<BM>(); }
+template <int BM> __device__ inline int gemm_b_tg(int wave) { return wave * gemm_b_per_wave<BM>() / 4; }
+
 template <int BM>
 __device__ inline int gemm_loads_per_chunk(int wave, bool b_live) {
   constexpr int NTD = Stage<BM>::NTD;
-  int n = 2 + (wave < 4 ? 1 : 0) + (wave >= 4 && wave < 4 + NTD / 4 ? 1 : 0);
-  if (b_live) n += BM == kBMFull ? 4 : 1;
+  int n = gemm_a_per_wave<BM>() + (wave < 4 ? 1 : 0) + (wave >= 4 && wave < 4 + NTD / 4 ? 1 : 0);
+  if (b_live) n += gemm_b_per_wave<BM>();
   return n;
 }
 
@@ -213,105 +236,132 @@ template <int PASS, int BM>
 __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>& S, int kc,
                                   int wave, int lane, bool b_live) {
   const int n = lane & 15, g4 = lane >> 4;
+  constexpr int AW = gemm_a_per_wave<BM>(), BW = gemm_b_per_wave<BM>();
+  const uint32_t slot = (uint32_t)chunk_slot(kc, p.kc_total);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rg = 2 * wave + i;
-    load_to_lds(c.nib + ((int64_t)(c.prb + rg) * p.kc_total + chunk_slot(kc, p.kc_total)) * 64 + lane,
-                &S.a[rg][0], 16);
+  for (int i = 0; i < AW; ++i) {
+    const int rg = AW * wave + i;
+    buf_to_lds(c.blob, &S.a[rg][0], 16, (uint32_t)lane * 16u,
+               ((uint32_t)(c.prb + rg) * (uint32_t)p.kc_total + slot) * 1024u);
   }
   if (wave < 4) {  // E8M0 bytes of row groups 4 wave .. 4 wave + 3
-    const int rg = 4 * wave + g4;
-    load_to_lds(c.scl + (((int64_t)(c.prb + rg) * p.sc_total + (kc >> 2)) * 16 + n) * 16 + (kc & 3) * 4,
-                &S.s[4 * wave][0], 4);
+    buf_to_lds(c.blob, &S.s[4 * wave][0], 4,
+               (uint32_t)g4 * (uint32_t)p.sc_total * 256u + (uint32_t)n * 16u,
+               (uint32_t)p.nib_bytes +
+                   ((uint32_t)(c.prb + 4 * wave) * (uint32_t)p.sc_total + (uint32_t)(kc >> 2)) * 256u +
+                   (uint32_t)(kc & 3) * 4u);
   } else if (wave < 4 + Stage<BM>::NTD / 4) {  // scales of token groups 4 q .. 4 q + 3
     const int qd = wave - 4;
     load_to_lds(p.xs + (int64_t)c.d_row * p.ld_xs + (int64_t)kc * 4, &S.d[4 * qd][0], 16);
   }
   if (b_live) {
     const uint8_t* src = p.xp + (int64_t)c.b_row * p.ld_xp + (int64_t)kc * 256 + 16 * g4;
-    if constexpr (BM == kBMFull) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_to_lds(src + 64 * j, &S.b[wave][j][0], 16);
-    } else {
-      load_to_lds(src + 64 * (wave & 3), &S.b[wave >> 2][wave & 3][0], 16);
+    for (int i = 0; i < BW; ++i) {
+      const int li = BW * wave + i, tg = li >> 2, j = li & 3;
+      load_to_lds(src + 64 * j, &S.b[tg][j][0], 16);
     }
   }
 }
 
 // K loop + epilogue of one wave owning row groups prb+4*rq .. +3 and token
-// groups tp, tp+2, .. (NQ of them live).  Branch-free inner loop.
+// groups tp, tp+TH, .. (NQ of them live).  Branch-free inner loop.
 template <int PASS, int NQ, int BM>
 __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = uniform(tid >> 6), lane = tid & 63;
   const int n = lane & 15, g4 = lane >> 4;
+  constexpr int TH = gemm_th<BM>();
   const int rq = wave & 3, tp = wave >> 2;
   const int nnt = (c.t.count + 15) >> 4;
   // token group this wave stages
-  const bool b_live = (BM == kBMFull ? wave : (wave >> 2)) < nnt;
+  const bool b_live = gemm_b_tg<BM>(wave) < nnt;
   const int per_chunk = gemm_loads_per_chunk<BM>(wave, b_live);
   // B scale of K slot g4 (digit plane g4 carries weight 4^g4)
   const int sb = 127 + 2 * g4;
 
-  f32x4 acc[4][NQ > 0 ? NQ : 1], run[4][NQ > 0 ? NQ : 1];
+  f32x4 acc[4][NQ > 0 ? NQ : 1];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int q4 = 0; q4 < NQ; ++q4) {
-      acc[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      run[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int q4 = 0; q4 < NQ; ++q4) acc[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KC = p.kc_total;
   // chunks 0 .. kRing-2 go out first; chunk kc + kRing - 1 after chunk kc lands
 #pragma unroll
   for (int k0 = 0; k0 < kRing - 1; ++k0)
     if (k0 < KC) gemm_issue<PASS, BM>(p, c, ring[k0], k0, wave, lane, b_live);
-  for (int kc = 0; kc < KC; ++kc) {
-    // chunk kc has landed when no more than the loads of the chunks issued
-    // after it are outstanding (loads complete in issue order)
-    wait_vmcnt(min(kRing - 2, KC - 1 - kc) * per_chunk);
-    ring_barrier();  // every wave's loads of chunk kc have landed; chunk kc-1 is consumed
-    if (kc + kRing - 1 < KC)
-      gemm_issue<PASS, BM>(p, c, ring[(kc + kRing - 1) % kRing], kc + kRing - 1, wave, lane, b_live);
-    if constexpr (NQ > 0) {
-      const Stage<BM>& S = ring[kc % kRing];
-      f32x4 dx[NQ];
+  int kc = 0;
+  // runs of kRunChunks chunks, each summed from zero and added in order
+  for (int kr = 0; kr < KC; kr += kRunChunks) {
+    f32x4 run[4][NQ > 0 ? NQ : 1];
 #pragma unroll
-      for (int q4 = 0; q4 < NQ; ++q4) dx[q4] = S.d[tp + 2 * q4][n];
-      uint32_t sw[4];
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) sw[g] = S.s[4 * rq + g][n];
+      for (int q4 = 0; q4 < NQ; ++q4) run[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kend = min(kr + kRunChunks, KC);
+    for (; kc < kend; ++kc) {
+      // chunk kc has landed when no more than the loads of the chunks issued
+      // after it are outstanding (loads complete in issue order)
+      wait_vmcnt(min(kRing - 2, KC - 1 - kc) * per_chunk);
+      ring_barrier();  // every wave's loads of chunk kc have landed; chunk kc-1 is consumed
+      if (kc + kRing - 1 < KC)
+        gemm_issue<PASS, BM>(p, c, ring[(kc + kRing - 1) % kRing], kc + kRing - 1, wave, lane,
+                             b_live);
+      if constexpr (NQ > 0) {
+        const Stage<BM>& S = ring[kc % kRing];
+        const float* sd = (const float*)&S.d[0][0];  // [token group][column][block]
+        uint32_t sw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 bq[NQ];
-#pragma unroll
-        for (int q4 = 0; q4 < NQ; ++q4) bq[q4] = S.b[tp + 2 * q4][j][lane];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // row n's block j, the same 16 bytes in all four K slots
-          const u32x4 a = S.a[4 * rq + g][16 * j + n];
-          const v8i32 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+        for (int g = 0; g < 4; ++g) sw[g] = S.s[4 * rq + g][n];
+        // operands of block j: A[g] (row n's block j of row group g, the same
+        // 16 bytes in all four K slots), B[q4] (digit planes), D[q4] (scale)
+        u32x4 A[2][4], B[2][NQ];
+        float D[2][NQ];
+        auto load = [&](int j, int slot) {
 #pragma unroll
           for (int q4 = 0; q4 < NQ; ++q4) {
-            const v8i32 bv = {(int)bq[q4][0], (int)bq[q4][1], (int)bq[q4][2], (int)bq[q4][3],
-                              0, 0, 0, 0};
-            const f32x4 r = mfma_fp4_block(av, bv, j, (int)sw[g], sb);
+            B[slot][q4] = S.b[tp + TH * q4][j][lane];
+            D[slot][q4] = sd[((tp + TH * q4) * 16 + n) * 4 + j];
+          }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) run[g][q4][i] = fmaf(r[i], dx[q4][j], run[g][q4][i]);
+          for (int g = 0; g < 4; ++g) A[slot][g] = S.a[4 * rq + g][16 * j + n];
+        };
+        load(0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int cur = j & 1;
+          if (j + 1 < 4) load(j + 1, cur ^ 1);  // next block's reads go out first
+          // row group g's products, then the scaling of row group g-1's:
+          // every FMA reads a result one row group old, never a fresh one
+          f32x4 R[2][NQ];
+#pragma unroll
+          for (int g = 0; g <= 4; ++g) {
+            if (g < 4) {
+              const v8i32 av = {(int)A[cur][g][0], (int)A[cur][g][1], (int)A[cur][g][2],
+                                (int)A[cur][g][3], 0, 0, 0, 0};
+#pragma unroll
+              for (int q4 = 0; q4 < NQ; ++q4) {
+                const v8i32 bv = {(int)B[cur][q4][0], (int)B[cur][q4][1], (int)B[cur][q4][2],
+                                  (int)B[cur][q4][3], 0, 0, 0, 0};
+                R[g & 1][q4] = mfma_fp4_block(av, bv, j, (int)sw[g], sb);
+              }
+            }
+            if (g > 0) {
+#pragma unroll
+              for (int q4 = 0; q4 < NQ; ++q4)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  run[g - 1][q4][i] = fmaf(R[(g - 1) & 1][q4][i], D[cur][q4], run[g - 1][q4][i]);
+            }
           }
         }
       }
-      if ((kc % kRunChunks) == kRunChunks - 1 || kc == KC - 1) {  // a run ends: fold it in
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int q4 = 0; q4 < NQ; ++q4) {
-            acc[g][q4] += run[g][q4];
-            run[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-      }
     }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int q4 = 0; q4 < NQ; ++q4) acc[g][q4] += run[g][q4];
   }
 
   if constexpr (NQ > 0) {
@@ -322,7 +372,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
       const int f0 = pr0 * 8;
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4) {
-        const int nt = tp + 2 * q4;
+        const int nt = tp + TH * q4;
         float hv[8];
         float m = 0.f;
 #pragma unroll
@@ -359,7 +409,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
     } else {
 #pragma unroll
       for (int q4 = 0; q4 < NQ; ++q4) {
-        const int col = (tp + 2 * q4) * 16 + n;
+        const int col = (tp + TH * q4) * 16 + n;
         if (col >= c.t.count) continue;
         const int64_t orow = c.shared ? (int64_t)c.A + c.t.start + col : p.sorted[c.t.start + col];
 #pragma unroll
@@ -371,7 +421,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
 }
 
 template <int PASS, int BM>
-__global__ __launch_bounds__(kGemmWaves * 64, BM == kBMShort ? 4 : 2) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(gemm_waves<BM>() * 64, BM == kBMFull ? 2 : 4) void gemm_kernel(GemmArgs p) {
   __shared__ Stage<BM> ring[kRing];
 
   // Block b runs on XCD b % 8 (round-robin dispatch).  XCD x walks tiles
@@ -383,32 +433,38 @@ __global__ __launch_bounds__(kGemmWaves * 64, BM == kBMShort ? 4 : 2) void gemm_
   const int tile_idx = (slot / n_nb) * 8 + xcd;
   const int nb = slot % n_nb;
   if (tile_idx * n_nb >= p.n_items) return;
-  int n_tiles;
+  // The shared expert's tiles (all full but the last) take the low ids, so
+  // the longest items start first and the short routed tiles fill the tail.
+  TileMap<BM> m;
+  m.load(p.offsets, p.n_experts, p.has_shared, p.rows);
   GemmCtx c;
-  c.t = find_tile<BM>(p.offsets, p.n_experts, p.has_shared, p.rows, tile_idx, &n_tiles);
+  c.t = m.lookup(p.n_experts, p.rows,
+                 tile_idx < m.shared_tiles ? m.routed + tile_idx : tile_idx - m.shared_tiles);
+  c.t.expert = uniform(c.t.expert);
+  c.t.start = uniform(c.t.start);
+  c.t.count = uniform(c.t.count);
   if (c.t.expert < 0) return;
   c.shared = c.t.expert == p.n_experts;
-  const uint8_t* blob = c.shared ? p.w_shared : p.w + (int64_t)c.t.expert * p.w_stride;
-  c.nib = (const u32x4*)blob;
-  c.scl = blob + p.nib_bytes;
+  const int64_t eoff = c.shared ? 0 : uniform((int64_t)c.t.expert * p.w_stride);
+  const uint8_t* blob = (c.shared ? p.w_shared : p.w) + eoff;
+  c.blob = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(blob), (short)0,
+      (int)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256), 0x00020000);
   c.prb = nb * kBNGroups;
   c.A = p.rows * p.top_k;
   c.row0 = c.shared ? (int64_t)c.A + c.t.start : c.t.start;
-  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
-  // the rows behind this lane's B load (token group of this wave, column
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = (int)(threadIdx.x & 63);
+  // the rows behind this lane's B load (the wave's token group, column
   // lane % 16) and scale load (token group 4 (wave - 4) + lane / 16)
-  const int b_tg = BM == kBMFull ? wave : (wave >> 2);
-  c.b_row = gemm_brow<PASS>(p, c, 16 * b_tg + (lane & 15));
+  c.b_row = gemm_brow<PASS>(p, c, 16 * gemm_b_tg<BM>(wave) + (lane & 15));
   c.d_row = gemm_brow<PASS>(p, c, 16 * (4 * max(wave - 4, 0) + (lane >> 4)) + (lane & 15));
 
-  // live token groups of this wave's part: tp, tp+2, ... below nnt
+  // live token groups of this wave's part: tp, tp+TH, ... below nnt
+  constexpr int TH = gemm_th<BM>();
   const int nnt = (c.t.count + 15) >> 4;
   const int tp = wave >> 2;
-  const int nq = min(BM / 32, max(0, (nnt - tp + 1) / 2));
-  if constexpr (BM == kBMShort) {
-    if (nq == 1) gemm_body<PASS, 1, BM>(p, c, ring);  // wave-uniform
-    else gemm_body<PASS, 0, BM>(p, c, ring);
-  } else {
+  const int nq = min(BM / 16 / TH, max(0, (nnt - tp + TH - 1) / TH));
+  if constexpr (BM == kBMFull) {
     switch (nq) {  // wave-uniform
       case 4: gemm_body<PASS, 4, BM>(p, c, ring); break;
       case 3: gemm_body<PASS, 3, BM>(p, c, ring); break;
@@ -416,6 +472,9 @@ __global__ __launch_bounds__(kGemmWaves * 64, BM == kBMShort ? 4 : 2) void gemm_
       case 1: gemm_body<PASS, 1, BM>(p, c, ring); break;
       default: gemm_body<PASS, 0, BM>(p, c, ring); break;
     }
+  } else {
+    if (nq == 1) gemm_body<PASS, 1, BM>(p, c, ring);
+    else gemm_body<PASS, 0, BM>(p, c, ring);
   }
 }
 
@@ -448,12 +507,12 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
   auto launch = [&](int pass, GemmArgs& g) {
     g.n_items = tiles * (g.rg_total / kBNGroups);
     const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
-    const dim3 block(kGemmWaves * 64);
+    const dim3 block(gemm_waves<kBMFull>() * 64), block_s(gemm_waves<kBMShort>() * 64);
     if (pass == GEMM_GATEUP) {
-      if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), block, 0, s, g);
+      if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), block_s, 0, s, g);
       else hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMFull>), dim3(grid), block, 0, s, g);
     } else {
-      if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMShort>), dim3(grid), block, 0, s, g);
+      if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMShort>), dim3(grid), block_s, 0, s, g);
       else hipLaunchKernelGGL((gemm_kernel<GEMM_DOWN, kBMFull>), dim3(grid), block, 0, s, g);
     }
   };

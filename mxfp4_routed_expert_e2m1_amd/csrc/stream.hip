@@ -42,18 +42,6 @@ constexpr int kSKPW = 4;  // K chunks of a wave per item
 constexpr int kSAhead = STREAM_AHEAD;
 static_assert(kSAhead >= 1 && kSAhead <= kSKPW, "prefetch distance");
 
-// Uniform (wave-wide) values live in scalar registers: the compiler cannot
-// see that a value read from LDS or a shuffle is the same in every lane.
-// Pointers stay kernel arguments plus a uniform offset, so the loads keep
-// their global address space (an integer-to-pointer cast would make them
-// flat loads, which also count as LDS traffic).
-__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ inline int64_t uniform(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // Raw buffer loads: a wave-uniform resource (base, size) in scalar registers,
 // a per-lane byte offset in one vector register, a uniform byte offset in a
 // scalar register and a constant in the instruction.  Offsets at or past the
