@@ -7,12 +7,17 @@ grouping, gate/up projection + SwiGLU + requant, down projection, weighted
 combine.  Layer weight sets are rotated per step so the MALL (256 MB) cannot
 hold them.  Prints one JSON line.
 
-Workloads (--workload):
-  decode        DS-V4 layer (256 experts, top-6 + shared, D 4096, F 2048),
-                1 token per step, 8 layer sets (27.5 GB)            [default]
-  decode-batch  same layer, --rows 2/4/8/16 tokens per step (--hot: +2.0 logit
-                bias on 16 experts)
-  prefill       same layer, --rows 512 or 4096 tokens per step, 2 layer sets
+With no --workload, the line's value is the 1-row decode step (the DS-V4
+layer, 8 rotated layer sets) and its "configs" object times every other
+configuration of the metric in the same run: decode at 2, 4, 8, 16 rows
+(uniform and hot-16 routes), prefill at 512 and 4096 rows, and the MXFP4
+matvec at K = 1..5 rows, each with its dominant kernel's roofline.
+
+One workload alone (--workload), e.g. under a profiler:
+  decode        1 token per step, 8 layer sets (27.5 GB)
+  decode-batch  --rows 2/4/8/16 tokens per step (--hot: +2.0 logit bias on 16
+                experts)
+  prefill       --rows 512 or 4096 tokens per step, 2 layer sets
   matvec        MXFP4 matvec 14336x4096, --rows K resident rows, 16 copies
   copy          calibration only: a plain 1 GiB device-to-device copy (torch),
                 the known-size reference for HBM byte counters
@@ -31,14 +36,28 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-FFN tokens/s + achieved HBM GB/s (decode 1-16 rows), TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+I8_MFMA_PEAK_TOPS = 5000.0
+FP4_MFMA_PEAK_TFLOPS = 10100.0
+
+# Issue ceiling of the prefill GEMMs.  Per 16x16 output tile and 32-element
+# block a SIMD issues one scaled FP4 16x16x128 instruction (16.5 cycles
+# measured) and four wave64 fp32 FMAs (the activation scale; 2.5 cycles each
+# with two waves per SIMD, measured; no packed fp32), which do not overlap
+# the matrix core when two waves share a SIMD, plus 2.5 cycles of operand
+# moves: 29 cycles measured for the pattern in isolation.  At the 2.4 GHz
+# peak clock on 1024 SIMDs:
+GEMM_UNIT_CYCLES = 29.0
+GEMM_CLOCK_GHZ = 2.4
+GEMM_SIMDS = 1024
 
 # HBM bytes per launch of each workload's dominant kernel, from rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE (KiB per dispatch) on the native counters driver
-# replaying this benchmark's own inputs (profiles/hbm_traffic_counters.md),
-# scaled by the plain-copy calibration: read = 2 x FETCH_SIZE, written =
-# WRITE_SIZE.  Valid only for the kernel sources they were taken with (hash
-# below, over the device code in csrc/): after any change to it the benchmark
-# reports traffic as null.
+# replaying this benchmark's own inputs, scaled by the plain-copy calibration:
+# read = 2 x FETCH_SIZE, written = WRITE_SIZE.  Counted offline (the source is
+# named in the line); valid only for the kernel sources they were taken with
+# (hash below, over the device code in csrc/): after any change to it the
+# benchmark reports traffic as null.
+TRAFFIC_DOC = "profiles/hbm_traffic_counters.md (moe_counters under rocprofv3 --pmc, offline)"
 TRAFFIC_SRC = "2d236613a72e4058"
 TRAFFIC = {  # (workload, rows[, variant]): (read bytes, written bytes)
     ("decode", 1): (2 * 30777.0 * 1024, 48.6 * 1024),
@@ -66,13 +85,14 @@ def kernel_sources_hash():
 
 
 def traffic_for(key):
-    """Counted HBM bytes per launch for this workload, or None (not counted,
-    or the kernels changed since)."""
-    if key not in TRAFFIC or kernel_sources_hash() != TRAFFIC_SRC:
-        return None
+    """Counted HBM bytes per launch for this workload and where they come
+    from, or (None, reason): not counted, or the kernels changed since."""
+    if key not in TRAFFIC:
+        return None, "not counted for this workload"
+    if kernel_sources_hash() != TRAFFIC_SRC:
+        return None, f"stale: counted on kernel sources {TRAFFIC_SRC}, now {kernel_sources_hash()}"
     r, w = TRAFFIC[key]
-    return int(r + w)
-I8_MFMA_PEAK_TOPS = 5000.0
+    return int(r + w), TRAFFIC_DOC
 
 
 def parse():
@@ -80,8 +100,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode-batch", "prefill", "matvec", "copy"])
+    ap.add_argument("--workload", default=None,
+                    choices=["decode", "decode-batch", "prefill", "matvec", "copy"],
+                    help="time this workload alone (default: the 1-row decode step as the "
+                         "value plus every configuration of the metric)")
     ap.add_argument("--rows", type=int, default=None)
     ap.add_argument("--hot", action="store_true")
     ap.add_argument("--shard", choices=["tp8"], default=None,
@@ -123,50 +145,123 @@ def main():
     m.lib()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
+    env = Env(m, synth, np, torch, dev)
 
     wl = args.workload
     if wl == "matvec":
-        return bench_matvec(args, m, synth, np, torch, dev)
+        return emit(bench_matvec(env, args, args.rows or 4, args.steps, args.warmup,
+                                 not args.no_cpu_baseline), args)
     if wl == "copy":
         return bench_copy(args, torch, dev)
+    if wl is not None:
+        T = args.rows or {"decode": 1, "decode-batch": 16, "prefill": 4096}[wl]
+        r = run_ffn(env, args, wl, T, args.hot, args.steps, args.warmup)
+        if r is None:   # --dump-inputs
+            return
+        cpu = None
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(env, args, r["L"], r["seed"], T, wl == "prefill")
+        return emit(line_of(r, args, cpu), args)
 
+    # the whole metric: the 1-row step is the value, every other configuration
+    # goes into "configs" (a few seconds each, layer sets packed once per seed)
+    t_all = time.perf_counter()
+    head = run_ffn(env, args, "decode", 1, False, args.steps, args.warmup)
+    configs = {"decode_t1": summary(head)}
+    plan = ([("decode-batch", t, False) for t in (2, 4, 8, 16)]
+            + [("decode-batch", t, True) for t in (2, 4, 8, 16)]
+            + [("prefill", 512, False), ("prefill", 4096, False)])
+    for wl2, T, hot in plan:
+        r = run_ffn(env, args, wl2, T, hot, None, None)
+        configs[f"{'prefill' if wl2 == 'prefill' else 'decode'}_t{T}{'_hot' if hot else ''}"] = \
+            summary(r)
+        print(f"[bench] {wl2} {T}{' hot' if hot else ''}: {r['ms_step']:.4f} ms/step, "
+              f"{r['roof']['kernel']} {r['roof']['avg_us']} us", file=sys.stderr, flush=True)
+    env.drop_layers()
+    for K in (1, 2, 3, 4, 5):
+        mv = bench_matvec(env, args, K, None, None, False)
+        configs[f"matvec_k{K}"] = {"rows": K, "ms_per_step": mv["ms_per_step"],
+                                   "rows_per_s": mv["value"], "roofline": mv["roofline"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(env, args, head["L"], head["seed"], 1, False)
+    line = line_of(head, args, cpu)
+    line["configs"] = configs
+    line["bench_wall_s"] = round(time.perf_counter() - t_all, 1)
+    emit(line, args)
+
+
+class Env:
+    """Torch, the binding and the packed layer sets of the last seed used."""
+
+    def __init__(self, m, synth, np, torch, dev):
+        self.m, self.synth, self.np, self.torch, self.dev = m, synth, np, torch, dev
+        self.key, self.layers = None, None
+
+    def layer_sets(self, L, seed, sets):
+        key = (L, seed, sets)
+        if self.key != key:
+            self.drop_layers()
+            t0 = time.time()
+            out = []
+            for s in range(sets):
+                fn = lambda e, s=s: self.synth.expert_weights(seed, s, e, L.d_model, L.d_ff,
+                                                              device=self.dev)
+                out.append(self.m.pack_layer(L.d_model, L.d_ff, L.n_experts, L.top_k, fn, True,
+                                             self.dev))
+            self.torch.cuda.synchronize()
+            print(f"[bench] packed {sets} layer sets (seed {seed}) in {time.time() - t0:.1f}s",
+                  file=sys.stderr, flush=True)
+            self.key, self.layers = key, out
+        return self.layers
+
+    def drop_layers(self):
+        self.key, self.layers = None, None
+        self.torch.cuda.empty_cache()
+
+
+def expert_bytes(L):
+    """Algorithmic bytes of one expert: E2M1 codes (half a byte) + one E8M0
+    byte per 32 weights, gate/up (2F x D) and down (D x F)."""
+    gu = 2 * L.d_ff * L.d_model // 2 + 2 * L.d_ff * L.d_model // 32
+    dn = L.d_model * L.d_ff // 2 + L.d_model * L.d_ff // 32
+    return gu, dn
+
+
+def run_ffn(env, args, wl, T, hot, steps, warmup):
+    """Time `steps` whole steps of one FFN workload (graph replays over the
+    rotated layer sets and inputs), then its dominant kernel alone."""
+    m, synth, np, torch, dev = env.m, env.synth, env.np, env.torch, env.dev
+    stream = torch.cuda.current_stream()
     L = synth.DSV4_LAYER
     if args.shard == "tp8":
         L = synth.Layer(n_experts=L.n_experts, top_k=L.top_k, d_model=L.d_model,
                         d_ff=L.d_ff // 8, has_shared=L.has_shared)
     if wl == "decode":
-        T, seed, sets = 1, synth.DECODE["seed"], 8
+        seed, sets = synth.DECODE["seed"], 8
     elif wl == "decode-batch":
-        T, seed, sets = (args.rows or 16), synth.DECODE_BATCH["seed"], 8
+        seed, sets = synth.DECODE_BATCH["seed"], 8
     else:
-        T, seed, sets = (args.rows or 4096), synth.PREFILL["seed"], 2
+        seed, sets = synth.PREFILL["seed"], 2
     sets = args.sets or sets
     prefill = wl == "prefill"
-    steps = args.steps or (200 if prefill else 1000)
-    warmup = args.warmup if args.warmup is not None else (20 if prefill else 50)
+    steps = steps or (200 if prefill else 1000)
+    warmup = warmup if warmup is not None else (20 if prefill else 50)
     n_inputs = 4 if prefill else 16
-    hot = 2.0 if args.hot else 0.0
+    hot_bias = 2.0 if hot else 0.0
 
-    t0 = time.time()
-    layers = []
-    for s in range(sets):
-        fn = lambda e, s=s: synth.expert_weights(seed, s, e, L.d_model, L.d_ff, device=dev)
-        layers.append(m.pack_layer(L.d_model, L.d_ff, L.n_experts, L.top_k, fn, True, dev))
+    layers = env.layer_sets(L, seed, sets)
     base_layers = layers
     wrs = []
     if args.router:
         wrs = [torch.from_numpy(synth.router_weights(seed, s, L.n_experts, L.d_model)
                                 .view(np.int16)).to(dev) for s in range(sets)]
         layers = [lay.variant(router=wr) for lay, wr in zip(base_layers, wrs)]
-    torch.cuda.synchronize()
-    print(f"[bench] packed {sets} layer sets in {time.time() - t0:.1f}s", file=sys.stderr,
-          flush=True)
 
     xs = [torch.from_numpy(synth.activations(seed, i, T, L.d_model)).to(dev)
           for i in range(n_inputs)]
-    lgs = [torch.from_numpy(synth.router_logits(seed, i, T, L.n_experts, hot_bias=hot)).to(dev)
-           for i in range(n_inputs)]
+    lgs = [torch.from_numpy(synth.router_logits(seed, i, T, L.n_experts, hot_bias=hot_bias))
+           .to(dev) for i in range(n_inputs)]
     lg_out = torch.empty((T, L.n_experts), dtype=torch.float32, device=dev)
     if args.router:   # the logits come from the router instead; routes from those
         lgs = [m.moe_router_logits(xs[i], wrs[i % sets]) for i in range(n_inputs)]
@@ -179,7 +274,6 @@ def main():
                  torch.empty(T * L.top_k, dtype=torch.int32, device=dev))
     y = torch.empty((T, L.d_model), dtype=torch.float32, device=dev)
     ws = torch.empty(m.moe_ffn_workspace_bytes(layers[0], T), dtype=torch.uint8, device=dev)
-    ffn = m.moe_ffn_prefill if prefill else m.moe_ffn_decode
 
     def step(i):
         lg = lgs[i % n_inputs]
@@ -189,7 +283,7 @@ def main():
                 lg = m.moe_router_logits(xs[i % n_inputs], wrs[i % sets], logits=lg_out)
             m.moe_route_group(lg, L.top_k, out=route_out)
             ids, w, counts, offsets, srt = route_out
-            ffn(layers[i % sets], q, qs, ids, w, offsets, srt, y=y, ws=ws)
+            m.moe_ffn_prefill(layers[i % sets], q, qs, ids, w, offsets, srt, y=y, ws=ws)
         else:  # decode: the whole step from the layer input in one call
             m.moe_ffn_decode_step(layers[i % sets], xs[i % n_inputs],
                                   lg_out if args.router else lg, q=q, scales=qs,
@@ -212,7 +306,7 @@ def main():
         lgs[last % n_inputs].cpu().numpy().tofile(os.path.join(args.dump_inputs, "logits.f32"))
         print(json.dumps({"dumped": args.dump_inputs, "workload": wl, "rows": T,
                           "experts_touched": touched[last % n_inputs]}))
-        return
+        return None
     for i in range(max(warmup, cycle)):
         step(i)
     torch.cuda.synchronize()
@@ -246,23 +340,26 @@ def main():
     if not torch.equal(y, y_eager):
         raise SystemExit("graph replay differs from the eager step")
     cycle_ms = [marks[i].elapsed_time(marks[i + 1]) / cycle for i in range(reps)]
+    # percentiles of the per-cycle step time, only with enough cycles to mean one
     step_pct = ([round(float(v), 5) for v in np.percentile(cycle_ms, [10, 50, 90])]
-                if cycle_ms else None)
+                if len(cycle_ms) >= 3 else None)
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / steps
     tok_s = T * steps / (ms_total / 1e3)
 
-    gu_bytes = 2 * L.d_ff * L.d_model // 2 + 2 * L.d_ff * L.d_model // 32
-    dn_bytes = L.d_model * L.d_ff // 2 + L.d_model * L.d_ff // 32
+    gu_bytes, dn_bytes = expert_bytes(L)
     A = T * L.top_k + T
-    act_bytes = T * (L.d_model * 4 + L.d_model + L.d_model // 8)  # x read, q + scales written
     mean_touched = float(np.mean(touched))
-    step_bytes = mean_touched * (gu_bytes + dn_bytes) + act_bytes + T * L.d_model * 4
+    # the step's algorithmic bytes: the touched experts' weights, x and the
+    # logits in, y out (int8 codes and hidden codes stay in the workspace)
+    step_bytes = (mean_touched * (gu_bytes + dn_bytes) + T * L.d_model * 4
+                  + T * L.n_experts * 4 + T * L.d_model * 4)
     if args.router:
-        step_bytes += L.n_experts * L.d_model * 2 + T * L.n_experts * 4
+        step_bytes += L.n_experts * L.d_model * 2
 
     # dominant kernel, alone over the rotated sets in a graph: the gate/up
-    # projection (decode) or the gate/up GEMM (prefill)
+    # projection (decode) or the gate/up GEMM without the digit-plane prep
+    # (prefill: MOE_STAGE_REUSE_ACTS; the timed step ran the prep just before)
     ids, w, counts, offsets, srt = route_out   # routes of input `last`
     n_k = sets * max(1, 64 // sets)
     fused1 = not prefill and T == 1   # one row: quantiser + router + gate/up, one kernel
@@ -271,7 +368,8 @@ def main():
             base_layers[i % sets], xs[last % n_inputs], lgs[last % n_inputs], q=q, scales=qs,
             route_out=route_out, y=y, ws=ws, stage_mask=m.MOE_STAGE_GATE_UP)
     else:
-        kcall = lambda i: m.moe_ffn_stages(base_layers[i % sets], int(prefill), m.MOE_STAGE_GATE_UP,
+        mask = m.MOE_STAGE_GATE_UP | (m.MOE_STAGE_REUSE_ACTS if prefill else 0)
+        kcall = lambda i: m.moe_ffn_stages(base_layers[i % sets], int(prefill), mask,
                                            q, qs, ids, w, offsets, srt, y, ws)
     g_k = capture(torch, lambda: [kcall(i) for i in range(n_k)])
     g_k.replay()
@@ -284,49 +382,59 @@ def main():
     torch.cuda.synchronize()
     k_us = ev0.elapsed_time(ev1) * 1e3 / (kreps * n_k)
     last_touched = touched[last % n_inputs]
+    counts_np = counts.cpu().numpy()
+    tkey = ((wl, T) + (("hot",) if hot else ())
+            if not args.shard and (not args.router or (T == 1 and not hot)) else None)
+    traffic, traffic_src = traffic_for(tkey)
+    # algorithmic bytes of the gate/up launch: the touched experts' gate/up
+    # weights, each token's int8 codes and scales once (T (D + D/8)), one
+    # byte per hidden code and its fp32 scale out (A (F + F/8))
+    k_bytes = last_touched * gu_bytes + T * (L.d_model + L.d_model // 8) + A * (L.d_ff + L.d_ff // 8)
     if prefill:
         k_flops = 2.0 * A * (2 * L.d_ff) * L.d_model
         achieved = k_flops / (k_us * 1e-6) / 1e12
-        # hidden codes are written as bf16 (2 bytes) with fp32 scales; the GEMM
-        # reads every hidden row's activations as gathered bf16 codes + scales
-        hidden_bytes = A * (2 * L.d_ff + L.d_ff // 32 * 4)
-        k_bytes = last_touched * gu_bytes + A * (2 * L.d_model + L.d_model // 8) + hidden_bytes
         hbm_gbs = k_bytes / (k_us * 1e-6) / 1e9
-        # the bound is the one the kernel's arithmetic intensity selects: below
-        # the ridge (peak flops / peak bytes) the weights' stream bounds it
+        # what this implementation's layout moves by design: the tokens'
+        # digit planes (2 bytes per code) gathered per assignment, hidden
+        # codes written as digit planes too
+        impl_bytes = (last_touched * gu_bytes + A * (2 * L.d_model + L.d_model // 8)
+                      + A * (2 * L.d_ff + L.d_ff // 8))
+        # issue ceiling: 16 x 16 output tiles x 32-element blocks, with each
+        # expert's rows padded to whole 16-row groups as the GEMM runs them
+        rows16 = int(sum((int(c) + 15) // 16 * 16 for c in counts_np)) + (T + 15) // 16 * 16
+        units = rows16 / 16 * (2 * L.d_ff / 16) * (L.d_model / 32)
+        ceil_us = units * GEMM_UNIT_CYCLES / GEMM_SIMDS / (GEMM_CLOCK_GHZ * 1e3)
         ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         intensity = k_flops / k_bytes
-        common = dict(traffic=traffic_for((wl, T) if not args.router and not args.shard else None),
-                      kernel="gemm_kernel<gate/up>", avg_us=round(k_us, 3),
-                      flop_per_byte=round(intensity, 1), ridge_flop_per_byte=round(ridge, 1))
-        if intensity >= ridge:
-            roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), **common,
-                        i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
-                        hbm_gbs=round(hbm_gbs, 1))
-        else:
-            roof = dict(bound="hbm", achieved=round(hbm_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(hbm_gbs / HBM_PEAK_GBS, 4), **common,
-                        tflops=round(achieved, 2),
-                        mfma_frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4))
+        roof = dict(kernel="gemm_kernel<gate/up>", avg_us=round(k_us, 3),
+                    bound="mfma" if intensity >= ridge else "hbm",
+                    achieved=round(achieved, 2) if intensity >= ridge else round(hbm_gbs, 1),
+                    peak=BF16_MFMA_PEAK_TFLOPS if intensity >= ridge else HBM_PEAK_GBS,
+                    unit="TFLOP/s" if intensity >= ridge else "GB/s",
+                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS if intensity >= ridge
+                               else hbm_gbs / HBM_PEAK_GBS, 4),
+                    tflops=round(achieved, 2),
+                    bf16_peak_frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                    i8_peak_frac=round(achieved / I8_MFMA_PEAK_TOPS, 4),
+                    fp4_peak_frac=round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
+                    issue_ceiling_us=round(ceil_us, 1),
+                    issue_ceiling_frac=round(ceil_us / k_us, 4),
+                    hbm_gbs=round(hbm_gbs, 1), hbm_frac=round(hbm_gbs / HBM_PEAK_GBS, 4),
+                    bytes_per_launch=int(k_bytes), impl_bytes_per_launch=int(impl_bytes),
+                    flop_per_byte=round(intensity, 1), ridge_flop_per_byte=round(ridge, 1),
+                    traffic=traffic, traffic_src=traffic_src, experts_touched=last_touched)
     else:
-        # gate/up weights of the touched experts, activations, hidden codes out
-        # (one row: the fp32 row and the logits in, its codes and routes out)
-        k_bytes = (last_touched * gu_bytes + T * (L.d_model + L.d_model // 8)
-                   + A * (2 * L.d_ff + L.d_ff // 32 * 4))
         kname = "stream_kernel<gate/up>"
-        if fused1:
+        if fused1:   # the fp32 row and its logits in, its codes and routes out
             k_bytes += T * (L.d_model * 4 + L.n_experts * 4)
             kname = "stream_step1_kernel<quantise + route + gate/up>"
+        # the layout's hidden codes are bf16 values (2 bytes per code)
+        impl_bytes = k_bytes + A * L.d_ff
         achieved = k_bytes / (k_us * 1e-6) / 1e9
-        # the counted routes are the benchmark's own (hot-expert and router runs
-        # route differently, except for the one-row step's 7 experts)
-        tkey = ((wl, T) + (("hot",) if hot else ())
-                if not args.shard and (not args.router or (T == 1 and not hot)) else None)
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(tkey),
-                    kernel=kname, avg_us=round(k_us, 3),
-                    bytes_per_launch=int(k_bytes), experts_touched=last_touched)
+        roof = dict(kernel=kname, avg_us=round(k_us, 3), bound="hbm", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                    bytes_per_launch=int(k_bytes), impl_bytes_per_launch=int(impl_bytes),
+                    traffic=traffic, traffic_src=traffic_src, experts_touched=last_touched)
 
     router = None
     if args.router:   # the router projection alone, over the rotated weights
@@ -345,35 +453,53 @@ def main():
         router = dict(kernel="router_kernel", avg_us=round(r_us, 3), bytes_per_launch=r_bytes,
                       hbm_gbs=round(r_bytes / (r_us * 1e-6) / 1e9, 1),
                       fp32_fma_tflops=round(r_flops / (r_us * 1e-6) / 1e12, 2))
+    del g_step, g_rem, g_k
+    return dict(wl=wl, T=T, hot=hot, L=L, seed=seed, sets=sets, steps=steps, warmup=warmup,
+                ms_step=ms_step, tok_s=tok_s, step_pct=step_pct, cycles=len(cycle_ms),
+                cycle=cycle, step_bytes=step_bytes, eager_ms=eager_ms, roof=roof, router=router,
+                mean_touched=mean_touched)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill)
 
+def summary(r):
+    """One configuration's entry in the line's "configs" object."""
+    out = {"rows": r["T"], "ms_per_step": round(r["ms_step"], 5),
+           "tokens_per_s": round(r["tok_s"], 1),
+           "step_hbm_gbs": round(r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9, 1),
+           "experts_touched_mean": round(r["mean_touched"], 2),
+           "roofline": r["roof"]}
+    if r["step_pct"] is not None:
+        out["ms_per_step_p10_p50_p90"] = r["step_pct"]
+        out["cycles"] = r["cycles"]
+    return out
+
+
+def line_of(r, args, cpu):
+    L, T, wl = r["L"], r["T"], r["wl"]
     line = {
-        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": round(r["tok_s"], 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": r["steps"], "warmup": r["warmup"], "ms_per_step": round(r["ms_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4(e2m1+e8m0) x int8 -> exact block dots, f32 accumulate",
         "data": "synthetic (seeded counter-hash weights, N(0,1) activations/logits)",
         "config": {"workload": f"{wl}: E256 top-6 + shared, d_model 4096, d_ff {L.d_ff}"
                                + (" (TP8 shard of d_ff 2048)" if args.shard else "") + ", "
-                               f"{T} token(s)/step, {sets} rotated layer sets"
-                               + (", hot-16 +2.0 bias" if hot else "")
+                               f"{T} token(s)/step, {r['sets']} rotated layer sets"
+                               + (", hot-16 +2.0 bias" if r["hot"] else "")
                                + (", router projection in the step (BF16 weights)"
                                   if args.router else ""),
-                   "rows": T, "layer_sets": sets, "seed": seed},
-        "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "eager_ms_per_step": round(eager_ms, 4),
-        # per-step ms of each replayed rotation cycle: p10, median, p90
-        "ms_per_step_p10_p50_p90": step_pct, "cycles": len(cycle_ms), "steps_per_cycle": cycle,
-        "step_bytes": int(step_bytes),
-        "roofline": roof,
+                   "rows": T, "layer_sets": r["sets"], "seed": r["seed"]},
+        "step_hbm_gbs": round(r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9, 1),
+        "eager_ms_per_step": round(r["eager_ms"], 4),
+        "cycles": r["cycles"], "steps_per_cycle": r["cycle"],
+        "step_bytes": int(r["step_bytes"]),
+        "roofline": r["roof"],
         "cpu_baseline": cpu,
     }
-    if router is not None:
-        line["router"] = router
-    emit(line, args)
+    if r["step_pct"] is not None:   # per-step ms of the replayed cycles: p10, median, p90
+        line["ms_per_step_p10_p50_p90"] = r["step_pct"]
+    if r["router"] is not None:
+        line["router"] = r["router"]
+    return line
 
 
 EAGER = False
@@ -405,14 +531,39 @@ def capture(torch, fn):
     return g
 
 
-def cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill):
+def host_info():
+    """What the CPU figures ran on: logical CPUs (all, and this process's
+    affinity), the CPU model, OMP_NUM_THREADS, and the threads the oracle
+    uses: every CPU of the affinity mask, capped by OMP_NUM_THREADS when that
+    is set (the host's share for one GPU)."""
+    aff = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = aff
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(aff, int(omp))
+    return {"nproc": os.cpu_count(), "affinity_cpus": aff, "cpu_model": model,
+            "OMP_NUM_THREADS": omp}, threads
+
+
+def cpu_baseline(env, args, L, seed, T, prefill):
     """The oracle, as it stands, on a bounded sample of the same workload: S
-    fresh rows with the workload's distributions (about 10-15 s of CPU work
-    on 16 threads), quantised, routed, grouped and run through the FFN."""
+    fresh rows with the workload's distributions (about 10-20 s of CPU work),
+    quantised, routed, grouped and run through the FFN, on the host's threads;
+    then the same steps on one thread over the first rows of the sample."""
     import oracle
 
+    synth, torch, dev = env.synth, env.torch, env.dev
+    info, threads = host_info()
     S = args.cpu_sample or 256
-    threads = min(16, len(os.sched_getaffinity(0)))
     x = synth.activations(seed, 1000 + T, S, L.d_model)
     lg = synth.router_logits(seed, 1000 + T, S, L.n_experts, hot_bias=2.0 if args.hot else 0.0)
     q, qs = oracle.quant_q8(x)
@@ -421,36 +572,35 @@ def cpu_baseline(args, L, seed, T, m, synth, np, torch, dev, prefill):
     ex = {e: {k: v.cpu().numpy() for k, v in
               synth.expert_weights(seed, 0, e, L.d_model, L.d_ff, device=dev).items()}
           for e in sorted(need)}
-    oracle.set_threads(threads)
-    t0 = time.perf_counter()
-    qo, qso = oracle.quant_q8(x)
-    ido, wo = oracle.route(lg, L.top_k)
-    oracle.group(ido, L.n_experts)
-    oracle.ffn(ex, L.n_experts, L.top_k, True, qo, qso, ido, wo)
-    dt = time.perf_counter() - t0
-    # the same steps on one thread, over the first S1 rows of the sample
-    S1 = min(S, 8)
-    oracle.set_threads(1)
-    t1 = time.perf_counter()
-    qo, qso = oracle.quant_q8(x[:S1])
-    ido, wo = oracle.route(lg[:S1], L.top_k)
-    oracle.group(ido, L.n_experts)
-    oracle.ffn(ex, L.n_experts, L.top_k, True, qo, qso, ido, wo)
-    dt1 = time.perf_counter() - t1
+
+    def run(rows, nthreads):
+        oracle.set_threads(nthreads)
+        t0 = time.perf_counter()
+        qo, qso = oracle.quant_q8(x[:rows])
+        ido, wo = oracle.route(lg[:rows], L.top_k)
+        oracle.group(ido, L.n_experts)
+        oracle.ffn(ex, L.n_experts, L.top_k, True, qo, qso, ido, wo)
+        return time.perf_counter() - t0
+
+    dt = run(S, threads)
+    S1 = min(S, 16)
+    dt1 = run(S1, 1)
     oracle.set_threads(threads)
     return {"value": round(S / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{S} rows drawn like the workload's (layer set 0, {len(need)} experts): "
                       f"quant, route, group, FFN in fp64; {dt:.1f}s wall on {threads} threads",
             "value_1_thread": round(S1 / dt1, 4),
-            "sample_1_thread": f"the first {S1} of those rows on 1 thread, {dt1:.1f}s wall"}
+            "sample_1_thread": f"the first {S1} of those rows on 1 thread, {dt1:.1f}s wall",
+            **info}
 
 
-def bench_matvec(args, m, synth, np, torch, dev):
+def bench_matvec(env, args, K, steps, warmup, with_cpu):
+    m, synth, torch, dev = env.m, env.synth, env.torch, env.dev
     c = synth.MATVEC
-    N, D, K = c["n_out"], c["d_in"], (args.rows or 4)
+    N, D = c["n_out"], c["d_in"]
     copies = args.sets or c["copies"]
-    steps = args.steps or 2000
-    warmup = args.warmup if args.warmup is not None else 100
+    steps = steps or 2000
+    warmup = warmup if warmup is not None else 100
     packs = []
     for i in range(copies):
         codes, scales = synth.matrix_weights(c["seed"], i, N, D, dev)
@@ -478,37 +628,43 @@ def bench_matvec(args, m, synth, np, torch, dev):
     ev1.record()
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / steps
+    # algorithmic bytes: the packed matrix (codes + E8M0), K int8 rows and
+    # their scales in, K fp32 rows out
     nbytes = packs[0].numel() + K * (D + D // 8) + K * N * 4
     gbs = nbytes / (us * 1e-6) / 1e9
+    traffic, traffic_src = traffic_for(("matvec", K))
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         import oracle
-        threads = min(16, len(os.sched_getaffinity(0)))
+        info, threads = host_info()
         codes, scales = synth.matrix_weights(c["seed"], 0, N, D, dev)
         cn, sn = codes.cpu().numpy(), scales.cpu().numpy()
         xn = x.cpu().numpy()
         oracle.set_threads(threads)
-        reps, t0 = 0, time.perf_counter()
+        n_rep, t0 = 0, time.perf_counter()
         while time.perf_counter() - t0 < 5.0:
             qo, qso = oracle.quant_q8(xn)
             oracle.matvec(cn, sn, qo, qso)
-            reps += 1
+            n_rep += 1
         dt = time.perf_counter() - t0
-        cpu = {"value": round(reps * K / dt, 4), "unit": "rows/s", "cores": threads,
-               "kind": "oracle", "sample": f"{reps} full matvecs of {K} rows, {dt:.1f}s wall"}
-    line = {
+        cpu = {"value": round(n_rep * K / dt, 4), "unit": "rows/s", "cores": threads,
+               "kind": "oracle", "sample": f"{n_rep} full matvecs of {K} rows, {dt:.1f}s wall",
+               **info}
+    del g, g_rem, packs
+    torch.cuda.empty_cache()
+    return {
         "metric": METRIC, "value": round(K / (us * 1e-6), 1), "unit": "rows/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(us / 1e3, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4(e2m1+e8m0) x int8 -> exact block dots, f32 accumulate",
         "data": "synthetic", "config": {"workload": f"matvec {N}x{D}, {K} rows, {copies} copies",
                                         "rows": K},
-        "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic_for(("matvec", K)),
-                         kernel="stream_kernel<matvec>", avg_us=round(us, 3)),
+        "roofline": dict(kernel="stream_kernel<matvec>", avg_us=round(us, 3), bound="hbm",
+                         achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), bytes_per_launch=int(nbytes),
+                         traffic=traffic, traffic_src=traffic_src),
         "cpu_baseline": cpu,
     }
-    emit(line, args)
 
 
 def bench_copy(args, torch, dev):

@@ -29,13 +29,28 @@ def test_world_size_above_one_exits():
 
 def test_traffic_reported_only_for_counted_sources(monkeypatch):
     # with the device code the counters were taken on, every counted workload
-    # reports bytes; any other key, or changed sources, report None
+    # reports bytes and names its source; any other key, or changed sources,
+    # report None with the reason
     if bench.kernel_sources_hash() != bench.TRAFFIC_SRC:
-        assert all(bench.traffic_for(k) is None for k in bench.TRAFFIC)
+        for k in bench.TRAFFIC:
+            b, why = bench.traffic_for(k)
+            assert b is None and why.startswith("stale")
         pytest.skip("device code changed since the counters were taken (traffic reads null)")
     for key in bench.TRAFFIC:
-        assert bench.traffic_for(key) > 0
-    assert bench.traffic_for(("decode-batch", 4)) is None
-    assert bench.traffic_for(None) is None
+        b, src = bench.traffic_for(key)
+        assert b > 0 and src == bench.TRAFFIC_DOC
+    assert bench.traffic_for(("decode-batch", 4))[0] is None
+    assert bench.traffic_for(None)[0] is None
     monkeypatch.setattr(bench, "TRAFFIC_SRC", "0" * 16)
-    assert all(bench.traffic_for(k) is None for k in bench.TRAFFIC)
+    assert all(bench.traffic_for(k)[0] is None for k in bench.TRAFFIC)
+
+
+def test_host_info_threads_follow_affinity_and_omp(monkeypatch):
+    aff = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    info, threads = bench.host_info()
+    assert threads == aff and info["affinity_cpus"] == aff and info["nproc"] == os.cpu_count()
+    assert info["OMP_NUM_THREADS"] is None
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    info, threads = bench.host_info()
+    assert threads == 1 and info["OMP_NUM_THREADS"] == "1"
