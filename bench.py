@@ -58,14 +58,14 @@ GEMM_SIMDS = 1024
 # (hash below, over the device code in csrc/): after any change to it the
 # benchmark reports traffic as null.
 TRAFFIC_DOC = "profiles/hbm_traffic_counters.md (moe_counters under rocprofv3 --pmc, offline)"
-TRAFFIC_SRC = "2d236613a72e4058"
+TRAFFIC_SRC = "ca79141f1674536f"
 TRAFFIC = {  # (workload, rows[, variant]): (read bytes, written bytes)
-    ("decode", 1): (2 * 30777.0 * 1024, 48.6 * 1024),
-    ("decode-batch", 16): (2 * 349734.1 * 1024, 687.7 * 1024),
-    ("decode-batch", 16, "hot"): (2 * 171023.99 * 1024, 676.9 * 1024),
-    ("prefill", 4096): (2 * 1346555.0 * 1024, 146336.0 * 1024),
-    ("prefill", 512): (2 * 1179207.25 * 1024, 15348.6 * 1024),
-    ("matvec", 5): (2 * 15404.8 * 1024, 280.0 * 1024),
+    ("decode", 1): (2 * 30787.9 * 1024, 48.6 * 1024),
+    ("decode-batch", 16): (2 * 349801.5 * 1024, 678.4 * 1024),
+    ("decode-batch", 16, "hot"): (2 * 171096.7 * 1024, 672.9 * 1024),
+    ("prefill", 4096): (2 * 1435971.7 * 1024, 139264.1 * 1024),
+    ("prefill", 512): (2 * 1209634.7 * 1024, 17499.3 * 1024),
+    ("matvec", 5): (2 * 15414.9 * 1024, 280.0 * 1024),
 }
 
 
