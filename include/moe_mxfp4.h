@@ -229,15 +229,19 @@ typedef struct moe_layer {
  *                                      (d_model or 2*d_ff not a multiple of
  *                                      256), store each int8 code as the exact
  *                                      bf16 value.  Prefill calls on the GEMM
- *                                      store each run of 32 codes as four E2M1
- *                                      digit planes of 16 bytes, plane 0
- *                                      first: code = d0 + 4 d1 + 16 d2 + 64 d3
- *                                      with every d in {-2..2}, plane s holding
- *                                      d_s of the 32 codes (element 2i in the
- *                                      low nibble of byte i).
+ *                                      store each run of 32 codes as two E3M2
+ *                                      (OCP FP6, bias 3) digit planes in 48
+ *                                      bytes, in the first 1.5*d_ff bytes of
+ *                                      the row: code = d0 + 16 d1 with d0 in
+ *                                      [-8, 7] and d1 in [-8, 8]; plane s is a
+ *                                      192-bit little-endian word holding d_s
+ *                                      of element e in bits 6e..6e+5; the 48
+ *                                      bytes are plane 0 bytes 0-15, plane 1
+ *                                      bytes 0-15, plane 0 bytes 16-23, plane
+ *                                      1 bytes 16-23.
  *   hidden scales f32  [A'][d_ff/32]
  *   partials      f32  [A'][d_model]  per-slot down projections
- *   activations   [rows][2*d_model bytes]  prefill GEMM: each token's int8
+ *   activations   [rows][1.5*d_model bytes]  prefill GEMM: each token's int8
  *                                      codes as digit planes, as above
  * Hidden row of routed assignment at sorted position p is p; the shared
  * expert's row for token t is rows*top_k + t.  Partials row of routed

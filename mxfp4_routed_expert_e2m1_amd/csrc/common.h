@@ -133,24 +133,27 @@ __device__ inline f32x4 mfma_block(bf16x8 a, bf16x8 b) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero, 0, 0, 0);
 }
 
-// D[16][16] = A[16][128] * B[128][16] on the scaled FP4 matrix core, zero C:
-// A and B are E2M1 codes (lane l supplies row / column l%16 and the 32
-// elements of K slot l/16 in the low 4 dwords, element 2i in the low nibble
-// of byte i), each (row or column, K slot) scaled by 2^(byte - 127) of its
-// lane's scale register -- byte J of sa, byte 0 of sb.  D as for mfma_block.
+// D[32][32] = A[32][64] * B[64][32] on gfx950's scaled matrix core, zero C,
+// with E2M1 codes in A and E3M2 codes in B.  Lane l supplies A row l%32 and
+// B column l%32, each with the 32 elements of K slot l/32: A as 16 bytes
+// (element 2i in the low nibble of byte i, dwords 0-3), B as 24 bytes
+// (element e in bits 6e..6e+5 of dwords 0-5).  Each (row or column, K slot)
+// is scaled by 2^(byte - 127) of its lane's scale register: byte J of sa,
+// byte 0 of sb.  Lane l receives column l%32 of D, element i at row
+// 8 (i/4) + 4 (l/32) + i%4.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <int J>
-__device__ inline f32x4 mfma_fp4_blk(v8i32 a, v8i32 b, int sa, int sb) {
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, J, sa, 0, sb);
+__device__ inline f32x16 mfma_fp4_bf6_32(v8i32 a, v8i32 b, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, f32x16{}, 4, 3, J, sa, 0, sb);
 }
 // j: a compile-time constant after unrolling (the byte select is part of the
 // instruction)
-__device__ __forceinline__ f32x4 mfma_fp4_block(v8i32 a, v8i32 b, int j, int sa, int sb) {
+__device__ __forceinline__ f32x16 mfma_fp4_bf6_block(v8i32 a, v8i32 b, int j, int sa, int sb) {
   switch (j) {
-    case 0: return mfma_fp4_blk<0>(a, b, sa, sb);
-    case 1: return mfma_fp4_blk<1>(a, b, sa, sb);
-    case 2: return mfma_fp4_blk<2>(a, b, sa, sb);
-    default: return mfma_fp4_blk<3>(a, b, sa, sb);
+    case 0: return mfma_fp4_bf6_32<0>(a, b, sa, sb);
+    case 1: return mfma_fp4_bf6_32<1>(a, b, sa, sb);
+    case 2: return mfma_fp4_bf6_32<2>(a, b, sa, sb);
+    default: return mfma_fp4_bf6_32<3>(a, b, sa, sb);
   }
 }
 

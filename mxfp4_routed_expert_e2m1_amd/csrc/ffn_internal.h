@@ -10,11 +10,12 @@ namespace moe {
 // a shared expert is present) hidden rows:
 //   hidden        [A'][2 d_ff bytes]   requantised intermediate codes: exact
 //                                      bf16 values (decode; prefill off the
-//                                      GEMM path), or E2M1 digit planes
-//                                      [d_ff/32][4][16 B] (prefill GEMM path)
+//                                      GEMM path), or E3M2 digit planes
+//                                      [d_ff/32][48 B] in the first 1.5 d_ff
+//                                      bytes of the row (prefill GEMM path)
 //   hidden_scales f32  [A'][d_ff/32]
 //   partials      f32  [A'][d_model]   per-slot down projections
-//   act           [rows][2 d_model bytes]  prefill GEMM path: each token's
+//   act           [rows][1.5 d_model bytes]  prefill GEMM path: each token's
 //                                      activation codes as digit planes
 struct WsLayout {
   size_t hidden, hidden_scales, partials, act, total;
@@ -30,7 +31,7 @@ inline WsLayout ws_layout(const moe_layer_t* L, int rows) {
   w.hidden_scales = w.hidden + round256(hrows * L->d_ff * 2);
   w.partials = w.hidden_scales + round256(hrows * (L->d_ff / kBlock) * 4);
   w.act = w.partials + round256(hrows * L->d_model * 4);
-  w.total = w.act + round256((size_t)rows * L->d_model * 2);
+  w.total = w.act + round256((size_t)rows * (L->d_model / kBlock) * 48);
   return w;
 }
 

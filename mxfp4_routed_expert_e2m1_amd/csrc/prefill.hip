@@ -1,5 +1,5 @@
-// prefill.hip -- grouped GEMM for prefill chunks on gfx950's scaled FP4
-// matrix core.
+// prefill.hip -- grouped GEMM for prefill chunks on gfx950's scaled matrix
+// core.
 //
 // The gfx90a report (§7.1) moves prefill from a per-assignment dot path to
 // INT8 MFMA routed gate and down kernels with FP4 unpack reused across rows,
@@ -10,57 +10,59 @@
 // per 128 tokens.  The contraction is exact on the matrix core without any
 // unpacking of the weights:
 //
-//   * gfx950's scaled 16x16x128 FP4 instruction takes the packed E2M1 codes
+//   * gfx950's scaled 32x32x64 instruction takes the packed E2M1 weight codes
 //     as they are and applies one E8M0 byte per row and 32-element K slot
 //     (picked from a register by the instruction's byte select), so the
 //     weights go from LDS to the matrix core untouched.
-//   * An int8 activation block has no exact FP4 form, but its code q in
-//     [-127, 127] splits into balanced base-4 digits, q = d0 + 4 d1 + 16 d2 +
-//     64 d3 with every d in {-2..2}, each an exact E2M1 value.  The four
-//     digit planes of one 32-element block fill the instruction's four K
-//     slots, with B scales 2^0, 2^2, 2^4, 2^6, against the same weight block
-//     in every slot: one instruction gives the exact integer block dot times
-//     2^(u-127) (every product and partial sum is a multiple of half an E2M1
-//     step below 2^15 of them, exact in fp32) -- the same fp32 value as the
-//     decode kernels' bf16 route.  The activation scale follows with one fp32
-//     FMA per output and block.
+//   * An int8 activation block has no exact 4-bit form, but its code q in
+//     [-127, 127] splits into two balanced base-16 digits, q = d0 + 16 d1
+//     with d0 in [-8, 7] and d1 in [-8, 8], and every integer in [-8, 8] is
+//     an exact E3M2 (6-bit) value.  The two digit planes of one 32-element
+//     block fill the instruction's two K slots, with B scales 2^0 and 2^4,
+//     against the same weight block in both: one instruction gives the exact
+//     integer block dot times 2^(u-127) for a 32 x 32 output tile (every
+//     product and partial sum is a multiple of half an E2M1 step below 2^16
+//     of them, exact in fp32) -- the same fp32 value as the decode kernels'
+//     bf16 route.  The activation scale follows with one fp32 FMA per output
+//     and block.
 //   * The sums run as in every decode kernel: runs of 16 blocks (4 chunks),
 //     each folded from zero in block order, added in order -- so a prefill
 //     row has the bits of the same row decoded alone (exact rows).
 //
 // Data movement:
 //   * A prep kernel turns each token's int8 codes into digit planes once
-//     (2 bytes per code); the gate/up GEMM reads the planes of its tile's
+//     (1.5 bytes per code); the gate/up GEMM reads the planes of its tile's
 //     tokens through the sorted assignment list.  Its epilogue (SwiGLU +
 //     group-32 requant) writes the hidden codes as digit planes too, in tile
 //     order, which the down GEMM reads directly.
 //   * Weights, scales, digit planes and activation scales stream through a
 //     3-stage LDS ring filled by direct global->LDS loads (no registers).
-//   * 16 waves (128-row tiles; 8 for 32-row tiles): 4 row quarters (4 row
-//     groups each) x 4 token parts (token groups tp, tp+4), a 64 x 32 output
-//     block per wave.
+//   * Waves: 4 row parts (64 weight rows, two 32-row tiles) x 2 token parts
+//     (128-row tiles: token tiles tp, tp+2 of 32 tokens; 8 waves), or x 1
+//     (32-row tiles: 4 waves, two workgroups per CU) -- a 64 x 64 output
+//     block per wave at most.
 //   * Block ids are remapped so the workgroups that share a token tile run on
 //     the same XCD and share its L2.
 #include "ffn_internal.h"
 
 namespace moe {
 
-// Token rows per tile: 128 (8 groups of 16), or 32 when experts hold few rows
-// each: a short tile's stage takes half the LDS, so two workgroups share a
-// CU and one streams while the other starts (finds its tile, waits for its
+// Token rows per tile: 128 (4 tiles of 32 tokens), or 32 when experts hold
+// few rows each: a short tile's stage takes less LDS, so two workgroups share
+// a CU and one streams while the other starts (finds its tile, waits for its
 // first chunk).
 constexpr int kBMFull = 128;
 constexpr int kBMShort = 32;
 constexpr int kBNGroups = 16;  // 16-row weight groups per workgroup (256 rows)
 constexpr int kRing = 3;       // LDS stages (chunks in flight ahead: kRing - 1)
 constexpr int kRunChunks = 4;  // chunks per exact-rows run (16 blocks)
-// Waves per workgroup: 4 row quarters x TH token parts, 4 waves per SIMD
-// (<= 128 VGPRs each) so latencies of one wave hide behind the others.
-// 128-row tiles: 16 waves, each 4 row groups x 2 of the 8 token groups;
-// 32-row tiles: 8 waves, each 4 row groups x 1 of the 2 (two workgroups
-// share a CU).
-template <int BM> constexpr int gemm_waves() { return 8; }
-template <int BM> constexpr int gemm_th() { return gemm_waves<BM>() / 4; }
+constexpr int kDigitBlock = 48;   // bytes of one 32-code block as two E3M2 digit planes
+constexpr int kDigitChunk = 4 * kDigitBlock;  // one 128-element K chunk
+// Waves per workgroup: 4 row parts x TP token parts, two waves per SIMD.
+template <int BM> constexpr int gemm_waves() { return BM == kBMFull ? 8 : 4; }
+template <int BM> constexpr int gemm_tp() { return gemm_waves<BM>() / 4; }
+// 32-token tiles per wave
+template <int BM> constexpr int gemm_qt() { return BM / 32 / gemm_tp<BM>(); }
 
 enum GemmPass : int { GEMM_GATEUP = 0, GEMM_DOWN = 1 };
 
@@ -74,7 +76,7 @@ struct GemmArgs {
   const int32_t* sorted;
   int n_experts, top_k, has_shared, rows;
   const uint8_t* xp;  // B digit planes: tokens (gate/up) or hidden rows (down)
-  int64_t ld_xp;      // bytes per row of planes (2 * K)
+  int64_t ld_xp;      // bytes per row of planes (>= 1.5 K)
   const float* xs;    // B scales: qs (gate/up) or hidden scales (down)
   int64_t ld_xs;
   int n_items;  // tiles bound x weight-row blocks
@@ -88,13 +90,17 @@ struct GemmArgs {
 
 // One LDS stage = one 128-element K chunk of the workgroup's operands, each
 // piece in the order its reader uses:
+//   b: per 16-token group, the 16-byte pieces of the chunk's digit planes,
+//   [piece][token]; block j of a token is pieces 3j (plane 0, bytes 0-15),
+//   3j+1 (plane 1, bytes 0-15) and 3j+2 (bytes 16-23 of plane 0, then of
+//   plane 1) -- the token's 192 bytes of the chunk in order.
 template <int BM>
 struct Stage {
   static constexpr int NTG = BM / 16;              // token groups
   static constexpr int NTD = NTG < 4 ? 4 : NTG;    // scale rows, whole loads of 4 groups
   u32x4 a[kBNGroups][64];  // packed tiles, lane 16 j + r: row r's block j   16 KiB
   uint32_t s[kBNGroups][16];  // E8M0 bytes of the chunk's 4 blocks, per row  1 KiB
-  u32x4 b[NTG][4][64];     // digit planes, [token group][block][16 s + col]  BM/4 KiB
+  u32x4 b[NTG][12][16];    // digit planes (see above)                       3 BM/16 KiB
   f32x4 d[NTD][16];        // activation scales of the chunk's 4 blocks, per column
 };
 
@@ -135,68 +141,109 @@ __device__ inline void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Direct buffer -> LDS load: lane l writes `bytes` (4 or 16) at lds_base + l *
-// bytes from the resource at voff (per lane) + soff (uniform).  A resource
-// in scalar registers and one 32-bit lane offset cost fewer vector registers
-// than a 64-bit address per lane.
-__device__ inline void buf_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, int bytes,
-                                  uint32_t voff, uint32_t soff) {
-  if (bytes == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 16, voff, soff, 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 4, voff, soff, 0, 0);
+// Direct global -> LDS loads (no registers): lane l writes 16 (or 4) bytes
+// at lds_base + 16 l (4 l).  They are written as asm so that the compiler
+// does not see them as LDS stores: it cannot tell the ring's stages apart,
+// and would wait for every load in flight (the prefetched chunks too)
+// before the first LDS read of each chunk.  The ring orders them itself: a
+// stage is read only after each wave's vmcnt wait for its own loads of it
+// and a barrier, and refilled only after the barrier that follows its last
+// reads.  M0 carries the LDS address (one wait state before the load); no
+// other code in these kernels uses M0.
+__device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr)p; }
+// from the buffer resource r (scalar registers) at voff (per lane) + soff
+// (uniform): a resource and a 32-bit lane offset cost fewer vector registers
+// than a 64-bit address per lane
+__device__ inline void buf_to_lds16(u32x4 r, const void* lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds_base)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+__device__ inline void buf_to_lds4(u32x4 r, const void* lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds_base)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+// from a per-lane global address
+__device__ inline void glb_to_lds16(const void* src, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_addr(lds_base)), "v"(src) : "memory", "m0");
 }
 
 // ------------------------------------------------------------ digit planes
-// E2M1 code of a digit in {-2..2}: sign bit 3, |d| = 1 -> 0b010, 2 -> 0b100.
-__device__ inline uint32_t digit_code(int d) {
-  return (d < 0 ? 8u : 0u) | ((uint32_t)(d < 0 ? -d : d) << 1);
+// E3M2 code (sign bit 5, 3 exponent bits with bias 3, 2 mantissa bits) of an
+// integer d in [-8, 8]: the magnitude codes of 0..8 are 7-bit fields of one
+// constant.
+__device__ inline uint32_t bf6_digit(int d) {
+  constexpr uint64_t kMag = (0x0CULL << 7) | (0x10ULL << 14) | (0x12ULL << 21) |
+                            (0x14ULL << 28) | (0x15ULL << 35) | (0x16ULL << 42) |
+                            (0x17ULL << 49) | (0x18ULL << 56);
+  const int a = d < 0 ? -d : d;
+  return (d < 0 ? 0x20u : 0u) | (uint32_t)((kMag >> (7 * a)) & 0x7Fu);
 }
-// The four balanced base-4 digits of q in [-127, 127] as E2M1 codes:
-// d_s = ((x + 2) mod 4) - 2, x <- (x - d_s) / 4, the last digit what is left.
-__device__ inline void q8_digit_codes(int q, uint32_t (&c)[4]) {
-  int x = q;
-#pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    const int dg = ((x + 2) & 3) - 2;
-    c[s] = digit_code(dg);
-    x = (x - dg) >> 2;
-  }
-  c[3] = digit_code(x);
+// The two balanced base-16 digits of q in [-128, 127] as E3M2 codes:
+// d0 = ((q + 8) mod 16) - 8 in [-8, 7], d1 = (q - d0) / 16 in [-8, 8].
+__device__ inline void q8_bf6_digits(int q, uint32_t& c0, uint32_t& c1) {
+  const int d0 = ((q + 8) & 15) - 8;
+  c0 = bf6_digit(d0);
+  c1 = bf6_digit((q - d0) >> 4);
+}
+// 24-bit run of 4 codes (element i at bits 6i)
+__device__ inline uint32_t bf6_run4(const uint32_t (&c)[4]) {
+  return c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18);
+}
+// One plane of 32 codes as 6 dwords from its eight 4-code runs (run m at bit
+// 24 m).
+__device__ inline void bf6_plane(const uint32_t (&t)[8], uint32_t (&w)[6]) {
+  w[0] = t[0] | (t[1] << 24);
+  w[1] = (t[1] >> 8) | (t[2] << 16);
+  w[2] = (t[2] >> 16) | (t[3] << 8);
+  w[3] = t[4] | (t[5] << 24);
+  w[4] = (t[5] >> 8) | (t[6] << 16);
+  w[5] = (t[6] >> 16) | (t[7] << 8);
+}
+// A block's 48 bytes from its two planes: plane 0 bytes 0-15, plane 1 bytes
+// 0-15, plane 0 bytes 16-23, plane 1 bytes 16-23.
+__device__ inline void bf6_store_block(uint8_t* dst, const uint32_t (&p0)[6],
+                                       const uint32_t (&p1)[6]) {
+  *(u32x4*)dst = u32x4{p0[0], p0[1], p0[2], p0[3]};
+  *(u32x4*)(dst + 16) = u32x4{p1[0], p1[1], p1[2], p1[3]};
+  *(u32x4*)(dst + 32) = u32x4{p0[4], p0[5], p1[4], p1[5]};
 }
 
-// One thread per 8 codes of a token row: plane s of block b holds the 32
-// digit-s codes of the block (16 bytes, element 2i in the low nibble of byte
-// i); a row is [K/32 blocks][4 planes][16 B].  Threads 4b..4b+3 of a row
-// write the 64 bytes of block b.
+// One thread per 32-code block of a token row: reads the block's int8 codes
+// and writes its 48 bytes of digit planes; a row is [K/32 blocks][48 B].
 __global__ __launch_bounds__(256) void prep_digits_kernel(const int8_t* __restrict__ q,
                                                           int64_t ld_q, int rows, int d_model,
                                                           uint8_t* __restrict__ xp,
                                                           int64_t ld_xp) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int per_row = d_model / 8;
+  const int per_row = d_model / 32;
   if (i >= (int64_t)rows * per_row) return;
   const int t = (int)(i / per_row);
-  const int c8 = (int)(i % per_row);  // 8-element group: block c8 / 4, quarter c8 % 4
-  const u32x2 v = *(const u32x2*)(q + (int64_t)t * ld_q + (int64_t)c8 * 8);
-  uint32_t plane[4] = {0u, 0u, 0u, 0u};
+  const int b = (int)(i % per_row);
+  const u32x2* src = (const u32x2*)(q + (int64_t)t * ld_q + (int64_t)b * 32);
+  uint32_t r0[8], r1[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int code = (int)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-    uint32_t c[4];
-    q8_digit_codes(code, c);
+  for (int k = 0; k < 4; ++k) {
+    const u32x2 v = src[k];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) plane[s] |= c[s] << (4 * e);
+    for (int hw = 0; hw < 2; ++hw) {
+      uint32_t c0[4], c1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q8_bf6_digits((int)(int8_t)((v[hw] >> (8 * e)) & 0xFFu), c0[e], c1[e]);
+      r0[2 * k + hw] = bf6_run4(c0);
+      r1[2 * k + hw] = bf6_run4(c1);
+    }
   }
-  uint8_t* dst = xp + (int64_t)t * ld_xp + (int64_t)(c8 >> 2) * 64 + (c8 & 3) * 4;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) *(uint32_t*)(dst + 16 * s) = plane[s];
+  uint32_t p0[6], p1[6];
+  bf6_plane(r0, p0);
+  bf6_plane(r1, p1);
+  bf6_store_block(xp + (int64_t)t * ld_xp + (int64_t)b * kDigitBlock, p0, p1);
 }
 
 // ------------------------------------------------------------------- GEMM
 // Everything a workgroup knows about its item once the tile is found.
 struct GemmCtx {
-  __amdgpu_buffer_rsrc_t blob;  // the expert's packed matrix (tiles, then E8M0 bytes)
+  u32x4 blob;  // buffer resource of the expert's packed matrix (tiles, then E8M0 bytes)
   int prb;       // first packed row group of the workgroup
   int64_t row0;  // first hidden row of the tile (A + start for the shared expert)
   Tile t;
@@ -216,19 +263,32 @@ __device__ inline int gemm_brow(const GemmArgs& p, const GemmCtx& c, int r) {
 }
 
 // The loads of one K chunk, spread over the waves: the 16 weight tiles
-// (16 / W per wave), the B digit-plane loads (one per token group and block:
-// NTG * 4 / W per wave, all of them in token group (wave * that) / 4), the
-// E8M0 bytes (waves 0-3, 4 row groups each) and the activation scales (waves
-// 4 .. 4 + NTD/4 - 1, 4 token groups each).
+// (16 / W per wave), the B digit-plane loads (three per token group, each 4
+// pieces x 16 tokens; wave w takes loads [w NB / W, (w + 1) NB / W), all in
+// one token group), the E8M0 bytes (waves 0-3, 4 row groups each) and the
+// activation scales (the last NTD/4 waves, 4 token groups each).
 template <int BM> constexpr int gemm_a_per_wave() { return kBNGroups / gemm_waves<BM>(); }
-template <int BM> constexpr int gemm_b_per_wave() { return Stage<BM>::NTG * 4 / gemm_waves<BM>(); }
-template <int BM> __device__ inline int gemm_b_tg(int wave) { return wave * gemm_b_per_wave<BM>() / 4; }
+template <int BM> constexpr int gemm_b_loads() { return Stage<BM>::NTG * 3; }
+template <int BM> constexpr int gemm_b_max() {
+  return (gemm_b_loads<BM>() + gemm_waves<BM>() - 1) / gemm_waves<BM>();
+}
+template <int BM> __device__ inline int gemm_b_first(int wave) {
+  return wave * gemm_b_loads<BM>() / gemm_waves<BM>();
+}
+template <int BM> __device__ inline int gemm_b_count(int wave) {
+  return gemm_b_first<BM>(wave + 1) - gemm_b_first<BM>(wave);
+}
+template <int BM> __device__ inline int gemm_b_tg(int wave) { return gemm_b_first<BM>(wave) / 3; }
+// index of the scale load of this wave (4 token groups from 4 * it), or -1
+template <int BM> __device__ inline int gemm_d_wave(int wave) {
+  constexpr int W = gemm_waves<BM>(), ND = Stage<BM>::NTD / 4;
+  return wave >= W - ND ? wave - (W - ND) : -1;
+}
 
 template <int BM>
 __device__ inline int gemm_loads_per_chunk(int wave, bool b_live) {
-  constexpr int NTD = Stage<BM>::NTD;
-  int n = gemm_a_per_wave<BM>() + (wave < 4 ? 1 : 0) + (wave >= 4 && wave < 4 + NTD / 4 ? 1 : 0);
-  if (b_live) n += gemm_b_per_wave<BM>();
+  int n = gemm_a_per_wave<BM>() + (wave < 4 ? 1 : 0) + (gemm_d_wave<BM>(wave) >= 0 ? 1 : 0);
+  if (b_live) n += gemm_b_count<BM>(wave);
   return n;
 }
 
@@ -236,55 +296,67 @@ template <int PASS, int BM>
 __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>& S, int kc,
                                   int wave, int lane, bool b_live) {
   const int n = lane & 15, g4 = lane >> 4;
-  constexpr int AW = gemm_a_per_wave<BM>(), BW = gemm_b_per_wave<BM>();
+  constexpr int AW = gemm_a_per_wave<BM>();
   const uint32_t slot = (uint32_t)chunk_slot(kc, p.kc_total);
 #pragma unroll
   for (int i = 0; i < AW; ++i) {
     const int rg = AW * wave + i;
-    buf_to_lds(c.blob, &S.a[rg][0], 16, (uint32_t)lane * 16u,
+    buf_to_lds16(c.blob, &S.a[rg][0], (uint32_t)lane * 16u,
                ((uint32_t)(c.prb + rg) * (uint32_t)p.kc_total + slot) * 1024u);
   }
   if (wave < 4) {  // E8M0 bytes of row groups 4 wave .. 4 wave + 3
-    buf_to_lds(c.blob, &S.s[4 * wave][0], 4,
+    buf_to_lds4(c.blob, &S.s[4 * wave][0],
                (uint32_t)g4 * (uint32_t)p.sc_total * 256u + (uint32_t)n * 16u,
                (uint32_t)p.nib_bytes +
                    ((uint32_t)(c.prb + 4 * wave) * (uint32_t)p.sc_total + (uint32_t)(kc >> 2)) * 256u +
                    (uint32_t)(kc & 3) * 4u);
-  } else if (wave < 4 + Stage<BM>::NTD / 4) {  // scales of token groups 4 q .. 4 q + 3
-    const int qd = wave - 4;
-    load_to_lds(p.xs + (int64_t)c.d_row * p.ld_xs + (int64_t)kc * 4, &S.d[4 * qd][0], 16);
   }
+  const int qd = gemm_d_wave<BM>(wave);
+  if (qd >= 0)  // scales of token groups 4 qd .. 4 qd + 3
+    glb_to_lds16(p.xs + (int64_t)c.d_row * p.ld_xs + (int64_t)kc * 4, &S.d[4 * qd][0]);
   if (b_live) {
-    const uint8_t* src = p.xp + (int64_t)c.b_row * p.ld_xp + (int64_t)kc * 256 + 16 * g4;
+    // load li: token group li / 3, pieces 4 (li % 3) .. + 3 of its 16 tokens
+    // (lane: piece 4 (li % 3) + lane / 16 of token lane % 16)
+    const uint8_t* src = p.xp + (int64_t)c.b_row * p.ld_xp + (int64_t)kc * kDigitChunk + 16 * g4;
+    const int b0 = gemm_b_first<BM>(wave), nb = gemm_b_count<BM>(wave);
 #pragma unroll
-    for (int i = 0; i < BW; ++i) {
-      const int li = BW * wave + i, tg = li >> 2, j = li & 3;
-      load_to_lds(src + 64 * j, &S.b[tg][j][0], 16);
+    for (int i = 0; i < gemm_b_max<BM>(); ++i) {
+      if (i < nb) {
+        const int li = b0 + i, tg = li / 3, part = li % 3;
+        glb_to_lds16(src + 64 * part, &S.b[tg][4 * part][0]);
+      }
     }
   }
 }
 
-// K loop + epilogue of one wave owning row groups prb+4*rq .. +3 and token
-// groups tp, tp+TH, .. (NQ of them live).  Branch-free inner loop.
+// K loop + epilogue of one wave: row tiles rt = 0, 1 (16-row groups
+// pr0 + 2 rt for rows 0-15 of the tile and pr0 + 2 rt + 1 for rows 16-31,
+// pr0 = prb + 4 rp) and its NQ live 32-token tiles tp, tp + TP.  Lane l
+// works on row / token l % 32 of a tile: 16-row group (or token group)
+// 2 x + hi, column n, hi = (l / 16) % 2; its K slot h = l / 32 carries digit
+// plane h.  Branch-free inner loop.
 template <int PASS, int NQ, int BM>
 __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring) {
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6), lane = tid & 63;
-  const int n = lane & 15, g4 = lane >> 4;
-  constexpr int TH = gemm_th<BM>();
-  const int rq = wave & 3, tp = wave >> 2;
+  const int n = lane & 15, hi = (lane >> 4) & 1, h = lane >> 5;
+  constexpr int TP = gemm_tp<BM>();
+  constexpr int NQ1 = NQ > 0 ? NQ : 1;
+  constexpr int NT = 2 * NQ;  // tiles per block
+  const int rp = wave & 3, tp = wave >> 2;
   const int nnt = (c.t.count + 15) >> 4;
+  auto tile_of = [&](int q) { return tp + TP * q; };  // token tile of slot q
   // token group this wave stages
   const bool b_live = gemm_b_tg<BM>(wave) < nnt;
   const int per_chunk = gemm_loads_per_chunk<BM>(wave, b_live);
-  // B scale of K slot g4 (digit plane g4 carries weight 4^g4)
-  const int sb = 127 + 2 * g4;
+  // B scale of K slot h (digit plane h carries weight 16^h)
+  const int sb = 127 + 4 * h;
 
-  f32x4 acc[4][NQ > 0 ? NQ : 1];
+  f32x16 acc[2][NQ1];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int q4 = 0; q4 < NQ; ++q4) acc[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NQ1; ++q) acc[rt][q] = f32x16{};
 
   const int KC = p.kc_total;
   // chunks 0 .. kRing-2 go out first; chunk kc + kRing - 1 after chunk kc lands
@@ -294,11 +366,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
   int kc = 0;
   // runs of kRunChunks chunks, each summed from zero and added in order
   for (int kr = 0; kr < KC; kr += kRunChunks) {
-    f32x4 run[4][NQ > 0 ? NQ : 1];
+    f32x16 run[2][NQ1];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int q4 = 0; q4 < NQ; ++q4) run[g][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < NQ1; ++q) run[rt][q] = f32x16{};
     const int kend = min(kr + kRunChunks, KC);
     for (; kc < kend; ++kc) {
       // chunk kc has landed when no more than the loads of the chunks issued
@@ -308,120 +380,151 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
       if (kc + kRing - 1 < KC)
         gemm_issue<PASS, BM>(p, c, ring[(kc + kRing - 1) % kRing], kc + kRing - 1, wave, lane,
                              b_live);
-      if constexpr (NQ > 0) {
+      if constexpr (NT > 0) {
         const Stage<BM>& S = ring[kc % kRing];
         const float* sd = (const float*)&S.d[0][0];  // [token group][column][block]
-        uint32_t sw[4];
+        uint32_t sw[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) sw[g] = S.s[4 * rq + g][n];
-        // operands of block j: A[g] (row n's block j of row group g, the same
-        // 16 bytes in all four K slots), B[q4] (digit planes), D[q4] (scale)
-        u32x4 A[2][4], B[2][NQ];
-        float D[2][NQ];
+        for (int rt = 0; rt < 2; ++rt) sw[rt] = S.s[4 * rp + 2 * rt + hi][n];
+        // operands of block j: A[rt] (this lane's row, block j: the same 16
+        // bytes in both K slots), BL/BH[q] (digit plane h of its token: bytes
+        // 0-15, 16-23), D[q] (the token's scale)
+        u32x4 A[2][2], BL[2][NQ1];
+        u32x2 BH[2][NQ1];
+        float D[2][NQ1];
         auto load = [&](int j, int slot) {
 #pragma unroll
-          for (int q4 = 0; q4 < NQ; ++q4) {
-            B[slot][q4] = S.b[tp + TH * q4][j][lane];
-            D[slot][q4] = sd[((tp + TH * q4) * 16 + n) * 4 + j];
+          for (int q = 0; q < NQ; ++q) {
+            const int tg = 2 * tile_of(q) + hi;
+            BL[slot][q] = S.b[tg][3 * j + h][n];
+            BH[slot][q] = ((const u32x2*)&S.b[tg][3 * j + 2][n])[h];
+            D[slot][q] = sd[(tg * 16 + n) * 4 + j];
           }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) A[slot][g] = S.a[4 * rq + g][16 * j + n];
+          for (int rt = 0; rt < 2; ++rt) A[slot][rt] = S.a[4 * rp + 2 * rt + hi][16 * j + n];
         };
         load(0, 0);
+        // the chunk's 4 x NT tile-blocks in order, u = NT j + t (tile t =
+        // (row tile t / NQ, token tile t % NQ)): tile-block u's instruction,
+        // then the scaling of tile-block u-1's value, so every FMA reads a
+        // result one instruction old.  Block j+1's operands
+        // are read right after block j's first instruction, into the slot of
+        // block j-1 (whose instructions are all out; the scale its last
+        // scaling needs is kept aside first): a block's reads have a whole
+        // block to land, and the wait before its first instruction covers no
+        // later reads.
+        f32x16 R[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int cur = j & 1;
-          if (j + 1 < 4) load(j + 1, cur ^ 1);  // next block's reads go out first
-          // row group g's products, then the scaling of row group g-1's:
-          // every FMA reads a result one row group old, never a fresh one
-          f32x4 R[2][NQ];
+        for (int u = 0; u <= 4 * NT; ++u) {
+          // the steps stay in this order (the scheduler would sink the
+          // reads next to their use and wait for them there)
+          __builtin_amdgcn_sched_barrier(0);
+          float dprev = 0.f;
+          if (u > 0) dprev = D[((u - 1) / NT) & 1][((u - 1) % NT) % NQ1];
+          if (u < 4 * NT) {
+            const int j = u / NT, t = u % NT, cur = j & 1;
+            const int rt = t / NQ1, q = t % NQ1;
+            const u32x4 a4 = A[cur][rt], bl = BL[cur][q];
+            const u32x2 bh = BH[cur][q];
+            const v8i32 av = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+            const v8i32 bv = {(int)bl[0], (int)bl[1], (int)bl[2], (int)bl[3],
+                              (int)bh[0], (int)bh[1], 0, 0};
+            R[u & 1] = mfma_fp4_bf6_block(av, bv, j, (int)sw[rt], sb);
+          }
+          // the scaling below reads the previous instruction's result: kept
+          // after this instruction, so the matrix core's latency is hidden
+          __builtin_amdgcn_sched_barrier(0);
+          if (u < 4 * NT && u % NT == 0 && u / NT + 1 < 4) load(u / NT + 1, (u / NT + 1) & 1);
+          if (u > 0) {
+            const int t = (u - 1) % NT;
+            const int rt = t / NQ1, q = t % NQ1;
 #pragma unroll
-          for (int g = 0; g <= 4; ++g) {
-            if (g < 4) {
-              const v8i32 av = {(int)A[cur][g][0], (int)A[cur][g][1], (int)A[cur][g][2],
-                                (int)A[cur][g][3], 0, 0, 0, 0};
-#pragma unroll
-              for (int q4 = 0; q4 < NQ; ++q4) {
-                const v8i32 bv = {(int)B[cur][q4][0], (int)B[cur][q4][1], (int)B[cur][q4][2],
-                                  (int)B[cur][q4][3], 0, 0, 0, 0};
-                R[g & 1][q4] = mfma_fp4_block(av, bv, j, (int)sw[g], sb);
-              }
-            }
-            if (g > 0) {
-#pragma unroll
-              for (int q4 = 0; q4 < NQ; ++q4)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  run[g - 1][q4][i] = fmaf(R[(g - 1) & 1][q4][i], D[cur][q4], run[g - 1][q4][i]);
-            }
+            for (int i = 0; i < 16; ++i)
+              run[rt][q][i] = fmaf(R[(u - 1) & 1][i], dprev, run[rt][q][i]);
           }
         }
       }
     }
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int q4 = 0; q4 < NQ; ++q4) acc[g][q4] += run[g][q4];
+      for (int q = 0; q < NQ1; ++q) acc[rt][q] += run[rt][q];
   }
 
-  if constexpr (NQ > 0) {
-    const int pr0 = c.prb + 4 * rq;
+  if constexpr (NT > 0) {
+    const int pr0 = c.prb + 4 * rp;
     if (PASS == GEMM_GATEUP) {
-      // rows pr0..pr0+3 = (gate j, up j, gate j+1, up j+1): 32 features from
-      // f0; this lane holds features f0 + 4 g4 + i and f0 + 16 + 4 g4 + i
+      // row tile rt = (gate, up) of hidden features f0 + 16 rt .. + 15; a
+      // lane holds features f0 + 16 rt + 8 a + 4 h + b (element 4 a + b of
+      // the gate rows, 8 + 4 a + b of the up rows), lane l ^ 32 the other 16
+      // of the 32 that share one requant scale.  Element e sits in 4-code
+      // run e / 4 = 2 (2 rt + a) + h of its plane; a lane builds its runs of
+      // both planes and writes plane h, taking the other runs of plane h
+      // from lane l ^ 32.
       const int f0 = pr0 * 8;
 #pragma unroll
-      for (int q4 = 0; q4 < NQ; ++q4) {
-        const int nt = tp + TH * q4;
-        float hv[8];
+      for (int q = 0; q < NQ; ++q) {
+        float hv[2][8];
         float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hv[i] = mid_round(swiglu(acc[0][q4][i], acc[1][q4][i]), p.bf16_mid);
-          hv[4 + i] = mid_round(swiglu(acc[2][q4][i], acc[3][q4][i]), p.bf16_mid);
-        }
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(hv[i]));
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
+          for (int i = 0; i < 8; ++i) {
+            hv[rt][i] = mid_round(swiglu(acc[rt][q][i], acc[rt][q][8 + i]), p.bf16_mid);
+            m = fmaxf(m, fabsf(hv[rt][i]));
+          }
         m = fmaxf(m, __shfl_xor(m, 32, 64));
         const float d = m / 127.0f;
-        const int col = nt * 16 + n;
+        // runs 2 k + h (k = 2 rt + a) of both planes
+        uint32_t r0[4], r1[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t c0[4], c1[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            q8_bf6_digits((int)q8_code(hv[k >> 1][4 * (k & 1) + b], d), c0[b], c1[b]);
+          r0[k] = bf6_run4(c0);
+          r1[k] = bf6_run4(c1);
+        }
+        uint32_t t8[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t own = h ? r1[k] : r0[k];
+          const uint32_t got = (uint32_t)__shfl_xor((int)(h ? r0[k] : r1[k]), 32, 64);
+          t8[2 * k] = h ? got : own;
+          t8[2 * k + 1] = h ? own : got;
+        }
+        uint32_t w6[6];
+        bf6_plane(t8, w6);
+        const int col = 32 * tile_of(q) + 16 * hi + n;
         if (col < c.t.count) {
-          // the 4 digit planes of this lane's 8 codes: elements 4 g4 .. +3
-          // (bytes 2 g4, 2 g4 + 1) and 16 + 4 g4 .. +3 (bytes 8 + 2 g4, ..)
-          uint32_t half[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            uint32_t cd[4];
-            q8_digit_codes((int)q8_code(hv[e], d), cd);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) half[e >> 2][s] |= cd[s] << (4 * (e & 3));
-          }
-          uint8_t* hrow = p.h + (c.row0 + col) * p.ld_h + (int64_t)(f0 >> 5) * 64 + 2 * g4;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            *(uint16_t*)(hrow + 16 * s) = (uint16_t)half[0][s];
-            *(uint16_t*)(hrow + 16 * s + 8) = (uint16_t)half[1][s];
-          }
-          if (g4 == 0) p.hs[(c.row0 + col) * p.ld_hs + (f0 >> 5)] = d;
+          uint8_t* hrow = p.h + (c.row0 + col) * p.ld_h + (int64_t)(f0 >> 5) * kDigitBlock;
+          *(u32x4*)(hrow + 16 * h) = u32x4{w6[0], w6[1], w6[2], w6[3]};
+          *(u32x2*)(hrow + 32 + 8 * h) = u32x2{w6[4], w6[5]};
+          if (h == 0) p.hs[(c.row0 + col) * p.ld_hs + (f0 >> 5)] = d;
         }
       }
     } else {
+      // rows pr0 * 16 + 32 rt + 8 a + 4 h + b: element 4 a + b of row tile rt
 #pragma unroll
-      for (int q4 = 0; q4 < NQ; ++q4) {
-        const int col = (tp + TH * q4) * 16 + n;
+      for (int q = 0; q < NQ; ++q) {
+        const int col = 32 * tile_of(q) + 16 * hi + n;
         if (col >= c.t.count) continue;
         const int64_t orow = c.shared ? (int64_t)c.A + c.t.start + col : p.sorted[c.t.start + col];
+        float* yr = p.y + orow * p.ld_y + (int64_t)pr0 * 16 + 4 * h;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(f32x4*)(p.y + orow * p.ld_y + (pr0 + g) * 16 + 4 * g4) = acc[g][q4];
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            *(f32x4*)(yr + 32 * rt + 8 * a) = f32x4{acc[rt][q][4 * a], acc[rt][q][4 * a + 1],
+                                                    acc[rt][q][4 * a + 2], acc[rt][q][4 * a + 3]};
       }
     }
   }
 }
 
 template <int PASS, int BM>
-__global__ __launch_bounds__(gemm_waves<BM>() * 64, BM == kBMFull ? 2 : 4) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(gemm_waves<BM>() * 64, 2) void gemm_kernel(GemmArgs p) {
   __shared__ Stage<BM> ring[kRing];
 
   // Block b runs on XCD b % 8 (round-robin dispatch).  XCD x walks tiles
@@ -447,27 +550,28 @@ __global__ __launch_bounds__(gemm_waves<BM>() * 64, BM == kBMFull ? 2 : 4) void 
   c.shared = c.t.expert == p.n_experts;
   const int64_t eoff = c.shared ? 0 : uniform((int64_t)c.t.expert * p.w_stride);
   const uint8_t* blob = (c.shared ? p.w_shared : p.w) + eoff;
-  c.blob = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(blob), (short)0,
-      (int)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256), 0x00020000);
+  // base address (48 bits, stride 0), size in bytes (reads past it return
+  // zero), raw dword access
+  const uint64_t ba = (uint64_t)(uintptr_t)blob;
+  c.blob = u32x4{(uint32_t)ba, (uint32_t)(ba >> 32) & 0xFFFFu,
+                 (uint32_t)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256), 0x00020000u};
   c.prb = nb * kBNGroups;
   c.A = p.rows * p.top_k;
   c.row0 = c.shared ? (int64_t)c.A + c.t.start : c.t.start;
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = (int)(threadIdx.x & 63);
-  // the rows behind this lane's B load (the wave's token group, column
-  // lane % 16) and scale load (token group 4 (wave - 4) + lane / 16)
+  // the rows behind this lane's B loads (the wave's token group, column
+  // lane % 16) and scale load (token group 4 qd + lane / 16)
   c.b_row = gemm_brow<PASS>(p, c, 16 * gemm_b_tg<BM>(wave) + (lane & 15));
-  c.d_row = gemm_brow<PASS>(p, c, 16 * (4 * max(wave - 4, 0) + (lane >> 4)) + (lane & 15));
+  c.d_row = gemm_brow<PASS>(p, c,
+                            16 * (4 * max(gemm_d_wave<BM>(wave), 0) + (lane >> 4)) + (lane & 15));
 
-  // live token groups of this wave's part: tp, tp+TH, ... below nnt
-  constexpr int TH = gemm_th<BM>();
-  const int nnt = (c.t.count + 15) >> 4;
+  // live 32-token tiles of this wave: tp, tp + TP, ... below n32
+  constexpr int TP = gemm_tp<BM>();
+  const int n32 = (c.t.count + 31) >> 5;
   const int tp = wave >> 2;
-  const int nq = min(BM / 16 / TH, max(0, (nnt - tp + TH - 1) / TH));
-  if constexpr (BM == kBMFull) {
+  const int nq = min(gemm_qt<BM>(), max(0, (n32 - tp + TP - 1) / TP));
+  if constexpr (gemm_qt<BM>() == 2) {
     switch (nq) {  // wave-uniform
-      case 4: gemm_body<PASS, 4, BM>(p, c, ring); break;
-      case 3: gemm_body<PASS, 3, BM>(p, c, ring); break;
       case 2: gemm_body<PASS, 2, BM>(p, c, ring); break;
       case 1: gemm_body<PASS, 1, BM>(p, c, ring); break;
       default: gemm_body<PASS, 0, BM>(p, c, ring); break;
@@ -519,9 +623,9 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
 
   if (stages & MOE_STAGE_GATE_UP) {
     uint8_t* xp = base + lay.act;
-    const int64_t ld_xp = 2 * (int64_t)L->d_model;
+    const int64_t ld_xp = (int64_t)(L->d_model / 32) * kDigitBlock;
     if (!(stages & MOE_STAGE_REUSE_ACTS)) {
-      const int64_t threads = (int64_t)rows * (L->d_model / 8);
+      const int64_t threads = (int64_t)rows * (L->d_model / 32);
       hipLaunchKernelGGL(prep_digits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
                          0, s, q, ld_q, rows, L->d_model, xp, ld_xp);
     }

@@ -265,22 +265,37 @@ def covering_rows(ids, n_experts, top_k, rows, tile, base, seed):
     return np.array(sorted(pick))
 
 
-E2M1_DIGIT = {0x0: 0, 0x2: 1, 0x4: 2, 0xA: -1, 0xC: -2}
+def e3m2_value(code):
+    """Value of a 6-bit E3M2 code (sign bit 5, exponent bits 4-2 with bias 3,
+    mantissa bits 1-0; exponent 0 is subnormal), per the OCP microscaling
+    format's FP6 E3M2 element."""
+    code = np.asarray(code, np.int64)
+    e, m = (code >> 2) & 7, code & 3
+    mag = np.where(e == 0, m / 4.0 * 2.0 ** -2, (1 + m / 4.0) * 2.0 ** (e.astype(np.float64) - 3))
+    return np.where(code & 32, -mag, mag)
 
 
 def codes_from_digit_planes(raw, d_ff):
-    """Hidden codes stored as E2M1 digit planes (the prefill GEMM's workspace
-    format): per row, d_ff/32 groups of 4 planes x 16 bytes, plane s holding
-    digit s of the group's 32 codes (element 2i in the low nibble of byte i);
-    code = sum_s 4^s * digit_s.  raw: uint8 [rows][2 * d_ff].  Any nibble
-    outside the five digit codes is an error."""
-    raw = np.asarray(raw, np.uint8).reshape(raw.shape[0], d_ff // 32, 4, 16)
-    nib = np.empty(raw.shape[:3] + (32,), np.uint8)
-    nib[..., 0::2], nib[..., 1::2] = raw & 0xF, raw >> 4
-    lut = np.full(16, 99, np.int32)
-    for c, v in E2M1_DIGIT.items():
-        lut[c] = v
-    dig = lut[nib]
-    assert np.all(dig != 99), "hidden digit plane holds a nibble that is not a digit 0, +-1, +-2"
-    w = np.array([1, 4, 16, 64], np.int32)[None, None, :, None]
-    return (dig * w).sum(axis=2).reshape(raw.shape[0], d_ff)
+    """Hidden codes stored as E3M2 digit planes (the prefill GEMM's workspace
+    format): per row, d_ff/32 blocks of 48 bytes in the first 1.5 d_ff bytes
+    -- plane 0 bytes 0-15, plane 1 bytes 0-15, plane 0 bytes 16-23, plane 1
+    bytes 16-23 -- plane s a 192-bit little-endian word holding digit s of the
+    block's element e in bits 6e..6e+5; code = d0 + 16 d1.  raw: uint8
+    [rows][>= 1.5 d_ff].  A digit that is not an integer in [-8, 8], or a
+    low digit outside [-8, 7], is an error."""
+    raw = np.asarray(raw, np.uint8)
+    nb = d_ff // 32
+    blk = raw[:, :nb * 48].reshape(raw.shape[0], nb, 48)
+    planes = [np.concatenate([blk[:, :, 0:16], blk[:, :, 32:40]], axis=2),
+              np.concatenate([blk[:, :, 16:32], blk[:, :, 40:48]], axis=2)]
+    digits = []
+    for pl in planes:
+        bits = np.unpackbits(pl, axis=2, bitorder="little")  # [rows][nb][192]
+        six = bits.reshape(raw.shape[0], nb, 32, 6)
+        code = (six * (1 << np.arange(6))).sum(axis=3)
+        v = e3m2_value(code)
+        assert np.all((v == np.round(v)) & (np.abs(v) <= 8)), \
+            "hidden digit plane holds a code that is not an integer digit in [-8, 8]"
+        digits.append(v.astype(np.int32))
+    assert np.all(digits[0] <= 7), "low hidden digit outside [-8, 7]"
+    return (digits[0] + 16 * digits[1]).reshape(raw.shape[0], d_ff)

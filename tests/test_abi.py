@@ -47,9 +47,10 @@ def test_packed_bytes_and_workspace_queries():
                         0x400000)
     L = m.lib()
     # 7 hidden rows: 2-byte codes, f32 scales, f32 partials; 1 token row of
-    # 2-byte activation digit planes; each region 256-byte aligned
+    # activation digit planes (48 bytes per 32 codes); each region 256-byte
+    # aligned
     assert L.moe_ffn_workspace_bytes(C.byref(lay), 1) == (7 * 2048 * 2 + 7 * 64 * 4
-                                                          + 7 * 4096 * 4 + 1 * 4096 * 2)
+                                                          + 7 * 4096 * 4 + 1 * 128 * 48)
     a, b, c = C.c_size_t(), C.c_size_t(), C.c_size_t()
     assert L.moe_ffn_workspace_layout(C.byref(lay), 1, C.byref(a), C.byref(b), C.byref(c)) == 0
     assert (a.value, b.value, c.value) == (0, 28672, 28672 + 1792)

@@ -224,6 +224,39 @@ def test_prefill_tile_fallback_shape(rows):
     run_case(ODD, seed, x, lg, entry="moe_ffn_prefill")
 
 
+# A layer whose every dimension takes the prefill grouped GEMM, with routes
+# that give its 128-row tiles each count of 32-token tiles from 1 to 4 (the
+# two token parts of a workgroup then hold 0, 1 or 2 of them), in both
+# passes.
+GEMM_MIX = synth.Layer(n_experts=16, top_k=2, d_model=256, d_ff=256, has_shared=True)
+
+
+@pytest.mark.parametrize("rows", [200, 330])
+def test_prefill_gemm_tile_mixes(rows):
+    seed = 31
+    L = GEMM_MIX
+    lg = synth.router_logits(seed, rows, rows, L.n_experts, hot_bias=0.5, n_hot=4)
+    ids_o, _ = oracle.route(lg, L.top_k)
+    counts = np.bincount(ids_o[ids_o >= 0].ravel(), minlength=L.n_experts)
+    assert rows * L.top_k > 16 * L.n_experts  # 128-row tiles
+    n32 = {-(-min(c - s, 128) // 32) for c in list(counts) + [rows] for s in range(0, c, 128)}
+    assert n32 == {1, 2, 3, 4}
+    x = synth.activations(seed, rows, rows, L.d_model)
+    run_case(L, seed, x, lg, entry="moe_ffn_prefill")
+    # and every row bit for bit equal to the oracle's exact-rows mode
+    layer = layer_for(L, seed)
+    xt, lt = torch.from_numpy(x).to(DEV), torch.from_numpy(lg).to(DEV)
+    q, qs = m.moe_quant_act_q8(xt)
+    ids, w, _, offsets, srt = m.moe_route_group(lt, L.top_k)
+    y = m.moe_ffn_prefill(layer, q, qs, ids, w, offsets, srt)
+    with oracle.exact_rows():
+        q_o, qs_o = oracle.quant_q8(x)
+        ids_e, w_e = oracle.route(lg, L.top_k)
+        ex = canonical_experts(L, seed, 0, range(L.n_experts + 1))
+        y_o = oracle.ffn(ex, L.n_experts, L.top_k, L.has_shared, q_o, qs_o, ids_e, w_e)
+    np.testing.assert_array_equal(y.cpu().numpy(), y_o)
+
+
 @pytest.mark.parametrize("rows", [1, 17])
 def test_prefill_gemm_small_rows(rows):
     c = synth.PREFILL
