@@ -386,19 +386,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
         uint32_t sw[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) sw[rt] = S.s[4 * rp + 2 * rt + hi][n];
+        // the token's activation scales of the chunk's 4 blocks, one 16-byte
+        // read per token tile (4-byte reads of single blocks would put the
+        // two 16-token groups of a tile on the same LDS banks)
+        f32x4 D[NQ1];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) D[q] = *(const f32x4*)&sd[((2 * tile_of(q) + hi) * 16 + n) * 4];
         // operands of block j: A[rt] (this lane's row, block j: the same 16
         // bytes in both K slots), BL/BH[q] (digit plane h of its token: bytes
-        // 0-15, 16-23), D[q] (the token's scale)
+        // 0-15, 16-23)
         u32x4 A[2][2], BL[2][NQ1];
         u32x2 BH[2][NQ1];
-        float D[2][NQ1];
         auto load = [&](int j, int slot) {
 #pragma unroll
           for (int q = 0; q < NQ; ++q) {
             const int tg = 2 * tile_of(q) + hi;
             BL[slot][q] = S.b[tg][3 * j + h][n];
             BH[slot][q] = ((const u32x2*)&S.b[tg][3 * j + 2][n])[h];
-            D[slot][q] = sd[(tg * 16 + n) * 4 + j];
           }
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) A[slot][rt] = S.a[4 * rp + 2 * rt + hi][16 * j + n];
@@ -407,10 +411,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
         // the chunk's 4 x NT tile-blocks in order, u = NT j + t (tile t =
         // (row tile t / NQ, token tile t % NQ)): tile-block u's instruction,
         // then the scaling of tile-block u-1's value, so every FMA reads a
-        // result one instruction old.  Block j+1's operands
-        // are read right after block j's first instruction, into the slot of
-        // block j-1 (whose instructions are all out; the scale its last
-        // scaling needs is kept aside first): a block's reads have a whole
+        // result one instruction old.  Block j+1's operands are read right
+        // after block j's first instruction, into the slot of block j-1
+        // (whose instructions are all out): a block's reads have a whole
         // block to land, and the wait before its first instruction covers no
         // later reads.
         f32x16 R[2];
@@ -420,7 +423,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
           // reads next to their use and wait for them there)
           __builtin_amdgcn_sched_barrier(0);
           float dprev = 0.f;
-          if (u > 0) dprev = D[((u - 1) / NT) & 1][((u - 1) % NT) % NQ1];
+          if (u > 0) dprev = D[((u - 1) % NT) % NQ1][(u - 1) / NT];
           if (u < 4 * NT) {
             const int j = u / NT, t = u % NT, cur = j & 1;
             const int rt = t / NQ1, q = t % NQ1;
