@@ -10,12 +10,12 @@
 // so each expert scans its packed weights once); the result is the stable
 // counting sort by expert.  Decode-sized calls (one workgroup, top-k
 // included): an assignment's position is its rank by (expert, index),
-// counted over the few ids in LDS.  Larger calls: an LDS histogram
-// (order-free), an exclusive scan, then a chunked stable scatter in which a
-// lane's destination is the expert's running base + the counts of earlier
-// waves in the chunk + its rank among earlier lanes of its wave with the
-// same expert (from ballots).  Atomics only add counts; no atomic decides an
-// order, so the permutation is unique and bit-exact.
+// counted over the few ids in LDS.  Larger calls: each wave counts its own
+// contiguous range of assignments per expert, a scan gives every wave its
+// base per expert, and each wave scatters its range in order, a lane's
+// destination being the running base + its rank among earlier lanes of its
+// wave with the same expert (from ballots).  No atomic decides an order, so
+// the permutation is unique and bit-exact.
 #include <float.h>
 
 #include "common.h"
@@ -46,27 +46,70 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 // Grouping of the ids of any number of rows (after route_topk_kernel).
 constexpr int kFusedMaxAssign = kGroupWaves * MOE_MAX_TOP_K;
 
+// Each wave owns a contiguous range of assignment indices (a multiple of 64)
+// and walks it in 64-wide pieces, kGroupWindow pieces per round trip of id
+// loads.  Pass 1 counts each wave's assignments per expert; one scan turns
+// the counts into each wave's base per expert (the expert's offset plus the
+// counts of the earlier waves); pass 2 scatters each wave's range in order,
+// a lane's position being its wave's running base for the expert plus its
+// rank among the lower lanes with the same expert.  The running bases are
+// private to a wave, so the scatter needs no workgroup barrier.
+constexpr int kGroupWindow = 16;
+
+// Per lane: rank among lower lanes holding the same (valid) expert, and that
+// expert's count in the wave.
+__device__ inline void wave_match(int e, bool valid, int nbits, uint64_t lt_mask, int& rank,
+                                  int& cnt) {
+  uint64_t same = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool b = valid && ((e >> bit) & 1);
+    const uint64_t m = __ballot(b);
+    same &= ((e >> bit) & 1) ? m : ~m;
+  }
+  rank = __popcll(same & lt_mask);
+  cnt = __popcll(same);
+}
+
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(
     const int32_t* __restrict__ ids_g, int n_assign, int n_experts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
-  __shared__ int hist[kMaxExperts];
-  __shared__ int running[kMaxExperts];
+  extern __shared__ int wbase[];  // [kGroupWaves][n_experts]: counts, then running bases
   __shared__ int wave_tot[kGroupWaves];
-  extern __shared__ int wcnt[];  // [kGroupWaves][n_experts]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto id_at = [&](int a) -> int { return ids_g[a]; };
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int nbits = 0;
+  while ((1 << nbits) < n_experts) ++nbits;
+  // this wave's range [r0, r1) of assignments, in 64-wide pieces
+  const int per_wave = (n_assign + kGroupWaves * 64 - 1) / (kGroupWaves * 64) * 64;
+  const int r0 = min(wave * per_wave, n_assign), r1 = min(r0 + per_wave, n_assign);
+  int* my = wbase + wave * n_experts;
 
-  for (int e = tid; e < n_experts; e += kGroupThreads) hist[e] = 0;
-  for (int e = tid; e < kGroupWaves * n_experts; e += kGroupThreads) wcnt[e] = 0;
+  for (int e = tid; e < kGroupWaves * n_experts; e += kGroupThreads) wbase[e] = 0;
   __syncthreads();
-  for (int a = tid; a < n_assign; a += kGroupThreads) {
-    const int e = id_at(a);
-    if (e >= 0) atomicAdd(&hist[e], 1);
+  // pass 1: this wave's count per expert (its leaders add whole matches)
+  for (int w0 = r0; w0 < r1; w0 += kGroupWindow * 64) {
+    int ev[kGroupWindow];
+#pragma unroll
+    for (int k = 0; k < kGroupWindow; ++k) {
+      const int a = w0 + 64 * k + lane;
+      ev[k] = a < r1 ? ids_g[a] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kGroupWindow; ++k) {
+      if (w0 + 64 * k >= r1) break;  // wave-uniform
+      int rank, cnt;
+      wave_match(ev[k], ev[k] >= 0, nbits, lt_mask, rank, cnt);
+      if (ev[k] >= 0 && rank == 0) my[ev[k]] += cnt;
+    }
   }
   __syncthreads();
 
-  // exclusive scan of hist (n_experts <= kGroupThreads: one entry per thread)
-  const int c = tid < n_experts ? hist[tid] : 0;
+  // counts, offsets (exclusive scan over experts), and each wave's base per
+  // expert (n_experts <= kGroupThreads: one expert per thread)
+  int c = 0;
+  if (tid < n_experts) {
+    for (int w2 = 0; w2 < kGroupWaves; ++w2) c += wbase[w2 * n_experts + tid];
+  }
   const int incl = wave_incl_scan(c);
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
@@ -76,42 +119,40 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
   if (tid < n_experts) {
     counts[tid] = c;
     offsets[tid] = excl;
-    running[tid] = excl;
+    int run = excl;
+    for (int w2 = 0; w2 < kGroupWaves; ++w2) {
+      const int t = wbase[w2 * n_experts + tid];
+      wbase[w2 * n_experts + tid] = run;
+      run += t;
+    }
   }
   int n_valid = 0;
   for (int w2 = 0; w2 < kGroupWaves; ++w2) n_valid += wave_tot[w2];
   if (tid == 0) offsets[n_experts] = n_valid;
   __syncthreads();
 
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int nbits = 0;
-  while ((1 << nbits) < n_experts) ++nbits;
-  for (int chunk = 0; chunk < n_assign; chunk += kGroupThreads) {
-    const int a = chunk + tid;
-    const int e = (a < n_assign) ? id_at(a) : -1;
-    const bool valid = e >= 0;
-    uint64_t same = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool b = valid && ((e >> bit) & 1);
-      const uint64_t m = __ballot(b);
-      same &= ((e >> bit) & 1) ? m : ~m;
+  // pass 2: scatter this wave's range in index order
+  for (int w0 = r0; w0 < r1; w0 += kGroupWindow * 64) {
+    int ev[kGroupWindow];
+#pragma unroll
+    for (int k = 0; k < kGroupWindow; ++k) {
+      const int a = w0 + 64 * k + lane;
+      ev[k] = a < r1 ? ids_g[a] : -1;
     }
-    const int rank = __popcll(same & lt_mask);
-    const int cnt = __popcll(same);
-    const bool leader = valid && rank == 0;
-    if (leader) wcnt[wave * n_experts + e] = cnt;
-    __syncthreads();
-    if (valid) {
-      int pos = running[e] + rank;
-      for (int w2 = 0; w2 < wave; ++w2) pos += wcnt[w2 * n_experts + e];
-      sorted[pos] = a;
+#pragma unroll
+    for (int k = 0; k < kGroupWindow; ++k) {
+      if (w0 + 64 * k >= r1) break;  // wave-uniform
+      const int e = ev[k];
+      const bool valid = e >= 0;
+      int rank, cnt;
+      wave_match(e, valid, nbits, lt_mask, rank, cnt);
+      const int pos = valid ? my[e] + rank : 0;
+      if (valid) sorted[pos] = w0 + 64 * k + lane;
+      // every lane has read the bases before the leaders move them on
+      __builtin_amdgcn_wave_barrier();
+      if (valid && rank == 0) my[e] += cnt;
+      __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&running[e], cnt);
-      wcnt[wave * n_experts + e] = 0;
-    }
-    __syncthreads();
   }
   for (int p = n_valid + tid; p < n_assign; p += kGroupThreads) sorted[p] = -1;
 }
