@@ -58,13 +58,13 @@ GEMM_SIMDS = 1024
 # (hash below, over the device code in csrc/): after any change to it the
 # benchmark reports traffic as null.
 TRAFFIC_DOC = "profiles/hbm_traffic_counters.md (moe_counters under rocprofv3 --pmc, offline)"
-TRAFFIC_SRC = "ca79141f1674536f"
+TRAFFIC_SRC = "4fa685d5dde2316e"
 TRAFFIC = {  # (workload, rows[, variant]): (read bytes, written bytes)
-    ("decode", 1): (2 * 30787.9 * 1024, 48.6 * 1024),
-    ("decode-batch", 16): (2 * 349801.5 * 1024, 678.4 * 1024),
-    ("decode-batch", 16, "hot"): (2 * 171096.7 * 1024, 672.9 * 1024),
-    ("prefill", 4096): (2 * 1435971.7 * 1024, 139264.1 * 1024),
-    ("prefill", 512): (2 * 1209634.7 * 1024, 17499.3 * 1024),
+    ("decode", 1): (2 * 30787.8 * 1024, 48.6 * 1024),
+    ("decode-batch", 16): (2 * 349796.3 * 1024, 677.1 * 1024),
+    ("decode-batch", 16, "hot"): (2 * 171095.7 * 1024, 673.0 * 1024),
+    ("prefill", 4096): (2 * 1413344.2 * 1024, 106591.2 * 1024),
+    ("prefill", 512): (2 * 1206866.2 * 1024, 13596.2 * 1024),
     ("matvec", 5): (2 * 15414.9 * 1024, 280.0 * 1024),
 }
 
