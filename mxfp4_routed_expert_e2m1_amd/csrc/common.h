@@ -6,10 +6,11 @@
 // 32-element blocks).  The unit of one wave load is a (row group, K chunk)
 // tile of 1 KiB nibbles: lane l = 16*j + r holds the 16 canonical bytes of
 // row r's block j (32 E2M1 codes, element 2i in the low nibble of byte i).
-// That is exactly the operand layout of the scaled FP4 matrix-core
-// instruction (16x16x128: lane l supplies row l%16 and the 32 elements of
-// K-slot l/16), so the prefill GEMM feeds LDS copies of the tiles to it
-// directly; the bf16 16x16x32 instruction of the decode kernels wants lane
+// A lane's 16 bytes are one row's 32-element block in the form the scaled
+// matrix-core instructions take an E2M1 operand slot, so the prefill GEMM
+// reads one row's block per lane from LDS copies of the tiles and feeds it
+// to the 32x32x64 instruction untouched; the bf16 16x16x32 instruction of
+// the decode kernels wants lane
 // 16*g + r to hold elements 8g..8g+7 of every block instead, which four
 // lane-group swaps per loaded tile produce (tile_to_bf16_frags).
 //   nibbles: [RG][KC slots][64 lanes][16 B]
