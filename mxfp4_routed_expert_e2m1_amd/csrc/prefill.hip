@@ -56,6 +56,7 @@ constexpr int kBMShort = 32;
 constexpr int kBNGroups = 16;  // 16-row weight groups per workgroup (256 rows)
 constexpr int kRing = 3;       // LDS stages (chunks in flight ahead: kRing - 1)
 constexpr int kRunChunks = 4;  // chunks per exact-rows run (16 blocks)
+constexpr int kMaxTileExperts = 512;  // TileMap's limit (8 experts per lane)
 constexpr int kDigitBlock = 48;   // bytes of one 32-code block as two E3M2 digit planes
 constexpr int kDigitChunk = 4 * kDigitBlock;  // one 128-element K chunk
 // Waves per workgroup: 4 row parts x TP token parts, two waves per SIMD.
@@ -79,6 +80,7 @@ struct GemmArgs {
   int64_t ld_xp;      // bytes per row of planes (>= 1.5 K)
   const float* xs;    // B scales: qs (gate/up) or hidden scales (down)
   int64_t ld_xs;
+  u32x4 xp_rsrc, xs_rsrc;  // buffer resources over the rows of xp and xs
   int n_items;  // tiles bound x weight-row blocks
   uint8_t* h;   // gate/up: hidden digit planes
   float* hs;
@@ -249,17 +251,25 @@ struct GemmCtx {
   Tile t;
   bool shared;
   int A;
-  int b_row;  // B / scale row of this lane's B loads (token or hidden row)
-  int d_row;  // B / scale row of this lane's scale loads
+  uint32_t b_off;  // byte offset in xp of this lane's B loads' row (+ its 16-byte piece)
+  uint32_t d_off;  // byte offset in xs of this lane's scale loads' row
 };
 
 // B row of tile row r (clamped into the tile): the token for gate/up (through
-// the sorted list for routed experts), the hidden row for down.
+// the sorted list for routed experts), the hidden row for down.  In two
+// steps, so that a persistent workgroup can load the next item's entries
+// early and use them late: gemm_brow_raw reads (the sorted list's
+// assignment for a routed gate/up tile, else the row itself), gemm_brow_fin
+// turns that into the row.
 template <int PASS>
-__device__ inline int gemm_brow(const GemmArgs& p, const GemmCtx& c, int r) {
+__device__ inline int gemm_brow_raw(const GemmArgs& p, const GemmCtx& c, int r) {
   r = min(r, c.t.count - 1);
   if (PASS == GEMM_DOWN) return (int)c.row0 + r;
-  return c.shared ? c.t.start + r : p.sorted[c.t.start + r] / p.top_k;
+  return c.shared ? c.t.start + r : p.sorted[c.t.start + r];
+}
+template <int PASS>
+__device__ inline int gemm_brow_fin(const GemmArgs& p, bool shared, int raw) {
+  return (PASS == GEMM_DOWN || shared) ? raw : raw / p.top_k;
 }
 
 // The loads of one K chunk, spread over the waves: the 16 weight tiles
@@ -313,17 +323,17 @@ __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>
   }
   const int qd = gemm_d_wave<BM>(wave);
   if (qd >= 0)  // scales of token groups 4 qd .. 4 qd + 3
-    glb_to_lds16(p.xs + (int64_t)c.d_row * p.ld_xs + (int64_t)kc * 4, &S.d[4 * qd][0]);
+    buf_to_lds16(p.xs_rsrc, &S.d[4 * qd][0], c.d_off, (uint32_t)kc * 16u);
   if (b_live) {
     // load li: token group li / 3, pieces 4 (li % 3) .. + 3 of its 16 tokens
     // (lane: piece 4 (li % 3) + lane / 16 of token lane % 16)
-    const uint8_t* src = p.xp + (int64_t)c.b_row * p.ld_xp + (int64_t)kc * kDigitChunk + 16 * g4;
     const int b0 = gemm_b_first<BM>(wave), nb = gemm_b_count<BM>(wave);
 #pragma unroll
     for (int i = 0; i < gemm_b_max<BM>(); ++i) {
       if (i < nb) {
         const int li = b0 + i, tg = li / 3, part = li % 3;
-        glb_to_lds16(src + 64 * part, &S.b[tg][4 * part][0]);
+        buf_to_lds16(p.xp_rsrc, &S.b[tg][4 * part][0], c.b_off,
+                     (uint32_t)kc * (uint32_t)kDigitChunk + 64u * (uint32_t)part);
       }
     }
   }
@@ -335,8 +345,27 @@ __device__ inline void gemm_issue(const GemmArgs& p, const GemmCtx& c, Stage<BM>
 // works on row / token l % 32 of a tile: 16-row group (or token group)
 // 2 x + hi, column n, hi = (l / 16) % 2; its K slot h = l / 32 carries digit
 // plane h.  Branch-free inner loop.
-template <int PASS, int NQ, int BM>
-__device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring) {
+template <int PASS, int BM> __device__ inline bool gemm_b_live(const GemmCtx& c, int wave) {
+  return gemm_b_tg<BM>(wave) < ((c.t.count + 15) >> 4);  // this wave stages a live token group
+}
+
+// The first kRing-1 chunks of an item (the rest go out as the K loop runs).
+template <int PASS, int BM>
+__device__ inline void gemm_issue_first(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring) {
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = (int)(threadIdx.x & 63);
+  const bool b_live = gemm_b_live<PASS, BM>(c, wave);
+#pragma unroll
+  for (int k0 = 0; k0 < kRing - 1; ++k0)
+    if (k0 < p.kc_total) gemm_issue<PASS, BM>(p, c, ring[k0], k0, wave, lane, b_live);
+}
+
+// Item c, whose first chunks are already out; between() runs between the K
+// loop and the epilogue (a persistent workgroup sends its next item's first
+// chunks there, after a barrier -- the ring is free once every wave is past
+// its last chunk -- so they land while this item's epilogue runs).
+template <int PASS, int NQ, int BM, typename Between>
+__device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring,
+                                          Between between) {
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6), lane = tid & 63;
   const int n = lane & 15, hi = (lane >> 4) & 1, h = lane >> 5;
@@ -344,10 +373,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
   constexpr int NQ1 = NQ > 0 ? NQ : 1;
   constexpr int NT = 2 * NQ;  // tiles per block
   const int rp = wave & 3, tp = wave >> 2;
-  const int nnt = (c.t.count + 15) >> 4;
   auto tile_of = [&](int q) { return tp + TP * q; };  // token tile of slot q
-  // token group this wave stages
-  const bool b_live = gemm_b_tg<BM>(wave) < nnt;
+  const bool b_live = gemm_b_live<PASS, BM>(c, wave);
   const int per_chunk = gemm_loads_per_chunk<BM>(wave, b_live);
   // B scale of K slot h (digit plane h carries weight 16^h)
   const int sb = 127 + 4 * h;
@@ -359,10 +386,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
     for (int q = 0; q < NQ1; ++q) acc[rt][q] = f32x16{};
 
   const int KC = p.kc_total;
-  // chunks 0 .. kRing-2 go out first; chunk kc + kRing - 1 after chunk kc lands
-#pragma unroll
-  for (int k0 = 0; k0 < kRing - 1; ++k0)
-    if (k0 < KC) gemm_issue<PASS, BM>(p, c, ring[k0], k0, wave, lane, b_live);
+  // chunk kc + kRing - 1 goes out after chunk kc lands
   int kc = 0;
   // runs of kRunChunks chunks, each summed from zero and added in order
   for (int kr = 0; kr < KC; kr += kRunChunks) {
@@ -453,6 +477,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
 #pragma unroll
       for (int q = 0; q < NQ1; ++q) acc[rt][q] += run[rt][q];
   }
+  between();  // (a persistent workgroup sends its next item's first chunks here)
 
   if constexpr (NT > 0) {
     const int pr0 = c.prb + 4 * rp;
@@ -526,30 +551,31 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, const GemmCtx& c, S
   }
 }
 
+// B / scale rows of this lane for an item with tile t: the token (gate/up,
+// through the sorted list for routed experts) or hidden row (down) behind
+// its B loads (the wave's token group, column lane % 16) and its scale load
+// (token group 4 qd + lane / 16).  These are the item's only loads before
+// its first chunk.
 template <int PASS, int BM>
-__global__ __launch_bounds__(gemm_waves<BM>() * 64, 2) void gemm_kernel(GemmArgs p) {
-  __shared__ Stage<BM> ring[kRing];
-
-  // Block b runs on XCD b % 8 (round-robin dispatch).  XCD x walks tiles
-  // x, x+8, x+16, ... and all weight-row blocks of a tile back to back, so the
-  // workgroups sharing a token tile share that XCD's L2, and the live tiles
-  // (the low ids) spread over all eight XCDs.
-  const int n_nb = p.rg_total / kBNGroups;
-  const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
-  const int tile_idx = (slot / n_nb) * 8 + xcd;
-  const int nb = slot % n_nb;
-  if (tile_idx * n_nb >= p.n_items) return;
-  // The shared expert's tiles (all full but the last) take the low ids, so
-  // the longest items start first and the short routed tiles fill the tail.
-  TileMap<BM> m;
-  m.load(p.offsets, p.n_experts, p.has_shared, p.rows);
+__device__ inline void gemm_rows(const GemmArgs& p, Tile t, int& raw_b, int& raw_d) {
   GemmCtx c;
-  c.t = m.lookup(p.n_experts, p.rows,
-                 tile_idx < m.shared_tiles ? m.routed + tile_idx : tile_idx - m.shared_tiles);
-  c.t.expert = uniform(c.t.expert);
-  c.t.start = uniform(c.t.start);
-  c.t.count = uniform(c.t.count);
-  if (c.t.expert < 0) return;
+  c.t = t;
+  c.shared = t.expert == p.n_experts;
+  c.row0 = c.shared ? (int64_t)p.rows * p.top_k + t.start : t.start;
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = (int)(threadIdx.x & 63);
+  raw_b = gemm_brow_raw<PASS>(p, c, 16 * gemm_b_tg<BM>(wave) + (lane & 15));
+  raw_d = gemm_brow_raw<PASS>(p, c, 16 * (4 * max(gemm_d_wave<BM>(wave), 0) + (lane >> 4)) +
+                                        (lane & 15));
+}
+
+// Everything about item (tile t, weight-row block nb) that the K loop and
+// the epilogue need, given its rows.
+template <int PASS, int BM>
+__device__ inline GemmCtx gemm_ctx_rows(const GemmArgs& p, Tile t, int nb, int raw_b, int raw_d) {
+  GemmCtx c;
+  c.t.expert = uniform(t.expert);
+  c.t.start = uniform(t.start);
+  c.t.count = uniform(t.count);
   c.shared = c.t.expert == p.n_experts;
   const int64_t eoff = c.shared ? 0 : uniform((int64_t)c.t.expert * p.w_stride);
   const uint8_t* blob = (c.shared ? p.w_shared : p.w) + eoff;
@@ -561,28 +587,173 @@ __global__ __launch_bounds__(gemm_waves<BM>() * 64, 2) void gemm_kernel(GemmArgs
   c.prb = nb * kBNGroups;
   c.A = p.rows * p.top_k;
   c.row0 = c.shared ? (int64_t)c.A + c.t.start : c.t.start;
-  const int wave = uniform((int)(threadIdx.x >> 6)), lane = (int)(threadIdx.x & 63);
-  // the rows behind this lane's B loads (the wave's token group, column
-  // lane % 16) and scale load (token group 4 qd + lane / 16)
-  c.b_row = gemm_brow<PASS>(p, c, 16 * gemm_b_tg<BM>(wave) + (lane & 15));
-  c.d_row = gemm_brow<PASS>(p, c,
-                            16 * (4 * max(gemm_d_wave<BM>(wave), 0) + (lane >> 4)) + (lane & 15));
+  const int lane = (int)(threadIdx.x & 63);
+  c.b_off = (uint32_t)gemm_brow_fin<PASS>(p, c.shared, raw_b) * (uint32_t)p.ld_xp +
+            16u * (uint32_t)(lane >> 4);
+  c.d_off = (uint32_t)gemm_brow_fin<PASS>(p, c.shared, raw_d) * (uint32_t)p.ld_xs * 4u;
+  return c;
+}
 
-  // live 32-token tiles of this wave: tp, tp + TP, ... below n32
+template <int PASS, int BM>
+__device__ inline GemmCtx gemm_ctx(const GemmArgs& p, Tile t, int nb) {
+  int raw_b, raw_d;
+  gemm_rows<PASS, BM>(p, t, raw_b, raw_d);
+  return gemm_ctx_rows<PASS, BM>(p, t, nb, raw_b, raw_d);
+}
+
+// One item with the K loop's instantiation for this wave's live token tiles
+// (tp, tp + TP, ... below the tile's 32-token tiles).
+template <int PASS, int BM, typename Between>
+__device__ inline void gemm_item(const GemmArgs& p, const GemmCtx& c, Stage<BM>* ring,
+                                 Between between) {
   constexpr int TP = gemm_tp<BM>();
   const int n32 = (c.t.count + 31) >> 5;
-  const int tp = wave >> 2;
+  const int tp = uniform((int)(threadIdx.x >> 6)) >> 2;
   const int nq = min(gemm_qt<BM>(), max(0, (n32 - tp + TP - 1) / TP));
   if constexpr (gemm_qt<BM>() == 2) {
     switch (nq) {  // wave-uniform
-      case 2: gemm_body<PASS, 2, BM>(p, c, ring); break;
-      case 1: gemm_body<PASS, 1, BM>(p, c, ring); break;
-      default: gemm_body<PASS, 0, BM>(p, c, ring); break;
+      case 2: gemm_body<PASS, 2, BM>(p, c, ring, between); break;
+      case 1: gemm_body<PASS, 1, BM>(p, c, ring, between); break;
+      default: gemm_body<PASS, 0, BM>(p, c, ring, between); break;
     }
   } else {
-    if (nq == 1) gemm_body<PASS, 1, BM>(p, c, ring);
-    else gemm_body<PASS, 0, BM>(p, c, ring);
+    if (nq == 1) gemm_body<PASS, 1, BM>(p, c, ring, between);
+    else gemm_body<PASS, 0, BM>(p, c, ring, between);
   }
+}
+
+// The call's tiles (as TileMap numbers them) kept in LDS for a persistent
+// workgroup: per expert its first tile number and first row; tile t of the
+// routed experts belongs to the last expert whose first tile is <= t.
+struct TileList {
+  int first_tile[kMaxTileExperts + 1];
+  int first_row[kMaxTileExperts + 1];
+};
+
+__device__ inline Tile tile_at(const TileList& tl, int n_experts, int rows, int routed, int t,
+                               int bm) {
+  Tile r{-1, 0, 0};
+  if (t < routed) {
+    int lo = 0, hi = n_experts - 1;  // the last e with first_tile[e] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tl.first_tile[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    r.expert = lo;
+    r.start = tl.first_row[lo] + (t - tl.first_tile[lo]) * bm;
+    r.count = min(bm, tl.first_row[lo + 1] - r.start);
+  } else {
+    const int st = t - routed;
+    r.expert = n_experts;
+    r.start = st * bm;
+    r.count = min(bm, rows - st * bm);
+  }
+  return r;
+}
+
+// Item k of XCD x is tile (k / n_nb) * 8 + x, weight-row block k % n_nb:
+// the workgroups that share a token tile run on one XCD and share its L2,
+// and the live tiles spread over all eight XCDs.  Tiles are numbered with
+// the shared expert's (all full but the last) first, so the longest items
+// start first and the short routed tiles fill the tail.
+//   128-row tiles: persistent workgroups, one per CU (block b runs on XCD
+//   b % 8 and takes that XCD's items b / 8, b / 8 + G, ... for G workgroups
+//   per XCD).  Each item's tile is found in a list built once into LDS, and
+//   the next item's tile, rows and first chunks go out before this item's
+//   epilogue, so no item waits for its own prologue.
+//   32-row tiles (two workgroups per CU): one item per workgroup.
+template <int PASS, int BM>
+__global__ __launch_bounds__(gemm_waves<BM>() * 64, 2) void gemm_kernel(GemmArgs p) {
+  __shared__ Stage<BM> ring[kRing];
+  const int n_nb = p.rg_total / kBNGroups;
+  const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
+  if constexpr (BM == kBMFull) {
+    __shared__ TileList s_tl;
+    __shared__ int s_routed, s_shared;
+    if (threadIdx.x < 64) {  // wave 0 counts the tiles (TileMap) and lists them in LDS
+      TileMap<BM> m;
+      m.load(p.offsets, p.n_experts, p.has_shared, p.rows);
+      int ft = m.incl - m.lsum;
+      const int per = (p.n_experts + 63) >> 6;  // this lane's experts: e0 .. e0 + per - 1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = m.e0 + i;
+        if (i < per && e < p.n_experts) {
+          s_tl.first_tile[e] = ft;
+          s_tl.first_row[e] = m.o[i];
+        }
+        ft += m.nt[i];
+      }
+      if (threadIdx.x == 0) {
+        s_tl.first_tile[p.n_experts] = m.routed;
+        s_tl.first_row[p.n_experts] = p.offsets[p.n_experts];
+        s_routed = m.routed;
+        s_shared = m.shared_tiles;
+      }
+    }
+    __syncthreads();
+    const int routed = uniform(s_routed), shared_tiles = uniform(s_shared);
+    const int n_tiles = routed + shared_tiles;
+    const int per_xcd = (int)(gridDim.x / 8);
+    auto item = [&](int k, Tile& t, int& nb) -> bool {  // (the same for the whole workgroup)
+      const int tile_idx = (k / n_nb) * 8 + xcd;
+      if (tile_idx >= n_tiles) return false;
+      t = tile_at(s_tl, p.n_experts, p.rows, routed,
+                  tile_idx < shared_tiles ? routed + tile_idx : tile_idx - shared_tiles, BM);
+      nb = k % n_nb;
+      return uniform(t.expert) >= 0;
+    };
+    int k = slot;
+    Tile t;
+    int nb;
+    if (!item(k, t, nb)) return;
+    GemmCtx c = gemm_ctx<PASS, BM>(p, t, nb);
+    gemm_issue_first<PASS, BM>(p, c, ring);
+    for (;;) {
+      // the next item's sorted-list entries are loaded now (they land while
+      // this item runs); its tile is found again in LDS, and the entries
+      // made rows, when its first chunks go out
+      Tile t2;
+      int nb2, br2, dr2;  // (set and read only with a next item: no write
+                          // to them may wait for the loads in flight)
+      const bool more = item(k + per_xcd, t2, nb2);
+      if (more) gemm_rows<PASS, BM>(p, t2, br2, dr2);
+      auto between = [&]() {
+        if (!more) return;  // workgroup-uniform
+        ring_barrier();
+        Tile tn;
+        int nbn;
+        item(k + per_xcd, tn, nbn);
+        gemm_issue_first<PASS, BM>(p, gemm_ctx_rows<PASS, BM>(p, tn, nbn, br2, dr2), ring);
+      };
+      gemm_item<PASS, BM>(p, c, ring, between);
+      if (!more) break;
+      k += per_xcd;
+      item(k, t2, nb2);
+      c = gemm_ctx_rows<PASS, BM>(p, t2, nb2, br2, dr2);
+    }
+  } else {
+    const int tile_idx = (slot / n_nb) * 8 + xcd;
+    if (tile_idx * n_nb >= p.n_items) return;
+    TileMap<BM> m;
+    m.load(p.offsets, p.n_experts, p.has_shared, p.rows);
+    const Tile t = m.lookup(p.n_experts, p.rows,
+                            tile_idx < m.shared_tiles ? m.routed + tile_idx
+                                                      : tile_idx - m.shared_tiles);
+    if (uniform(t.expert) < 0) return;
+    const GemmCtx c = gemm_ctx<PASS, BM>(p, t, slot % n_nb);
+    gemm_issue_first<PASS, BM>(p, c, ring);
+    gemm_item<PASS, BM>(p, c, ring, []() {});
+  }
+}
+
+// Raw buffer resource over [base, base + bytes): 48-bit base, stride 0, the
+// size in bytes (reads past it return zero), raw dword access.
+static u32x4 buffer_rsrc(const void* base, int64_t bytes) {
+  const uint64_t ba = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)ba, (uint32_t)(ba >> 32) & 0xFFFFu,
+               (uint32_t)std::min<int64_t>(bytes, 0xFFFFFFFFll), 0x00020000u};
 }
 
 int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
@@ -613,7 +784,11 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
 
   auto launch = [&](int pass, GemmArgs& g) {
     g.n_items = tiles * (g.rg_total / kBNGroups);
-    const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
+    // 32-row tiles: one workgroup per item; 128-row tiles: persistent, at
+    // most one per CU (a multiple of 8, one share per XCD)
+    const unsigned items = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
+    const unsigned cus8 = (unsigned)std::max(8, device_cu_count() / 8 * 8);
+    const unsigned grid = short_tiles ? items : std::min(items, cus8);
     const dim3 block(gemm_waves<kBMFull>() * 64), block_s(gemm_waves<kBMShort>() * 64);
     if (pass == GEMM_GATEUP) {
       if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), block_s, 0, s, g);
@@ -645,6 +820,8 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     g.ld_xp = ld_xp;
     g.xs = qs;
     g.ld_xs = ld_qs;
+    g.xp_rsrc = buffer_rsrc(xp, (int64_t)rows * ld_xp);
+    g.xs_rsrc = buffer_rsrc(qs, (int64_t)rows * ld_qs * 4);
     g.bf16_mid = (L->flags & MOE_LAYER_BF16_INTERMEDIATE) != 0;
     launch(GEMM_GATEUP, g);
   }
@@ -662,6 +839,9 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
     d.ld_xp = a.ld_h;
     d.xs = a.hs;
     d.ld_xs = a.ld_hs;
+    const int64_t hrows = (int64_t)A + (L->has_shared ? rows : 0);
+    d.xp_rsrc = buffer_rsrc(a.h, hrows * a.ld_h);
+    d.xs_rsrc = buffer_rsrc(a.hs, hrows * a.ld_hs * 4);
     d.y = (float*)(base + lay.partials);
     d.ld_y = L->d_model;
     launch(GEMM_DOWN, d);
