@@ -738,6 +738,9 @@ __global__ __launch_bounds__(gemm_waves<BM>() * 64, 2) void gemm_kernel(GemmArgs
     if (tile_idx * n_nb >= p.n_items) return;
     TileMap<BM> m;
     m.load(p.offsets, p.n_experts, p.has_shared, p.rows);
+    // (the grid is sized from a bound on the tiles: past the last tile the
+    // renumbering below would land on the shared expert's tiles again)
+    if (tile_idx >= m.n_tiles()) return;
     const Tile t = m.lookup(p.n_experts, p.rows,
                             tile_idx < m.shared_tiles ? m.routed + tile_idx
                                                       : tile_idx - m.shared_tiles);
