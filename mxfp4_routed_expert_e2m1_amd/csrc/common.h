@@ -215,16 +215,30 @@ __device__ inline float q8_code(float v, float d) {
   return d != 0.f ? fminf(fmaxf(rintf(v / d), -127.f), 127.f) : 0.f;
 }
 
+// Lane moves on DPP (a VALU operand modifier: no LDS round trip).
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, false));
+}
+// DPP move limited to the rows in ROWS (other rows keep v).
+template <int CTRL, int ROWS>
+__device__ inline float dpp_rows(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                              __builtin_bit_cast(int, v), CTRL,
+                                                              ROWS, 0xF, false));
+}
+
 // The quantiser's arithmetic for 8 consecutive elements of a 32-element
 // block, 4 aligned lanes per block (all 4 must call it together): amax by
-// two lane xors, d = amax / 127 in fp32, codes packed little-endian into w0
-// (elements 0-3) and w1 (4-7).  Returns d.
+// two lane swaps within the quad, d = amax / 127 in fp32, codes packed
+// little-endian into w0 (elements 0-3) and w1 (4-7).  Returns d.
 __device__ inline float q8_quant8(const float (&v)[8], uint32_t& w0, uint32_t& w1) {
   float m = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
-  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  m = fmaxf(m, dpp_mov<0xB1>(m));  // quad_perm [1,0,3,2]: lane ^ 1
+  m = fmaxf(m, dpp_mov<0x4E>(m));  // quad_perm [2,3,0,1]: lane ^ 2
   const float d = m / 127.0f;
   w0 = 0;
   w1 = 0;
@@ -271,24 +285,6 @@ __device__ inline void quant_q8_thread(int64_t i, const float* __restrict__ x, i
   }
 }
 
-// Max over each aligned group of 32 lanes (lanes 0-31, 32-63), returned in
-// every lane: quad swaps and the row half-mirror / mirror on DPP give each
-// 16-lane row its max, then one lane-xor-16 shuffle combines rows 0/1 and
-// 2/3.  Exact: max does not round.  (permlane16_swap(v, v) would do the last
-// step without LDS, but this compiler folds the max of its two results away.)
-template <int CTRL>
-__device__ inline float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
-                                                            0xF, false));
-}
-// DPP move limited to the rows in ROWS (other rows keep v).
-template <int CTRL, int ROWS>
-__device__ inline float dpp_rows(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
-                                                              __builtin_bit_cast(int, v), CTRL,
-                                                              ROWS, 0xF, false));
-}
-
 // Max over the whole wave, returned as a wave-uniform value: row maxima on
 // DPP, row broadcasts 15 and 31 fold them into lane 63, read from there.
 __device__ inline float wave_max(float v) {
@@ -301,6 +297,11 @@ __device__ inline float wave_max(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Max over each aligned group of 32 lanes (lanes 0-31, 32-63), returned in
+// every lane: quad swaps and the row half-mirror / mirror on DPP give each
+// 16-lane row its max, then one lane-xor-16 shuffle combines rows 0/1 and
+// 2/3.  Exact: max does not round.  (permlane16_swap(v, v) would do the last
+// step without LDS, but this compiler folds the max of its two results away.)
 __device__ inline float max32(float v) {
   v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
   v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
@@ -471,50 +472,100 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// One wave: top_k picks of one row; lane s < top_k receives slot s.  Each
-// round takes the largest remaining logit (a wave max of the keys on DPP)
-// and, among the experts holding exactly that value, the lowest index
-// (per-slot ballots, lowest slot first: expert e sits in lane e % 64, slot
-// e / 64); the pick's key becomes 0.  The weights follow the rounds: each
-// pick's sigmoid in its own lane, then their sum in pick order.
+// Min of an unsigned value over the whole wave (the same DPP steps).
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  auto f = [](uint32_t u) { return __builtin_bit_cast(float, u); };
+  auto u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+  v = min(v, u(dpp_mov<0xB1>(f(v))));
+  v = min(v, u(dpp_mov<0x4E>(f(v))));
+  v = min(v, u(dpp_mov<0x141>(f(v))));
+  v = min(v, u(dpp_mov<0x140>(f(v))));
+  v = min(v, u(dpp_rows<0x142, 0xA>(f(v))));
+  v = min(v, u(dpp_rows<0x143, 0xC>(f(v))));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// One wave: the top_k picks of one row of logits; lane s < top_k receives
+// pick s (its expert and its key).  Expert e sits in lane e % 64, slot
+// e / 64.  Each round takes the largest remaining key (a wave max over
+// every lane's best; a lane's best is its largest key, the lower slot among
+// equal ones) and, among the experts holding exactly that key, the lowest
+// index: when one lane holds it, that lane's best; when several do, a wave
+// min of their indices.  The pick's key becomes 0.  (Once no key is left,
+// i.e. the row has fewer real logits than picks, which the argument checks
+// rule out, the round takes the lowest slot, then lane, holding 0.)  The
+// loads are unconditional, the index clamped into the row, so they all go
+// out at once.
 template <int PER_LANE>
-__device__ inline void topk_row(const float* __restrict__ l, int n_experts, int top_k,
-                                int* my_id, float* my_w) {
+__device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int top_k,
+                                 int* my_id, uint32_t* my_key) {
   const int lane = lane_id();
+  float lv[PER_LANE];
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) lv[j] = l[min(lane + 64 * j, n_experts - 1)];
+  // (an empty asm reading every value keeps the compiler from moving a load
+  // under the select below, where it would wait for each load in turn)
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) asm volatile("" : "+v"(lv[j]));
   uint32_t kv[PER_LANE];
 #pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) {
-    const int e = lane + 64 * j;
-    kv[j] = (e < n_experts) ? logit_key(l[e]) : 0u;
-  }
+  for (int j = 0; j < PER_LANE; ++j) kv[j] = lane + 64 * j < n_experts ? logit_key(lv[j]) : 0u;
   uint32_t my_k = 0;
   int id = 0;
   for (int s = 0; s < top_k; ++s) {
     uint32_t lk = kv[0];
+    int lj = 0;
 #pragma unroll
-    for (int j = 1; j < PER_LANE; ++j) lk = max(lk, kv[j]);
+    for (int j = 1; j < PER_LANE; ++j) {
+      lj = kv[j] > lk ? j : lj;
+      lk = max(lk, kv[j]);
+    }
     const uint32_t bk = wave_max_u32(lk);
-    int be = -1;
+    const uint64_t hit = __ballot(lk == bk);
+    int be;
+    if (bk != 0u && __popcll(hit) == 1) {
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      be = 64 * __builtin_amdgcn_readlane(lj, L) + L;
+    } else if (bk != 0u) {
+      be = (int)wave_min_u32(lk == bk ? (uint32_t)(64 * lj + lane) : 0xFFFFFFFFu);
+    } else {
+      be = -1;
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-      const uint64_t hit = __ballot(kv[j] == bk);
-      if (be < 0 && hit != 0) be = 64 * j + __ffsll((unsigned long long)hit) - 1;
+      for (int j = 0; j < PER_LANE; ++j) {
+        const uint64_t z = __ballot(kv[j] == 0u);
+        if (be < 0 && z != 0) be = 64 * j + __ffsll((unsigned long long)z) - 1;
+      }
     }
-    if ((be & 63) == lane) {
+    be = __builtin_amdgcn_readfirstlane(be);
 #pragma unroll
-      for (int j = 0; j < PER_LANE; ++j)
-        if ((be >> 6) == j) kv[j] = 0u;
-    }
+    for (int j = 0; j < PER_LANE; ++j)
+      if (lane == (be & 63) && j == (be >> 6)) kv[j] = 0u;
     if (lane == s) {
       my_k = bk;
       id = be;
     }
   }
-  const float my_sig = 1.0f / (1.0f + exp_rows(-logit_of_key(my_k)));
-  float sum = 0.f;
-  for (int s = 0; s < top_k; ++s) sum += __shfl(my_sig, s, 64);
   *my_id = id;
-  *my_w = my_sig / sum;
+  *my_key = my_k;
+}
+
+// The picks' weights (lane s < top_k: pick s): each pick's sigmoid in its
+// own lane, then their sum in pick order, read lane by lane.
+__device__ inline float topk_weight(uint32_t my_key, int top_k) {
+  const float my_sig = 1.0f / (1.0f + exp_rows(-logit_of_key(my_key)));
+  float sum = 0.f;
+  for (int s = 0; s < top_k; ++s)
+    sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_sig), s));
+  return my_sig / sum;
+}
+
+// Both: lane s < top_k receives pick s and its weight.
+template <int PER_LANE>
+__device__ inline void topk_row(const float* __restrict__ l, int n_experts, int top_k,
+                                int* my_id, float* my_w) {
+  uint32_t my_key;
+  topk_pick<PER_LANE>(l, n_experts, top_k, my_id, &my_key);
+  *my_w = topk_weight(my_key, top_k);
 }
 
 // ------------------------------------------------------------ host side

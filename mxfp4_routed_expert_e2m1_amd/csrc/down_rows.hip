@@ -18,6 +18,7 @@
 // the E8M0 scale folded in, one 16x16x32 bf16 matrix-core op per 32-element
 // block, fp32 FMA with the hidden scale).
 #include <atomic>
+#include <type_traits>
 
 #include "ffn_internal.h"
 
@@ -53,7 +54,12 @@ struct DownRowsArgs {
 // token t).
 // NC: 16-byte pieces of hidden codes each thread copies (a constant, so the
 // number of loads in flight is known when the copy waits).
-template <int NC>
+// ONE: a one-row step.  Its tiles are its valid slots (ids >= 0) in the
+// stable order by expert (by id, then by slot) -- the order the sorted list
+// and offsets of moe_route_group give -- each of one column, then the
+// shared expert's.  Every wave finds them from the ids alone: no round trip
+// for the offsets and no tile-map scan before its weights go out.
+template <int NC, bool ONE>
 __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p,
                                                                     int tiles_cap) {
   extern __shared__ __align__(16) float dyn[];
@@ -79,13 +85,16 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   const int per_row = F / 8;             // 16-byte pieces of codes per row
   const int per_row_s = F / kBlock / 4;  // 16-byte pieces of scales per row
   const int n_pc = R * per_row, n_ps = R * per_row_s;
-  const int srt = tid < n_assign ? p.sorted[tid] : -1;
-  const int idv = tid < n_assign ? p.ids[tid] : -1;
-  const float wv = tid < n_assign ? p.w[tid] : 0.f;
-  // every wave reads the offsets and finds its own first tile, so its
-  // weights go out without waiting for a workgroup barrier
+  // ONE: every wave reads the ids and weights (lane s: slot s); else thread
+  // a reads assignment a's, and every wave reads the offsets and finds its
+  // own first tile, so its weights go out without a workgroup barrier
+  const int ra = ONE ? lane : tid;
+  const int ra_c = min(ra, n_assign - 1);  // (unconditional loads)
+  const int idv_raw = p.ids[ra_c];
+  const float wv_raw = p.w[ra_c];
+  const int srt = (!ONE && tid < n_assign) ? p.sorted[tid] : -1;
   TileMap<16> tm;
-  tm.fetch(p.offsets, p.n_experts);
+  if constexpr (!ONE) tm.fetch(p.offsets, p.n_experts);
   // (copy pieces past the end read piece 0 of hidden row 0, which always
   // exists)
   u32x4 cp[NC];
@@ -101,7 +110,20 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     cs = *(const f32x4*)(p.hs + off);
   }
   __builtin_amdgcn_sched_barrier(0);  // every load of the round trip goes out first
-  tm.count(p.n_experts, p.has_shared, p.rows);
+  const int idv = ra < n_assign ? idv_raw : -1;
+  const float wv = ra < n_assign ? wv_raw : 0.f;
+  // ONE: lane s's place among the valid slots in the stable order, their
+  // number, and the expert of this wave's tile (and of tile 0)
+  int rank1 = 0, nv1 = 0;
+  if constexpr (ONE) {
+    for (int s2 = 0; s2 < p.top_k; ++s2) {
+      const int o = __builtin_amdgcn_readlane(idv, s2);
+      rank1 += o >= 0 && (o < idv || (o == idv && s2 < lane)) ? 1 : 0;
+      nv1 += o >= 0 ? 1 : 0;
+    }
+  } else {
+    tm.count(p.n_experts, p.has_shared, p.rows);
+  }
 
   // this wave's weight stream: row group rg of tile ti, K chunks kg..kg+15
   u32x4 a[kDRGroup];
@@ -127,7 +149,18 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   // (they merge with that tile's misses in L2); with no tile at all (no
   // shared expert and every slot a sentinel) routed expert 0's row group,
   // which always exists.  So the issue is unconditional.
-  {
+  if constexpr (ONE) {
+    const int total = nv1 + p.has_shared;
+    const int want = wave < total ? wave : 0;
+    int4 te0 = int4{0, 0, 0, 0};
+    if (want < nv1) {
+      const uint64_t m = __ballot(idv >= 0 && rank1 == want);
+      te0 = int4{__builtin_amdgcn_readlane(idv, __ffsll((unsigned long long)m) - 1), want, 1, 0};
+    } else if (p.has_shared) {
+      te0 = int4{p.n_experts, 0, 1, 0};
+    }
+    issue_head(te0, 0);
+  } else {
     const int total = tm.n_tiles();
     const Tile t0 = tm.lookup(p.n_experts, p.rows, wave < total ? wave : 0);
     const int4 te0 = t0.expert >= 0 ? int4{t0.expert, t0.start, t0.count, 0} : int4{0, 0, 0, 0};
@@ -137,7 +170,16 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
 
   // the tile map, positions, ids, weights and hidden rows go to LDS while
   // the weights are in flight
-  if (wave == 0) {
+  if (ONE && wave == 0) {
+    // tile r: the valid slot of place r; the combine's partial index of
+    // slot s (its tile's first column), -1 for a sentinel
+    if (idv >= 0) s_tiles[rank1] = int4{idv, rank1, 1, 0};
+    if (lane == 0) {
+      if (p.has_shared) s_tiles[nv1] = int4{p.n_experts, 0, 1, 0};
+      s_ntiles = nv1 + p.has_shared;
+      s_routed = nv1;
+    }
+  } else if (!ONE && wave == 0) {
     int idx = tm.incl - tm.lsum;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -155,8 +197,8 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
       s_routed = tm.routed;
     }
   }
-  if (srt >= 0) s_pos[srt] = tid;
-  if (tid < n_assign) s_wt[tid] = wv;
+  if (!ONE && srt >= 0) s_pos[srt] = tid;
+  if (!ONE && tid < n_assign) s_wt[tid] = wv;
   uint16_t* hl = (uint16_t*)(part + (size_t)tiles_cap * 256);
   float* hsl = (float*)(hl + (size_t)R * F);
 #pragma unroll
@@ -170,7 +212,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   // the combine's index of each assignment's partial row (-1: a sentinel),
   // found now, while the weights are in flight: s_pos[a] becomes
   // (tile * 16 + column) * 16 (only thread a reads or writes entry a)
-  if (tid < n_assign) {
+  if (!ONE && tid < n_assign) {
     int pidx = -1;
     if (idv >= 0) {
       const int pos = s_pos[tid];
@@ -240,6 +282,29 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   __syncthreads();
 
   // y[t][16 rg + r] = sum over the token's slots in slot order, shared last
+  if constexpr (ONE) {
+    // (threads 0-15: row r = tid; each slot's partial index and weight come
+    // from wave 0's lanes, all of the slots' partials are read at once)
+    if (tid < 16) {
+      const int pl = idv >= 0 ? rank1 * 256 : -1;
+      float pv[MOE_MAX_TOP_K];
+#pragma unroll
+      for (int s2 = 0; s2 < MOE_MAX_TOP_K; ++s2) {
+        const int pi = s2 < p.top_k ? __builtin_amdgcn_readlane(pl, s2) : -1;
+        pv[s2] = part[max(pi, 0) + tid];
+      }
+      float v = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < MOE_MAX_TOP_K; ++s2) {
+        if (s2 < p.top_k && __builtin_amdgcn_readlane(pl, s2) >= 0)
+          v = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), s2)),
+                   pv[s2], v);  // as the combine kernel
+      }
+      if (p.has_shared) v = v + part[nv1 * 256 + tid];
+      p.y[16 * rg + tid] = v;
+    }
+    return;
+  }
   for (int e = tid; e < p.rows * 16; e += kDRThreads) {
     const int t = e >> 4, r = e & 15;
     float v = 0.f;
@@ -325,42 +390,37 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
   // allow more than 64 KiB of dynamic LDS: once per device and variant (an
   // atomic flag: concurrent first calls from several host threads both set
   // the attribute, which is harmless)
-  static std::atomic<bool> lds_raised[64][17];
+  static std::atomic<bool> lds_raised[64][17][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  const bool one = rows == 1;
   const void* fn = nullptr;
+  auto pick = [&](auto nc_c) {
+    constexpr int NC = decltype(nc_c)::value;
+    fn = one ? (const void*)down_rows_kernel<NC, true> : (const void*)down_rows_kernel<NC, false>;
+  };
   switch (nc) {
-    case 1: fn = (const void*)down_rows_kernel<1>; break;
-    case 2: fn = (const void*)down_rows_kernel<2>; break;
-    case 3: fn = (const void*)down_rows_kernel<3>; break;
-    case 4: fn = (const void*)down_rows_kernel<4>; break;
-    case 5: fn = (const void*)down_rows_kernel<5>; break;
-    case 6: fn = (const void*)down_rows_kernel<6>; break;
-    case 7: fn = (const void*)down_rows_kernel<7>; break;
-    case 8: fn = (const void*)down_rows_kernel<8>; break;
-    case 12: fn = (const void*)down_rows_kernel<12>; break;
-    default: fn = (const void*)down_rows_kernel<16>; break;
+    case 1: pick(std::integral_constant<int, 1>{}); break;
+    case 2: pick(std::integral_constant<int, 2>{}); break;
+    case 3: pick(std::integral_constant<int, 3>{}); break;
+    case 4: pick(std::integral_constant<int, 4>{}); break;
+    case 5: pick(std::integral_constant<int, 5>{}); break;
+    case 6: pick(std::integral_constant<int, 6>{}); break;
+    case 7: pick(std::integral_constant<int, 7>{}); break;
+    case 8: pick(std::integral_constant<int, 8>{}); break;
+    case 12: pick(std::integral_constant<int, 12>{}); break;
+    default: pick(std::integral_constant<int, 16>{}); break;
   }
-  if (!lds_raised[dev][nc].load(std::memory_order_acquire)) {
+  if (!lds_raised[dev][nc][one].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDownRowsMaxLds) !=
         hipSuccess)
       return MOE_ERR_HIP;
-    lds_raised[dev][nc].store(true, std::memory_order_release);
+    lds_raised[dev][nc][one].store(true, std::memory_order_release);
   }
   const int cap = tiles_bound(L, rows);
-  const dim3 grid((unsigned)pd.rg), block(kDRThreads);
-  switch (nc) {
-    case 1: hipLaunchKernelGGL(down_rows_kernel<1>, grid, block, lds, s, a, cap); break;
-    case 2: hipLaunchKernelGGL(down_rows_kernel<2>, grid, block, lds, s, a, cap); break;
-    case 3: hipLaunchKernelGGL(down_rows_kernel<3>, grid, block, lds, s, a, cap); break;
-    case 4: hipLaunchKernelGGL(down_rows_kernel<4>, grid, block, lds, s, a, cap); break;
-    case 5: hipLaunchKernelGGL(down_rows_kernel<5>, grid, block, lds, s, a, cap); break;
-    case 6: hipLaunchKernelGGL(down_rows_kernel<6>, grid, block, lds, s, a, cap); break;
-    case 7: hipLaunchKernelGGL(down_rows_kernel<7>, grid, block, lds, s, a, cap); break;
-    case 8: hipLaunchKernelGGL(down_rows_kernel<8>, grid, block, lds, s, a, cap); break;
-    case 12: hipLaunchKernelGGL(down_rows_kernel<12>, grid, block, lds, s, a, cap); break;
-    default: hipLaunchKernelGGL(down_rows_kernel<16>, grid, block, lds, s, a, cap); break;
-  }
+  void* args[] = {&a, (void*)&cap};
+  if (hipLaunchKernel(fn, dim3((unsigned)pd.rg), dim3(kDRThreads), args, lds, s) != hipSuccess)
+    return MOE_ERR_HIP;
   return launch_status();
 }
 

@@ -86,75 +86,62 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
 
   // The call's tiles (one round trip, wave 0) and sorted list go to LDS.
   int n_items = n_rb;
+  int my_id = 0;        // F1, wave 0: lane s < top_k holds pick s
+  uint32_t my_key = 0;  // and its logit key
   if constexpr (F1) {
-    // One row, straight from the layer input.  Every workgroup quantises the
-    // row into LDS (one 8-element piece per thread: K/8 = NT) and wave 0
-    // routes it (top-k of the logits), all in one round trip, so no earlier
-    // launch has to finish first.  With one row every picked expert is a
-    // tile of one column and its sorted position is its rank by expert id
-    // (the picks are distinct); the shared expert's tile follows.
-    // Workgroup 0 also writes what the quantiser and the router would:
-    // codes, scales, ids, weights, counts, offsets, sorted.
-    float v[8];
-    {
-      const float4 x0 = *(const float4*)(in.x + 8 * tid);
-      const float4 x1 = *(const float4*)(in.x + 8 * tid + 4);
-      v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-      v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-    }
-    int my_id = 0;
-    float my_w = 0.f;
-    if (wave == 0) topk_row<TOPK_PL>(in.logits, p.n_experts, p.top_k, &my_id, &my_w);
-    uint32_t w0, w1;
-    const float dq = q8_quant8(v, w0, w1);
-    *(u32x2*)(s_q8 + 8 * tid) = u32x2{w0, w1};
-    if ((tid & 3) == 0) s_qs[tid >> 2] = dq;
-    if (blockIdx.x == 0) {
-      *(u32x2*)(in.q + 8 * tid) = u32x2{w0, w1};
-      if ((tid & 3) == 0) in.qs[tid >> 2] = dq;
-    }
-    if (tid < 32) s_amax[tid >> 4][tid & 15] = 0u;
+    // One row, straight from the layer input.  Wave 0 routes it (top-k of
+    // the logits) while the other waves quantise it into LDS (8 elements
+    // per piece, K/8 = NT pieces: one per thread of waves 1.., and wave 0's
+    // pieces by wave 1), all in one round trip, so no earlier launch has to
+    // finish first.  With one row every picked expert is a tile of one
+    // column and its sorted position is its rank by expert id (the picks
+    // are distinct); the shared expert's tile follows.  Workgroup 0 also
+    // writes what the quantiser and the router would: codes, scales, ids,
+    // weights, counts, offsets, sorted (after its first loads go out).
+    auto quant_piece = [&](int pc, const float4 x0, const float4 x1) {
+      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t w0, w1;
+      const float dq = q8_quant8(v, w0, w1);
+      *(u32x2*)(s_q8 + 8 * pc) = u32x2{w0, w1};
+      if ((pc & 3) == 0) s_qs[pc >> 2] = dq;
+      if (blockIdx.x == 0) {
+        *(u32x2*)(in.q + 8 * pc) = u32x2{w0, w1};
+        if ((pc & 3) == 0) in.qs[pc >> 2] = dq;
+      }
+    };
     if (wave == 0) {
+      topk_pick<TOPK_PL>(in.logits, p.n_experts, p.top_k, &my_id, &my_key);
       // (an id < 0 -- the router found no pick, e.g. NaN logits, outside the
       // contract -- is a sentinel as in moe_route_group: in no tile)
       const bool ok = lane < p.top_k && my_id >= 0;
       int rank = 0, n_valid = 0;
       for (int s2 = 0; s2 < p.top_k; ++s2) {
-        const int o = __shfl(my_id, s2, 64);
+        const int o = __builtin_amdgcn_readlane(my_id, s2);
         rank += o >= 0 && o < my_id ? 1 : 0;
         n_valid += o >= 0 ? 1 : 0;
       }
-      if (lane < p.top_k) {
-        s_rid[lane] = my_id;
-        if (blockIdx.x == 0) {
-          in.ids[lane] = my_id;
-          in.w[lane] = my_w;
-          if (lane >= n_valid) in.sorted[lane] = -1;
-        }
-      }
+      if (lane < p.top_k) s_rid[lane] = my_id;
       if (ok) {
         s_sorted[rank] = lane;
         s_tiles[rank] = int4{my_id, rank, 1, 0};
-        if (blockIdx.x == 0) in.sorted[rank] = lane;
       }
       if (lane == 0) {
         if (p.has_shared) s_tiles[n_valid] = int4{p.n_experts, 0, 1, 0};
         s_ntiles = n_valid + p.has_shared;
       }
+    } else {
+      const float4* xv = (const float4*)in.x;
+      const float4 a0 = xv[2 * tid], a1 = xv[2 * tid + 1];
+      float4 b0, b1;
+      if (wave == 1) {
+        b0 = xv[2 * lane];
+        b1 = xv[2 * lane + 1];
+      }
+      quant_piece(tid, a0, a1);
+      if (wave == 1) quant_piece(lane, b0, b1);
+      if (tid < 96) s_amax[(tid - 64) >> 4][tid & 15] = 0u;
     }
     lds_barrier();
-    if (blockIdx.x == 0) {
-      for (int e = tid; e <= p.n_experts; e += NT) {
-        int below = 0, same = 0;
-        for (int s2 = 0; s2 < p.top_k; ++s2) {
-          const int o = s_rid[s2];
-          below += o >= 0 && o < e ? 1 : 0;
-          same += o == e ? 1 : 0;
-        }
-        in.offsets[e] = below;
-        if (e < p.n_experts) in.counts[e] = same;
-      }
-    }
     n_items = uniform(s_ntiles) * n_rb;
   } else if constexpr (PASS != STREAM_MATVEC) {
     // sorted list and tile map are loaded together: one round trip
@@ -181,8 +168,42 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
     lds_barrier();
     n_items = uniform(s_ntiles) * n_rb;
   }
+  // F1, workgroup 0: the router's outputs for the down stage
+  auto publish = [&]() {
+    if constexpr (F1) {
+      if (blockIdx.x != 0) return;
+      if (wave == 0) {
+        const float my_w = topk_weight(my_key, p.top_k);
+        int n_valid = 0;
+        for (int s2 = 0; s2 < p.top_k; ++s2) n_valid += __builtin_amdgcn_readlane(my_id, s2) >= 0;
+        if (lane < p.top_k) {
+          in.ids[lane] = my_id;
+          in.w[lane] = my_w;
+          if (lane >= n_valid) in.sorted[lane] = -1;
+        }
+      }
+      if (tid < p.top_k && s_rid[tid] >= 0) {
+        int rank = 0;
+        for (int s2 = 0; s2 < p.top_k; ++s2) rank += s_rid[s2] >= 0 && s_rid[s2] < s_rid[tid];
+        in.sorted[rank] = tid;
+      }
+      for (int e = tid; e <= p.n_experts; e += NT) {
+        int below = 0, same = 0;
+        for (int s2 = 0; s2 < p.top_k; ++s2) {
+          const int o = s_rid[s2];
+          below += o >= 0 && o < e ? 1 : 0;
+          same += o == e ? 1 : 0;
+        }
+        in.offsets[e] = below;
+        if (e < p.n_experts) in.counts[e] = same;
+      }
+    }
+  };
   int it = blockIdx.x;
-  if (it >= n_items) return;  // the same for the whole workgroup
+  if (it >= n_items) {  // the same for the whole workgroup
+    publish();
+    return;
+  }
 
   // per-item values, all wave-uniform
   struct Item {
@@ -355,6 +376,7 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
   issue_s(cur, sv);
 #pragma unroll
   for (int kk = 0; kk < kSAhead; ++kk) issue(cur, br_cur, kk);
+  publish();  // (its first loads are in flight)
 
   // One item: (NEXT) the next item's scales into the other scale registers,
   // then compute chunk kk and issue the chunk kSAhead places further on in
