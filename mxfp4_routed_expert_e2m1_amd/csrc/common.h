@@ -472,30 +472,35 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Min of an unsigned value over the whole wave (the same DPP steps).
-__device__ inline uint32_t wave_min_u32(uint32_t v) {
-  auto f = [](uint32_t u) { return __builtin_bit_cast(float, u); };
-  auto u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
-  v = min(v, u(dpp_mov<0xB1>(f(v))));
-  v = min(v, u(dpp_mov<0x4E>(f(v))));
-  v = min(v, u(dpp_mov<0x141>(f(v))));
-  v = min(v, u(dpp_mov<0x140>(f(v))));
-  v = min(v, u(dpp_rows<0x142, 0xA>(f(v))));
-  v = min(v, u(dpp_rows<0x143, 0xC>(f(v))));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+// Max of a 64-bit unsigned value over the whole wave (the DPP steps of
+// wave_max on both halves), returned wave-uniform.
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+  auto step = [](uint64_t a, uint64_t b) { return b > a ? b : a; };
+  auto hi = [](uint64_t x) { return __builtin_bit_cast(float, (uint32_t)(x >> 32)); };
+  auto lo = [](uint64_t x) { return __builtin_bit_cast(float, (uint32_t)x); };
+  auto mk = [](float h, float l) {
+    return ((uint64_t)__builtin_bit_cast(uint32_t, h) << 32) | __builtin_bit_cast(uint32_t, l);
+  };
+  v = step(v, mk(dpp_mov<0xB1>(hi(v)), dpp_mov<0xB1>(lo(v))));
+  v = step(v, mk(dpp_mov<0x4E>(hi(v)), dpp_mov<0x4E>(lo(v))));
+  v = step(v, mk(dpp_mov<0x141>(hi(v)), dpp_mov<0x141>(lo(v))));
+  v = step(v, mk(dpp_mov<0x140>(hi(v)), dpp_mov<0x140>(lo(v))));
+  v = step(v, mk(dpp_rows<0x142, 0xA>(hi(v)), dpp_rows<0x142, 0xA>(lo(v))));
+  v = step(v, mk(dpp_rows<0x143, 0xC>(hi(v)), dpp_rows<0x143, 0xC>(lo(v))));
+  const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 63);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  return ((uint64_t)h << 32) | l;
 }
 
 // One wave: the top_k picks of one row of logits; lane s < top_k receives
 // pick s (its expert and its key).  Expert e sits in lane e % 64, slot
-// e / 64.  Each round takes the largest remaining key (a wave max over
-// every lane's best; a lane's best is its largest key, the lower slot among
-// equal ones) and, among the experts holding exactly that key, the lowest
-// index: when one lane holds it, that lane's best; when several do, a wave
-// min of their indices.  The pick's key becomes 0.  (Once no key is left,
-// i.e. the row has fewer real logits than picks, which the argument checks
-// rule out, the round takes the lowest slot, then lane, holding 0.)  The
-// loads are unconditional, the index clamped into the row, so they all go
-// out at once.
+// e / 64, as the composite (key << 32) | ~e: a larger composite is a larger
+// key, then a lower index.  Each round takes the wave max of the lanes'
+// largest composites; the pick's key half becomes 0 (its index half stays,
+// so once no key is left -- the row has fewer real logits than picks, which
+// the argument checks rule out -- a round takes the lowest index holding 0,
+// picked or not).  The loads are unconditional, the index clamped into the
+// row, so they all go out at once.
 template <int PER_LANE>
 __device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int top_k,
                                  int* my_id, uint32_t* my_key) {
@@ -507,39 +512,25 @@ __device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int
   // under the select below, where it would wait for each load in turn)
 #pragma unroll
   for (int j = 0; j < PER_LANE; ++j) asm volatile("" : "+v"(lv[j]));
-  uint32_t kv[PER_LANE];
+  uint64_t c[PER_LANE];
 #pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) kv[j] = lane + 64 * j < n_experts ? logit_key(lv[j]) : 0u;
+  for (int j = 0; j < PER_LANE; ++j) {
+    const int e = lane + 64 * j;
+    const uint32_t k = e < n_experts ? logit_key(lv[j]) : 0u;
+    c[j] = ((uint64_t)k << 32) | (uint32_t)~e;
+  }
   uint32_t my_k = 0;
   int id = 0;
   for (int s = 0; s < top_k; ++s) {
-    uint32_t lk = kv[0];
-    int lj = 0;
+    uint64_t lc = c[0];
 #pragma unroll
-    for (int j = 1; j < PER_LANE; ++j) {
-      lj = kv[j] > lk ? j : lj;
-      lk = max(lk, kv[j]);
-    }
-    const uint32_t bk = wave_max_u32(lk);
-    const uint64_t hit = __ballot(lk == bk);
-    int be;
-    if (bk != 0u && __popcll(hit) == 1) {
-      const int L = __ffsll((unsigned long long)hit) - 1;
-      be = 64 * __builtin_amdgcn_readlane(lj, L) + L;
-    } else if (bk != 0u) {
-      be = (int)wave_min_u32(lk == bk ? (uint32_t)(64 * lj + lane) : 0xFFFFFFFFu);
-    } else {
-      be = -1;
-#pragma unroll
-      for (int j = 0; j < PER_LANE; ++j) {
-        const uint64_t z = __ballot(kv[j] == 0u);
-        if (be < 0 && z != 0) be = 64 * j + __ffsll((unsigned long long)z) - 1;
-      }
-    }
-    be = __builtin_amdgcn_readfirstlane(be);
+    for (int j = 1; j < PER_LANE; ++j) lc = c[j] > lc ? c[j] : lc;
+    const uint64_t bc = wave_max_u64(lc);
+    const int be = (int)~(uint32_t)bc;
+    const uint32_t bk = (uint32_t)(bc >> 32);
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j)
-      if (lane == (be & 63) && j == (be >> 6)) kv[j] = 0u;
+      if (lane == (be & 63) && j == (be >> 6)) c[j] &= 0xFFFFFFFFull;
     if (lane == s) {
       my_k = bk;
       id = be;
@@ -566,6 +557,27 @@ __device__ inline void topk_row(const float* __restrict__ l, int n_experts, int 
   uint32_t my_key;
   topk_pick<PER_LANE>(l, n_experts, top_k, my_id, &my_key);
   *my_w = topk_weight(my_key, top_k);
+}
+
+// Raw buffer loads: a wave-uniform resource (base, size) in scalar registers,
+// a per-lane byte offset in one vector register, a uniform byte offset in a
+// scalar register and a constant in the instruction.  Offsets at or past the
+// resource size read as zero (the hardware range check covers the per-lane
+// offset and the constant).  The explicit form also keeps the compiler
+// from merging or re-deriving addresses per load.
+constexpr int kBufDword3 = 0x00020000;  // raw 32-bit data format (gfx9 family)
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufDword3);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ inline uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
 // ------------------------------------------------------------ host side

@@ -34,7 +34,7 @@ struct DownRowsArgs {
   int64_t dn_stride;
   const uint8_t* dn_shared;
   int64_t nib_bytes;
-  int kc_total, sc_total;
+  int kc_total, sc_total, rg_total;
   const int32_t* offsets;
   const int32_t* sorted;
   const int32_t* ids;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
   __shared__ int s_ptile[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // sorted position -> tile
   __shared__ float s_wt[MOE_MAX_DECODE_ROWS * MOE_MAX_TOP_K];  // the step's weights
   __shared__ int s_ntiles, s_routed;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   const int F = p.kc_total * kChunkK;
   const int rg = blockIdx.x;  // 16 output rows 16*rg .. 16*rg+15
   const int col = lane & 15, g8 = 8 * (lane >> 4);
@@ -125,25 +125,32 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     tm.count(p.n_experts, p.has_shared, p.rows);
   }
 
-  // this wave's weight stream: row group rg of tile ti, K chunks kg..kg+15
+  // this wave's weight stream: row group rg of tile ti, K chunks kg..kg+15,
+  // as raw buffer loads (one resource per tile, the chunk's offset in a
+  // scalar register, the lane's in a vector register)
   u32x4 a[kDRGroup];
   uint32_t s[kDRGroup];
+  const uint32_t blob_bytes = (uint32_t)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256);
+  const uint32_t nib_row = (uint32_t)rg * (uint32_t)p.kc_total * 1024u;
+  const uint32_t scl_row = (uint32_t)p.nib_bytes + (uint32_t)rg * (uint32_t)p.sc_total * 256u;
+  const uint32_t a_lane = (uint32_t)lane * 16u, s_lane = (uint32_t)col * 16u;
+  auto tile_rsrc = [&](const int4 te) {
+    const int ex = uniform(te.x);
+    const uint8_t* blob = ex == p.n_experts ? p.dn_shared : p.dn + (int64_t)ex * p.dn_stride;
+    return buf_rsrc(blob, blob_bytes);
+  };
   // chunk kk of the group at kg (a group shorter than kDRGroup repeats its
   // last chunk, so every issue is unconditional and the count in flight a
   // constant)
-  auto issue_chunk = [&](const int4 te, int kg, int kk) {
-    const uint8_t* blob =
-        te.x == p.n_experts ? p.dn_shared : p.dn + (int64_t)te.x * p.dn_stride;
-    const u32x4* nib = (const u32x4*)blob;
-    const uint8_t* scl = blob + p.nib_bytes;
+  auto issue_chunk = [&](__amdgpu_buffer_rsrc_t r, int kg, int kk) {
     const int kc = kg + min(kk, min(kDRGroup, p.kc_total - kg) - 1);
-    a[kk] = nib[((int64_t)rg * p.kc_total + chunk_slot(kc, p.kc_total)) * 64 + lane];
-    s[kk] = *(const uint32_t*)(scl + (((int64_t)rg * p.sc_total + (kc >> 2)) * 16 + col) * 16 +
-                               (kc & 3) * 4);
+    a[kk] = buf_load16(r, a_lane, nib_row + (uint32_t)chunk_slot(kc, p.kc_total) * 1024u);
+    s[kk] = buf_load4(r, s_lane, scl_row + (uint32_t)(kc >> 2) * 256u + (uint32_t)(kc & 3) * 4u);
   };
   auto issue_head = [&](const int4 te, int kg) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(te);
 #pragma unroll
-    for (int kk = 0; kk < kDRAhead; ++kk) issue_chunk(te, kg, kk);
+    for (int kk = 0; kk < kDRAhead; ++kk) issue_chunk(r, kg, kk);
   };
   // Every wave issues: a wave without a tile repeats tile 0's addresses
   // (they merge with that tile's misses in L2); with no tile at all (no
@@ -224,6 +231,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
 
   for (int ti = wave; ti < n_tiles; ti += kDRWaves) {
     const int4 te = s_tiles[ti];
+    const __amdgpu_buffer_rsrc_t rt = tile_rsrc(te);
     const bool shared = te.x == p.n_experts;
     const int ccol = col < te.z ? col : 0;  // columns past the tile repeat column 0
     const int lrow = shared ? n_assign + te.y + ccol : te.y + ccol;  // row of the LDS copy
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
         }
         if (kk + kDRAhead < kDRGroup) {
           __builtin_amdgcn_sched_barrier(0);  // keep the issue after this chunk's math
-          issue_chunk(te, kg, kk + kDRAhead);
+          issue_chunk(rt, kg, kk + kDRAhead);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -366,6 +374,7 @@ int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const floa
   a.nib_bytes = pd.nib_bytes;
   a.kc_total = (int)pd.kc;
   a.sc_total = (int)pd.sc;
+  a.rg_total = (int)pd.rg;
   a.offsets = offsets;
   a.sorted = sorted;
   a.ids = ids;

@@ -42,24 +42,6 @@ constexpr int kSKPW = 4;  // K chunks of a wave per item
 constexpr int kSAhead = STREAM_AHEAD;
 static_assert(kSAhead >= 1 && kSAhead <= kSKPW, "prefetch distance");
 
-// Raw buffer loads: a wave-uniform resource (base, size) in scalar registers,
-// a per-lane byte offset in one vector register, a uniform byte offset in a
-// scalar register and a constant in the instruction.  Offsets at or past the
-// resource size read as zero (the hardware range check covers the per-lane
-// offset and the constant).  The explicit form also keeps the compiler
-// from merging or re-deriving addresses per load.
-constexpr int kBufDword3 = 0x00020000;  // raw 32-bit data format (gfx9 family)
-__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kBufDword3);
-}
-__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
-
 // F1 (gate/up only): a one-row step straight from the layer input; see the
 // prologue.
 template <int PASS, int W, bool F1, int TOPK_PL = 4>
