@@ -496,11 +496,11 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
 // pick s (its expert and its key).  Expert e sits in lane e % 64, slot
 // e / 64, as the composite (key << 32) | ~e: a larger composite is a larger
 // key, then a lower index.  Each round takes the wave max of the lanes'
-// largest composites; the pick's key half becomes 0 (its index half stays,
-// so once no key is left -- the row has fewer real logits than picks, which
-// the argument checks rule out -- a round takes the lowest index holding 0,
-// picked or not).  The loads are unconditional, the index clamped into the
-// row, so they all go out at once.
+// largest composites; the pick's key becomes 0.  A round that finds no key
+// left (only logits whose key is 0, the all-ones NaN, remain: outside the
+// contract) yields the sentinel -1, never an expert past the row.  The loads
+// are unconditional, the index clamped into the row, so they all go out at
+// once.
 template <int PER_LANE>
 __device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int top_k,
                                  int* my_id, uint32_t* my_key) {
@@ -533,7 +533,7 @@ __device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int
       if (lane == (be & 63) && j == (be >> 6)) c[j] &= 0xFFFFFFFFull;
     if (lane == s) {
       my_k = bk;
-      id = be;
+      id = bk != 0u ? be : -1;
     }
   }
   *my_id = id;
