@@ -58,14 +58,14 @@ GEMM_SIMDS = 1024
 # (hash below, over the device code in csrc/): after any change to it the
 # benchmark reports traffic as null.
 TRAFFIC_DOC = "profiles/hbm_traffic_counters.md (moe_counters under rocprofv3 --pmc, offline)"
-TRAFFIC_SRC = "b8fde70da0282b94"
+TRAFFIC_SRC = "86719f9b4bd97a7d"
 TRAFFIC = {  # (workload, rows[, variant]): (read bytes, written bytes)
-    ("decode", 1): (2 * 30787.8 * 1024, 48.6 * 1024),
-    ("decode-batch", 16): (2 * 349796.3 * 1024, 677.1 * 1024),
-    ("decode-batch", 16, "hot"): (2 * 171095.7 * 1024, 673.0 * 1024),
-    ("prefill", 4096): (2 * 1413344.2 * 1024, 106591.2 * 1024),
-    ("prefill", 512): (2 * 1206866.2 * 1024, 13596.2 * 1024),
-    ("matvec", 5): (2 * 15414.9 * 1024, 280.0 * 1024),
+    ("decode", 1): (2 * 30806.5 * 1024, 48.6 * 1024),
+    ("decode-batch", 16): (2 * 349806.1 * 1024, 676.9 * 1024),
+    ("decode-batch", 16, "hot"): (2 * 171091.0 * 1024, 672.8 * 1024),
+    ("prefill", 4096): (2 * 1281705.0 * 1024, 93876.4 * 1024),
+    ("prefill", 512): (2 * 1161408.0 * 1024, 11925.5 * 1024),
+    ("matvec", 5): (2 * 15407.5 * 1024, 280.0 * 1024),
 }
 
 
