@@ -562,7 +562,12 @@ __device__ inline void gemm_rows(const GemmArgs& p, Tile t, int& raw_b, int& raw
   c.t = t;
   c.shared = t.expert == p.n_experts;
   c.row0 = c.shared ? (int64_t)p.rows * p.top_k + t.start : t.start;
-  const int wave = uniform((int)(threadIdx.x >> 6)), lane = (int)(threadIdx.x & 63);
+  const int wave = uniform((int)(threadIdx.x >> 6));
+  // (the lane index passes an empty asm, so the rows below are derived from
+  // it afresh for each item: held across the K loop, the derived values were
+  // spilled, and the reload's wait also waited for the chunks in flight)
+  int lane = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(lane));
   raw_b = gemm_brow_raw<PASS>(p, c, 16 * gemm_b_tg<BM>(wave) + (lane & 15));
   raw_d = gemm_brow_raw<PASS>(p, c, 16 * (4 * max(gemm_d_wave<BM>(wave), 0) + (lane >> 4)) +
                                         (lane & 15));
@@ -657,18 +662,23 @@ __device__ inline Tile tile_at(const TileList& tl, int n_experts, int rows, int 
 // and the live tiles spread over all eight XCDs.  Tiles are numbered with
 // the shared expert's (all full but the last) first, so the longest items
 // start first and the short routed tiles fill the tail.
-//   128-row tiles: persistent workgroups, one per CU (block b runs on XCD
-//   b % 8 and takes that XCD's items b / 8, b / 8 + G, ... for G workgroups
-//   per XCD).  Each item's tile is found in a list built once into LDS, and
-//   the next item's tile, rows and first chunks go out before this item's
-//   epilogue, so no item waits for its own prologue.
-//   32-row tiles (two workgroups per CU): one item per workgroup.
+// Persistent workgroups (one per CU for 128-row tiles, two for 32-row
+// tiles): block b runs on XCD b % 8 and takes that XCD's items b / 8,
+// b / 8 + G, ... for G workgroups per XCD.  Each item's tile is found in a
+// list built once into LDS, and the next item's tile, rows and first chunks
+// go out before this item's epilogue, so no item waits for its own prologue.
+#ifndef GEMM_SHORT_PERSISTENT
+#define GEMM_SHORT_PERSISTENT 1
+#endif
+template <int BM> constexpr bool gemm_persistent() {
+  return BM == kBMFull || GEMM_SHORT_PERSISTENT;
+}
 template <int PASS, int BM>
 __global__ __launch_bounds__(gemm_waves<BM>() * 64, 2) void gemm_kernel(GemmArgs p) {
   __shared__ Stage<BM> ring[kRing];
   const int n_nb = p.rg_total / kBNGroups;
   const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
-  if constexpr (BM == kBMFull) {
+  if constexpr (gemm_persistent<BM>()) {
     __shared__ TileList s_tl;
     __shared__ int s_routed, s_shared;
     if (threadIdx.x < 64) {  // wave 0 counts the tiles (TileMap) and lists them in LDS
@@ -787,11 +797,12 @@ int prefill_run(const moe_layer_t* L, int stages, const int8_t* q, int64_t ld_q,
 
   auto launch = [&](int pass, GemmArgs& g) {
     g.n_items = tiles * (g.rg_total / kBNGroups);
-    // 32-row tiles: one workgroup per item; 128-row tiles: persistent, at
-    // most one per CU (a multiple of 8, one share per XCD)
+    // persistent workgroups: at most one per CU (128-row tiles) or two
+    // (32-row tiles), a multiple of 8 (one share per XCD); else one per item
     const unsigned items = (unsigned)((tiles + 7) / 8 * 8 * (g.rg_total / kBNGroups));
     const unsigned cus8 = (unsigned)std::max(8, device_cu_count() / 8 * 8);
-    const unsigned grid = short_tiles ? items : std::min(items, cus8);
+    const unsigned grid = short_tiles ? (gemm_persistent<kBMShort>() ? std::min(items, 2 * cus8) : items)
+                                      : std::min(items, cus8);
     const dim3 block(gemm_waves<kBMFull>() * 64), block_s(gemm_waves<kBMShort>() * 64);
     if (pass == GEMM_GATEUP) {
       if (short_tiles) hipLaunchKernelGGL((gemm_kernel<GEMM_GATEUP, kBMShort>), dim3(grid), block_s, 0, s, g);
