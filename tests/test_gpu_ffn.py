@@ -385,6 +385,28 @@ def test_decode_step_graph_replays_match_eager():
         assert torch.isfinite(other[-1]).all()
 
 
+def test_decode_step_one_row_all_ones_nan_logits():
+    """The one-row step from logits with only 3 real values (the rest the
+    all-ones NaN, outside the contract): its ids, counts, offsets and sorted
+    list are moe_route_group's -- 3 picks, then sentinels -- and it runs
+    (only the picks' weights are NaN)."""
+    c = synth.DECODE
+    layer = layer_for(DSV4, c["seed"])
+    rng = np.random.default_rng(23)
+    bits = np.full((1, DSV4.n_experts), 0xFFFFFFFF, np.uint32)
+    ex = rng.choice(DSV4.n_experts, 3, replace=False)
+    bits[0, ex] = rng.standard_normal(3).astype(np.float32).view(np.uint32)
+    lg = torch.from_numpy(bits.view(np.float32)).to(DEV)
+    x = torch.from_numpy(synth.activations(c["seed"], 710, 1, DSV4.d_model)).to(DEV)
+    outs = m.moe_ffn_decode_step(layer, x, lg)
+    ids, w, counts, offsets, srt = m.moe_route_group(lg, DSV4.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[2], ids) and torch.equal(outs[4], counts)
+    assert torch.equal(outs[5], offsets) and torch.equal(outs[6], srt)
+    got = ids.cpu().numpy()[0]
+    assert sorted(got[:3].tolist()) == sorted(ex.tolist()) and np.all(got[3:] == -1)
+
+
 def test_decode_exact_rows_across_batch_sizes():
     # Exact rows ([strix] "The exact-rows contract"): a row's output does not
     # depend on the rows sharing its step.  The same rows decoded all 16

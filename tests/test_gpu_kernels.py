@@ -123,6 +123,42 @@ def test_route_group_tiny_and_ties():
     _route_case(synth.normal(9, 11, (3, 6)), 6)
 
 
+def _all_ones_nan_rows(rows, n_experts, live):
+    """Logits whose bits are all ones (a NaN whose order key is 0) for every
+    expert but `live` finite ones per row, and those rows' expected picks."""
+    rng = np.random.default_rng(17)
+    bits = np.full((rows, n_experts), 0xFFFFFFFF, np.uint32)
+    picks = []
+    for r in range(rows):
+        ex = rng.choice(n_experts, live, replace=False)
+        vals = rng.standard_normal(live).astype(np.float32)
+        bits[r, ex] = vals.view(np.uint32)
+        picks.append([int(e) for e in ex[np.lexsort((ex, -vals))]])  # logit desc, index asc
+    return bits.view(np.float32), picks
+
+
+@pytest.mark.parametrize("rows", [1, 4, 512])
+def test_route_group_all_ones_nan_logits_yield_sentinels(rows):
+    """Fewer real logits than picks (outside the contract): the remaining
+    picks are sentinels, never an expert past the row, and the grouping
+    counts only the real ones."""
+    E, k, live = 256, 6, 3
+    lg, picks = _all_ones_nan_rows(rows, E, live)
+    ids, w, counts, offsets, srt = m.moe_route_group(torch.from_numpy(lg).to(DEV), k)
+    _sync()
+    ids = ids.cpu().numpy()
+    want = np.array([p + [-1] * (k - live) for p in picks], np.int32)
+    np.testing.assert_array_equal(ids, want)
+    c = np.bincount(want[want >= 0], minlength=E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(c)]))
+    flat = want.reshape(-1)
+    order = [a for a in np.lexsort((np.arange(flat.size), flat)) if flat[a] >= 0]
+    got = srt.cpu().numpy()
+    np.testing.assert_array_equal(got[: len(order)], order)
+    assert np.all(got[len(order): rows * k] == -1)
+
+
 def test_route_group_zero_rows():
     lg = torch.zeros((0, 256), device=DEV)
     ids, w, counts, offsets, srt = m.moe_route_group(lg, 6)
