@@ -48,12 +48,13 @@ constexpr int kFusedMaxAssign = kGroupWaves * MOE_MAX_TOP_K;
 
 // Each wave owns a contiguous range of assignment indices (a multiple of 64)
 // and walks it in 64-wide pieces, kGroupWindow pieces per round trip of id
-// loads.  Pass 1 counts each wave's assignments per expert; one scan turns
-// the counts into each wave's base per expert (the expert's offset plus the
-// counts of the earlier waves); pass 2 scatters each wave's range in order,
-// a lane's position being its wave's running base for the expert plus its
-// rank among the lower lanes with the same expert.  The running bases are
-// private to a wave, so the scatter needs no workgroup barrier.
+// loads.  Pass 1 counts each wave's assignments per expert (LDS atomic adds
+// into the wave's own row: a count does not depend on their order); one scan
+// turns the counts into each wave's base per expert (the expert's offset
+// plus the counts of the earlier waves); pass 2 scatters each wave's range in
+// order, a lane's position being its wave's running base for the expert plus
+// its rank among the lower lanes with the same expert.  The running bases
+// are private to a wave, so the scatter needs no workgroup barrier.
 constexpr int kGroupWindow = 16;
 
 // Per lane: rank among lower lanes holding the same (valid) expert, and that
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
 
   for (int e = tid; e < kGroupWaves * n_experts; e += kGroupThreads) wbase[e] = 0;
   __syncthreads();
-  // pass 1: this wave's count per expert (its leaders add whole matches)
+  // pass 1: this wave's count per expert
   for (int w0 = r0; w0 < r1; w0 += kGroupWindow * 64) {
     int ev[kGroupWindow];
 #pragma unroll
@@ -95,12 +96,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
       ev[k] = a < r1 ? ids_g[a] : -1;
     }
 #pragma unroll
-    for (int k = 0; k < kGroupWindow; ++k) {
-      if (w0 + 64 * k >= r1) break;  // wave-uniform
-      int rank, cnt;
-      wave_match(ev[k], ev[k] >= 0, nbits, lt_mask, rank, cnt);
-      if (ev[k] >= 0 && rank == 0) my[ev[k]] += cnt;
-    }
+    for (int k = 0; k < kGroupWindow; ++k)
+      if (ev[k] >= 0) atomicAdd(&my[ev[k]], 1);
   }
   __syncthreads();
 
