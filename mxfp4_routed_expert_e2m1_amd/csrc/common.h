@@ -502,12 +502,16 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
 // are unconditional, the index clamped into the row, so they all go out at
 // once.
 template <int PER_LANE>
-__device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int top_k,
-                                 int* my_id, uint32_t* my_key) {
+__device__ inline void topk_load(const float* __restrict__ l, int n_experts, float (&lv)[PER_LANE]) {
   const int lane = lane_id();
-  float lv[PER_LANE];
 #pragma unroll
   for (int j = 0; j < PER_LANE; ++j) lv[j] = l[min(lane + 64 * j, n_experts - 1)];
+}
+// (the rounds, on logits topk_load brought in)
+template <int PER_LANE>
+__device__ inline void topk_pick_loaded(float (&lv)[PER_LANE], int n_experts, int top_k,
+                                        int* my_id, uint32_t* my_key) {
+  const int lane = lane_id();
   // (an empty asm reading every value keeps the compiler from moving a load
   // under the select below, where it would wait for each load in turn)
 #pragma unroll
@@ -538,6 +542,13 @@ __device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int
   }
   *my_id = id;
   *my_key = my_k;
+}
+template <int PER_LANE>
+__device__ inline void topk_pick(const float* __restrict__ l, int n_experts, int top_k,
+                                 int* my_id, uint32_t* my_key) {
+  float lv[PER_LANE];
+  topk_load<PER_LANE>(l, n_experts, lv);
+  topk_pick_loaded<PER_LANE>(lv, n_experts, top_k, my_id, my_key);
 }
 
 // The picks' weights (lane s < top_k: pick s): each pick's sigmoid in its

@@ -54,11 +54,12 @@ struct DownRowsArgs {
 // token t).
 // NC: 16-byte pieces of hidden codes each thread copies (a constant, so the
 // number of loads in flight is known when the copy waits).
-// ONE: a one-row step.  Its tiles are its valid slots (ids >= 0) in the
-// stable order by expert (by id, then by slot) -- the order the sorted list
-// and offsets of moe_route_group give -- each of one column, then the
-// shared expert's.  Every wave finds them from the ids alone: no round trip
-// for the offsets and no tile-map scan before its weights go out.
+// ONE: a one-row step.  Its tiles are the shared expert's (first: it needs
+// no route, so wave 0 issues its weights before the ids arrive), then its
+// valid slots (ids >= 0) in the stable order by expert (by id, then by
+// slot) -- the order the sorted list and offsets of moe_route_group give --
+// each of one column.  Every wave finds them from the ids alone: no round
+// trip for the offsets and no tile-map scan before its weights go out.
 template <int NC, bool ONE>
 __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p,
                                                                     int tiles_cap) {
@@ -109,34 +110,33 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     const int64_t off = tid < n_ps ? (int64_t)(tid / per_row_s) * p.ld_hs + (tid % per_row_s) * 4 : 0;
     cs = *(const f32x4*)(p.hs + off);
   }
-  __builtin_amdgcn_sched_barrier(0);  // every load of the round trip goes out first
-  const int idv = ra < n_assign ? idv_raw : -1;
-  const float wv = ra < n_assign ? wv_raw : 0.f;
-  // ONE: lane s's place among the valid slots in the stable order, their
-  // number, and the expert of this wave's tile (and of tile 0)
-  int rank1 = 0, nv1 = 0;
-  if constexpr (ONE) {
-    for (int s2 = 0; s2 < p.top_k; ++s2) {
-      const int o = __builtin_amdgcn_readlane(idv, s2);
-      rank1 += o >= 0 && (o < idv || (o == idv && s2 < lane)) ? 1 : 0;
-      nv1 += o >= 0 ? 1 : 0;
-    }
-  } else {
-    tm.count(p.n_experts, p.has_shared, p.rows);
+  // What the first weight loads need besides the route -- the blobs' base
+  // addresses and the head chunks' offsets (every head starts at chunk 0) --
+  // is in scalar registers before the ids arrive.
+  const uint32_t blob_bytes = (uint32_t)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256);
+  const uint32_t nib_row = (uint32_t)rg * (uint32_t)p.kc_total * 1024u;
+  const uint32_t scl_row = (uint32_t)p.nib_bytes + (uint32_t)rg * (uint32_t)p.sc_total * 256u;
+  const uint32_t a_lane = (uint32_t)lane * 16u, s_lane = (uint32_t)col * 16u;
+  const uint8_t* dn = p.dn;
+  const uint8_t* dn_shared = p.dn_shared;
+  int64_t dn_stride = p.dn_stride;
+  asm volatile("" : "+s"(dn), "+s"(dn_shared), "+s"(dn_stride));
+  uint32_t head_a[kDRAhead], head_s[kDRAhead];
+#pragma unroll
+  for (int kk = 0; kk < kDRAhead; ++kk) {
+    const int kc = min(kk, min(kDRGroup, p.kc_total) - 1);
+    head_a[kk] = nib_row + (uint32_t)chunk_slot(kc, p.kc_total) * 1024u;
+    head_s[kk] = scl_row + (uint32_t)(kc >> 2) * 256u + (uint32_t)(kc & 3) * 4u;
+    asm volatile("" : "+s"(head_a[kk]), "+s"(head_s[kk]));
   }
-
   // this wave's weight stream: row group rg of tile ti, K chunks kg..kg+15,
   // as raw buffer loads (one resource per tile, the chunk's offset in a
   // scalar register, the lane's in a vector register)
   u32x4 a[kDRGroup];
   uint32_t s[kDRGroup];
-  const uint32_t blob_bytes = (uint32_t)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256);
-  const uint32_t nib_row = (uint32_t)rg * (uint32_t)p.kc_total * 1024u;
-  const uint32_t scl_row = (uint32_t)p.nib_bytes + (uint32_t)rg * (uint32_t)p.sc_total * 256u;
-  const uint32_t a_lane = (uint32_t)lane * 16u, s_lane = (uint32_t)col * 16u;
   auto tile_rsrc = [&](const int4 te) {
     const int ex = uniform(te.x);
-    const uint8_t* blob = ex == p.n_experts ? p.dn_shared : p.dn + (int64_t)ex * p.dn_stride;
+    const uint8_t* blob = ex == p.n_experts ? dn_shared : dn + (int64_t)ex * dn_stride;
     return buf_rsrc(blob, blob_bytes);
   };
   // chunk kk of the group at kg (a group shorter than kDRGroup repeats its
@@ -147,42 +147,91 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     a[kk] = buf_load16(r, a_lane, nib_row + (uint32_t)chunk_slot(kc, p.kc_total) * 1024u);
     s[kk] = buf_load4(r, s_lane, scl_row + (uint32_t)(kc >> 2) * 256u + (uint32_t)(kc & 3) * 4u);
   };
-  auto issue_head = [&](const int4 te, int kg) {
+  auto issue_head = [&](const int4 te) {  // chunks 0 .. kDRAhead-1
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(te);
 #pragma unroll
-    for (int kk = 0; kk < kDRAhead; ++kk) issue_chunk(r, kg, kk);
+    for (int kk = 0; kk < kDRAhead; ++kk) {
+      a[kk] = buf_load16(r, a_lane, head_a[kk]);
+      s[kk] = buf_load4(r, s_lane, head_s[kk]);
+    }
   };
+  __builtin_amdgcn_sched_barrier(0);  // every load of the round trip goes out first
+  // the ids and weights, taken where each path first needs them (the empty
+  // asm keeps the compiler from hoisting the wait for them)
+  int idv = -1;
+  float wv = 0.f;
+  auto take_ids = [&]() {
+    int r = idv_raw;
+    float f = wv_raw;
+    asm volatile("" : "+v"(r), "+v"(f));
+    idv = ra < n_assign ? r : -1;
+    wv = ra < n_assign ? f : 0.f;
+  };
+  // ONE: lane s's place among the valid slots in the stable order, their
+  // number, and the expert of this wave's tile (and of tile 0)
+  int rank1 = 0, nv1 = 0;
+  auto ranks = [&]() {
+    // (a valid slot's key is its expert, then its slot (< 16): unique; a
+    // sentinel's sorts after every pick)
+    const int key = idv >= 0 ? (idv << 4) | lane : INT_MAX;
+    for (int s2 = 0; s2 < p.top_k; ++s2) rank1 += __builtin_amdgcn_readlane(key, s2) < key ? 1 : 0;
+    nv1 = (int)__popcll(__ballot(idv >= 0));
+  };
+  // ONE with a shared expert: its tile comes first, wave 0's, and needs no
+  // route, so wave 0 issues it before the ids arrive and ranks after
+  const bool early0 = ONE && p.has_shared && wave == 0;
+  if constexpr (ONE) {
+    if (!early0) {
+      take_ids();
+      ranks();
+    }
+  } else {
+    take_ids();
+    tm.count(p.n_experts, p.has_shared, p.rows);
+  }
+
   // Every wave issues: a wave without a tile repeats tile 0's addresses
   // (they merge with that tile's misses in L2); with no tile at all (no
   // shared expert and every slot a sentinel) routed expert 0's row group,
   // which always exists.  So the issue is unconditional.
   if constexpr (ONE) {
-    const int total = nv1 + p.has_shared;
-    const int want = wave < total ? wave : 0;
+    // ONE: tile 0 is the shared expert's (if any), then the valid slots by
+    // place: wave w's routed place is w - has_shared
+    const int sh = p.has_shared;
     int4 te0 = int4{0, 0, 0, 0};
-    if (want < nv1) {
-      const uint64_t m = __ballot(idv >= 0 && rank1 == want);
-      te0 = int4{__builtin_amdgcn_readlane(idv, __ffsll((unsigned long long)m) - 1), want, 1, 0};
-    } else if (p.has_shared) {
+    if (early0) {
       te0 = int4{p.n_experts, 0, 1, 0};
+    } else {
+      const int want = (wave < nv1 + sh ? wave : 0) - sh;
+      if (want >= 0 && want < nv1) {
+        const uint64_t m = __ballot(idv >= 0 && rank1 == want);
+        te0 = int4{__builtin_amdgcn_readlane(idv, __ffsll((unsigned long long)m) - 1), want, 1, 0};
+      } else if (sh) {
+        te0 = int4{p.n_experts, 0, 1, 0};
+      }
     }
-    issue_head(te0, 0);
+    issue_head(te0);
+    if (early0) {
+      __builtin_amdgcn_sched_barrier(0);
+      take_ids();
+      ranks();
+    }
   } else {
     const int total = tm.n_tiles();
     const Tile t0 = tm.lookup(p.n_experts, p.rows, wave < total ? wave : 0);
     const int4 te0 = t0.expert >= 0 ? int4{t0.expert, t0.start, t0.count, 0} : int4{0, 0, 0, 0};
-    issue_head(te0, 0);
+    issue_head(te0);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // the tile map, positions, ids, weights and hidden rows go to LDS while
   // the weights are in flight
   if (ONE && wave == 0) {
-    // tile r: the valid slot of place r; the combine's partial index of
-    // slot s (its tile's first column), -1 for a sentinel
-    if (idv >= 0) s_tiles[rank1] = int4{idv, rank1, 1, 0};
+    // tile has_shared + r: the valid slot of place r; tile 0 the shared
+    // expert's
+    if (idv >= 0) s_tiles[p.has_shared + rank1] = int4{idv, rank1, 1, 0};
     if (lane == 0) {
-      if (p.has_shared) s_tiles[nv1] = int4{p.n_experts, 0, 1, 0};
+      if (p.has_shared) s_tiles[0] = int4{p.n_experts, 0, 1, 0};
       s_ntiles = nv1 + p.has_shared;
       s_routed = nv1;
     }
@@ -249,7 +298,11 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};  // the runs so far
     f32x4 run = {0.f, 0.f, 0.f, 0.f};  // the current run of 4 chunks
     for (int kg = 0; kg < p.kc_total; kg += kDRGroup) {
-      if (kg > 0) issue_head(te, kg);  // the head of the first group is already in flight
+      if (kg > 0) {  // the head of the first group is already in flight
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(te);
+#pragma unroll
+        for (int kk = 0; kk < kDRAhead; ++kk) issue_chunk(r, kg, kk);
+      }
       const int n_in = min(kDRGroup, p.kc_total - kg);
       u32x4 b[2][4];
       f32x4 d[2];
@@ -285,7 +338,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     // lane l holds rows 4*(l/16) + i of column l % 16
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[(ti * 16 + col) * 16 + 4 * (lane >> 4) + i] = acc[i];
-    if (ti + kDRWaves < n_tiles) issue_head(s_tiles[ti + kDRWaves], 0);
+    if (ti + kDRWaves < n_tiles) issue_head(s_tiles[ti + kDRWaves]);
   }
   __syncthreads();
 
@@ -294,7 +347,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
     // (threads 0-15: row r = tid; each slot's partial index and weight come
     // from wave 0's lanes, all of the slots' partials are read at once)
     if (tid < 16) {
-      const int pl = idv >= 0 ? rank1 * 256 : -1;
+      const int pl = idv >= 0 ? (p.has_shared + rank1) * 256 : -1;  // (tile's partial)
       float pv[MOE_MAX_TOP_K];
 #pragma unroll
       for (int s2 = 0; s2 < MOE_MAX_TOP_K; ++s2) {
@@ -308,7 +361,7 @@ __global__ __launch_bounds__(kDRThreads, 2) void down_rows_kernel(DownRowsArgs p
           v = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), s2)),
                    pv[s2], v);  // as the combine kernel
       }
-      if (p.has_shared) v = v + part[nv1 * 256 + tid];
+      if (p.has_shared) v = v + part[tid];  // tile 0
       p.y[16 * rg + tid] = v;
     }
     return;

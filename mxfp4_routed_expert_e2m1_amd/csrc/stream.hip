@@ -66,10 +66,109 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
   const int n_tok_assign = p.rows * p.top_k;
   const int kc0 = wave * KPW;
 
+  // per-item values, all wave-uniform
+  struct Item {
+    int expert, start, count, rb;
+    bool shared;
+    __amdgpu_buffer_rsrc_t w;  // the expert's blob
+    uint32_t a_soff, s_soff;   // row group pr0 in its nibble and scale regions
+  };
+  const uint32_t blob_bytes =
+      (uint32_t)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256);
+  // tile te's row block rb
+  auto item_of = [&](const int4 te, int rb) {
+    Item x;
+    x.rb = rb;
+    const uint8_t* blob = p.w;
+    int64_t eoff = 0;
+    if constexpr (PASS == STREAM_MATVEC) {
+      x.expert = 0;
+      x.start = 0;
+      x.count = p.rows;
+      x.shared = false;
+    } else {
+      x.expert = uniform(te.x);
+      x.start = uniform(te.y);
+      x.count = uniform(te.z);
+      x.shared = x.expert == p.n_experts;
+      if (x.shared) blob = p.w_shared;
+      else eoff = (int64_t)x.expert * p.w_stride;
+    }
+    x.w = buf_rsrc(blob + uniform(eoff), blob_bytes);
+    const int pr0 = x.rb * RGW;
+    x.a_soff = (uint32_t)pr0 * (uint32_t)p.kc_total * 1024u;
+    x.s_soff = (uint32_t)p.nib_bytes + (uint32_t)pr0 * (uint32_t)p.sc_total * 256u;
+    return x;
+  };
+  auto item_at = [&](int i) {
+    return item_of(PASS == STREAM_MATVEC ? int4{0, 0, 0, 0} : s_tiles[i / n_rb], i % n_rb);
+  };
+  // this lane's B row; columns past the tile point one row past the operand,
+  // where the buffer range check returns zeros without reading memory (their
+  // outputs are never stored)
+  auto brow_of = [&](const Item& x) -> int {
+    if (col >= x.count) return PASS == STREAM_DOWN ? n_tok_assign + (p.has_shared ? p.rows : 0) : p.rows;
+    const int ccol = col;
+    if (PASS == STREAM_MATVEC) return ccol;
+    if (PASS == STREAM_GATEUP) return x.shared ? x.start + ccol : s_sorted[x.start + ccol] / p.top_k;
+    return x.shared ? n_tok_assign + x.start + ccol : x.start + ccol;
+  };
+
+  // B operand rows: tokens (MATVEC, GATEUP) or hidden rows (DOWN)
+  const int b_rows = PASS == STREAM_DOWN ? n_tok_assign + (p.has_shared ? p.rows : 0) : p.rows;
+  const __amdgpu_buffer_rsrc_t rb_b = buf_rsrc(p.b, (uint32_t)(b_rows * p.ld_b * kBBytes));
+  const __amdgpu_buffer_rsrc_t rb_d = buf_rsrc(p.bs, (uint32_t)(b_rows * p.ld_bs * 4));
+  // lane offsets that do not depend on the item
+  // chunk kc0 + kk of a row group sits in slot W * kk + wave (KC = 4W, the
+  // interleaved chunk order of the packed layout): at each kk the waves read
+  // adjacent tiles
+  const uint32_t a_lane = (uint32_t)(wave * 1024 + lane * 16);
+  const uint32_t a_gstride = (uint32_t)p.kc_total * 1024u;
+  const uint32_t s_lane = (uint32_t)(((kc0 >> 2) * 16 + col) * 16);
+  const uint32_t s_gstride = (uint32_t)p.sc_total * 256u;
+  const uint32_t b_lane = (uint32_t)((kc0 * kChunkK + 8 * (lane >> 4)) * kBBytes);
+
+  u32x4 a[KPW][RGW];
+  u32x4 sv[RGW], sv_n[RGW];
+  BV b[KPW][4];
+  f32x4 d[KPW];
+  // the 16 scale bytes of row `col` for this wave's 4 chunks (kc0 % 4 == 0)
+  auto issue_s = [&](const Item& x, u32x4 (&sd)[RGW]) {
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) sd[g] = buf_load16(x.w, s_lane, x.s_soff + g * s_gstride);
+  };
+  auto issue_w = [&](const Item& x, int kk) {  // the weights of chunk kk
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) a[kk][g] = buf_load16(x.w, a_lane + kk * W * 1024, x.a_soff + g * a_gstride);
+  };
+  auto issue_b = [&](int brow, int kk) {  // the B operand of chunk kk
+    if constexpr (F1) {
+      // the row from LDS, in every column: columns past the tile's one are
+      // computed alike and never stored (and their amax is their own)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[kk][j] = *(const u32x2*)(s_q8 + (kc0 + kk) * kChunkK + j * kBlock + 8 * (lane >> 4));
+      d[kk] = *(const f32x4*)(s_qs + (kc0 + kk) * 4);
+    } else {
+      const uint32_t bo = (uint32_t)(brow * p.ld_b * kBBytes) + b_lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t o = bo + (kk * kChunkK + j * kBlock) * kBBytes;
+        if constexpr (PASS == STREAM_DOWN) b[kk][j] = buf_load16(rb_b, o, 0);
+        else b[kk][j] = buf_load8(rb_b, o, 0);
+      }
+      d[kk] = __builtin_bit_cast(f32x4, buf_load16(rb_d, (uint32_t)(brow * p.ld_bs * 4 + (kc0 + kk) * 16), 0));
+    }
+  };
+  auto issue = [&](const Item& x, int brow, int kk) {
+    issue_w(x, kk);
+    issue_b(brow, kk);
+  };
   // The call's tiles (one round trip, wave 0) and sorted list go to LDS.
   int n_items = n_rb;
   int my_id = 0;        // F1, wave 0: lane s < top_k holds pick s
   uint32_t my_key = 0;  // and its logit key
+  bool early = false;   // F1: this workgroup's first item went out before the route
   if constexpr (F1) {
     // One row, straight from the layer input.  Wave 0 routes it (top-k of
     // the logits) while the other waves quantise it into LDS (8 elements
@@ -77,9 +176,13 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
     // pieces by wave 1), all in one round trip, so no earlier launch has to
     // finish first.  With one row every picked expert is a tile of one
     // column and its sorted position is its rank by expert id (the picks
-    // are distinct); the shared expert's tile follows.  Workgroup 0 also
-    // writes what the quantiser and the router would: codes, scales, ids,
-    // weights, counts, offsets, sorted (after its first loads go out).
+    // are distinct).  The shared expert's tile comes first: a workgroup
+    // whose first item is one of its row blocks (blockIdx.x < n_rb) needs no
+    // route for it, so that item's weights and scales go out right after the
+    // row's and the logits' own loads, while the route and the quantiser
+    // run.  Workgroup 0 also writes what the quantiser and the router would:
+    // codes, scales, ids, weights, counts, offsets, sorted (after its first
+    // loads go out).
     auto quant_piece = [&](int pc, const float4 x0, const float4 x1) {
       const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       uint32_t w0, w1;
@@ -91,37 +194,58 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
         if ((pc & 3) == 0) in.qs[pc >> 2] = dq;
       }
     };
+    early = p.has_shared && (int)blockIdx.x < n_rb;
+    const float4* xv = (const float4*)in.x;
+    float lv[TOPK_PL];
+    float4 a0, a1, b0, b1;
     if (wave == 0) {
-      topk_pick<TOPK_PL>(in.logits, p.n_experts, p.top_k, &my_id, &my_key);
-      // (an id < 0 -- the router found no pick, e.g. NaN logits, outside the
-      // contract -- is a sentinel as in moe_route_group: in no tile)
-      const bool ok = lane < p.top_k && my_id >= 0;
-      int rank = 0, n_valid = 0;
-      for (int s2 = 0; s2 < p.top_k; ++s2) {
-        const int o = __builtin_amdgcn_readlane(my_id, s2);
-        rank += o >= 0 && o < my_id ? 1 : 0;
-        n_valid += o >= 0 ? 1 : 0;
-      }
-      if (lane < p.top_k) s_rid[lane] = my_id;
-      if (ok) {
-        s_sorted[rank] = lane;
-        s_tiles[rank] = int4{my_id, rank, 1, 0};
-      }
-      if (lane == 0) {
-        if (p.has_shared) s_tiles[n_valid] = int4{p.n_experts, 0, 1, 0};
-        s_ntiles = n_valid + p.has_shared;
-      }
+      topk_load<TOPK_PL>(in.logits, p.n_experts, lv);
     } else {
-      const float4* xv = (const float4*)in.x;
-      const float4 a0 = xv[2 * tid], a1 = xv[2 * tid + 1];
-      float4 b0, b1;
+      a0 = xv[2 * tid];
+      a1 = xv[2 * tid + 1];
       if (wave == 1) {
         b0 = xv[2 * lane];
         b1 = xv[2 * lane + 1];
       }
+    }
+    auto route_or_quantise = [&]() {
+    if (wave == 0) {
+      topk_pick_loaded<TOPK_PL>(lv, p.n_experts, p.top_k, &my_id, &my_key);
+      // (an id < 0 -- the router found no pick, e.g. NaN logits, outside the
+      // contract -- is a sentinel as in moe_route_group: in no tile)
+      const bool ok = lane < p.top_k && my_id >= 0;
+      const int key = ok ? my_id : INT_MAX;  // (the picks are distinct)
+      int rank = 0;
+      for (int s2 = 0; s2 < p.top_k; ++s2) rank += __builtin_amdgcn_readlane(key, s2) < key ? 1 : 0;
+      const int n_valid = (int)__popcll(__ballot(ok));
+      if (lane < p.top_k) s_rid[lane] = my_id;
+      const int sh = p.has_shared;
+      if (ok) {
+        s_sorted[rank] = lane;
+        s_tiles[sh + rank] = int4{my_id, rank, 1, 0};
+      }
+      if (lane == 0) {
+        if (sh) s_tiles[0] = int4{p.n_experts, 0, 1, 0};
+        s_ntiles = n_valid + sh;
+      }
+    } else {
       quant_piece(tid, a0, a1);
       if (wave == 1) quant_piece(lane, b0, b1);
       if (tid < 96) s_amax[(tid - 64) >> 4][tid & 15] = 0u;
+    }
+    };
+    // (two copies, so each keeps its own load-counter waits: with the early
+    // loads in flight they wait only for the row's and the logits' loads)
+    if (early) {
+      const Item x0 = item_of(int4{p.n_experts, 0, 1, 0}, (int)blockIdx.x);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_s(x0, sv);
+#pragma unroll
+      for (int kk = 0; kk < kSAhead; ++kk) issue_w(x0, kk);
+      __builtin_amdgcn_sched_barrier(0);
+      route_or_quantise();
+    } else {
+      route_or_quantise();
     }
     lds_barrier();
     n_items = uniform(s_ntiles) * n_rb;
@@ -187,95 +311,6 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
     return;
   }
 
-  // per-item values, all wave-uniform
-  struct Item {
-    int expert, start, count, rb;
-    bool shared;
-    __amdgpu_buffer_rsrc_t w;  // the expert's blob
-    uint32_t a_soff, s_soff;   // row group pr0 in its nibble and scale regions
-  };
-  const uint32_t blob_bytes =
-      (uint32_t)(p.nib_bytes + (int64_t)p.rg_total * p.sc_total * 256);
-  auto item_at = [&](int i) {
-    Item x;
-    x.rb = i % n_rb;
-    const uint8_t* blob = p.w;
-    int64_t eoff = 0;
-    if constexpr (PASS == STREAM_MATVEC) {
-      x.expert = 0;
-      x.start = 0;
-      x.count = p.rows;
-      x.shared = false;
-    } else {
-      const int4 te = s_tiles[i / n_rb];
-      x.expert = uniform(te.x);
-      x.start = uniform(te.y);
-      x.count = uniform(te.z);
-      x.shared = x.expert == p.n_experts;
-      if (x.shared) blob = p.w_shared;
-      else eoff = (int64_t)x.expert * p.w_stride;
-    }
-    x.w = buf_rsrc(blob + uniform(eoff), blob_bytes);
-    const int pr0 = x.rb * RGW;
-    x.a_soff = (uint32_t)pr0 * (uint32_t)p.kc_total * 1024u;
-    x.s_soff = (uint32_t)p.nib_bytes + (uint32_t)pr0 * (uint32_t)p.sc_total * 256u;
-    return x;
-  };
-  // this lane's B row; columns past the tile point one row past the operand,
-  // where the buffer range check returns zeros without reading memory (their
-  // outputs are never stored)
-  auto brow_of = [&](const Item& x) -> int {
-    if (col >= x.count) return PASS == STREAM_DOWN ? n_tok_assign + (p.has_shared ? p.rows : 0) : p.rows;
-    const int ccol = col;
-    if (PASS == STREAM_MATVEC) return ccol;
-    if (PASS == STREAM_GATEUP) return x.shared ? x.start + ccol : s_sorted[x.start + ccol] / p.top_k;
-    return x.shared ? n_tok_assign + x.start + ccol : x.start + ccol;
-  };
-
-  // B operand rows: tokens (MATVEC, GATEUP) or hidden rows (DOWN)
-  const int b_rows = PASS == STREAM_DOWN ? n_tok_assign + (p.has_shared ? p.rows : 0) : p.rows;
-  const __amdgpu_buffer_rsrc_t rb_b = buf_rsrc(p.b, (uint32_t)(b_rows * p.ld_b * kBBytes));
-  const __amdgpu_buffer_rsrc_t rb_d = buf_rsrc(p.bs, (uint32_t)(b_rows * p.ld_bs * 4));
-  // lane offsets that do not depend on the item
-  // chunk kc0 + kk of a row group sits in slot W * kk + wave (KC = 4W, the
-  // interleaved chunk order of the packed layout): at each kk the waves read
-  // adjacent tiles
-  const uint32_t a_lane = (uint32_t)(wave * 1024 + lane * 16);
-  const uint32_t a_gstride = (uint32_t)p.kc_total * 1024u;
-  const uint32_t s_lane = (uint32_t)(((kc0 >> 2) * 16 + col) * 16);
-  const uint32_t s_gstride = (uint32_t)p.sc_total * 256u;
-  const uint32_t b_lane = (uint32_t)((kc0 * kChunkK + 8 * (lane >> 4)) * kBBytes);
-
-  u32x4 a[KPW][RGW];
-  u32x4 sv[RGW], sv_n[RGW];
-  BV b[KPW][4];
-  f32x4 d[KPW];
-  // the 16 scale bytes of row `col` for this wave's 4 chunks (kc0 % 4 == 0)
-  auto issue_s = [&](const Item& x, u32x4 (&sd)[RGW]) {
-#pragma unroll
-    for (int g = 0; g < RGW; ++g) sd[g] = buf_load16(x.w, s_lane, x.s_soff + g * s_gstride);
-  };
-  auto issue = [&](const Item& x, int brow, int kk) {
-#pragma unroll
-    for (int g = 0; g < RGW; ++g) a[kk][g] = buf_load16(x.w, a_lane + kk * W * 1024, x.a_soff + g * a_gstride);
-    if constexpr (F1) {
-      // the row from LDS, in every column: columns past the tile's one are
-      // computed alike and never stored (and their amax is their own)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[kk][j] = *(const u32x2*)(s_q8 + (kc0 + kk) * kChunkK + j * kBlock + 8 * (lane >> 4));
-      d[kk] = *(const f32x4*)(s_qs + (kc0 + kk) * 4);
-    } else {
-      const uint32_t bo = (uint32_t)(brow * p.ld_b * kBBytes) + b_lane;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t o = bo + (kk * kChunkK + j * kBlock) * kBBytes;
-        if constexpr (PASS == STREAM_DOWN) b[kk][j] = buf_load16(rb_b, o, 0);
-        else b[kk][j] = buf_load8(rb_b, o, 0);
-      }
-      d[kk] = __builtin_bit_cast(f32x4, buf_load16(rb_d, (uint32_t)(brow * p.ld_bs * 4 + (kc0 + kk) * 16), 0));
-    }
-  };
   auto compute = [&](int kk, const u32x4 (&sc4)[RGW], f32x4 (&acc)[RGW]) {
     u32x4 af[RGW];
 #pragma unroll
@@ -355,9 +390,14 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
 
   Item cur = item_at(it);
   int br_cur = brow_of(cur);
-  issue_s(cur, sv);
+  if (F1 && early) {  // (its weights and scales are in flight)
 #pragma unroll
-  for (int kk = 0; kk < kSAhead; ++kk) issue(cur, br_cur, kk);
+    for (int kk = 0; kk < kSAhead; ++kk) issue_b(br_cur, kk);
+  } else {
+    issue_s(cur, sv);
+#pragma unroll
+    for (int kk = 0; kk < kSAhead; ++kk) issue(cur, br_cur, kk);
+  }
   publish();  // (its first loads are in flight)
 
   // One item: (NEXT) the next item's scales into the other scale registers,

@@ -407,6 +407,28 @@ def test_decode_step_one_row_all_ones_nan_logits():
     assert sorted(got[:3].tolist()) == sorted(ex.tolist()) and np.all(got[3:] == -1)
 
 
+# The one-row step's router selects the picks (the top_k-th key, bit by bit)
+# from 64 experts per lane slot: full and part-filled slots, top_k 6..16.
+ROUTER_TIES = [
+    synth.Layer(n_experts=256, top_k=16, d_model=2048, d_ff=512, has_shared=True),
+    synth.Layer(n_experts=256, top_k=8, d_model=1024, d_ff=512, has_shared=False),
+    synth.Layer(n_experts=200, top_k=6, d_model=4096, d_ff=256, has_shared=True),
+    synth.Layer(n_experts=512, top_k=9, d_model=4096, d_ff=256, has_shared=True),
+]
+
+
+@pytest.mark.parametrize("shape", range(len(ROUTER_TIES)))
+def test_decode_step_one_row_tied_logits(shape):
+    """Logits rounded to integers tie within and across lane slots, also at
+    the cut: the picks among equal logits are the lowest experts, as the
+    oracle's, in the oracle's order."""
+    L = ROUTER_TIES[shape]
+    seed = 71 + shape
+    x = synth.activations(seed, 1, 1, L.d_model)
+    lg = np.round(synth.router_logits(seed, 1, 1, L.n_experts)) + np.float32(0.0)  # (no -0)
+    run_case(L, seed, x, lg.astype(np.float32), entry="step")
+
+
 def test_decode_exact_rows_across_batch_sizes():
     # Exact rows ([strix] "The exact-rows contract"): a row's output does not
     # depend on the rows sharing its step.  The same rows decoded all 16
