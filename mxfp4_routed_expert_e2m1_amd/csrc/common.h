@@ -494,12 +494,13 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
 
 // One wave: the top_k picks of one row of logits; lane s < top_k receives
 // pick s (its expert and its key).  Expert e sits in lane e % 64, slot
-// e / 64, as the composite (key << 32) | ~e: a larger composite is a larger
-// key, then a lower index.  Each round takes the wave max of the lanes'
-// largest composites; the pick's key becomes 0.  A round that finds no key
-// left (only logits whose key is 0, the all-ones NaN, remain: outside the
-// contract) yields the sentinel -1, never an expert past the row.  The loads
-// are unconditional, the index clamped into the row, so they all go out at
+// e / 64.  Each round takes the wave max of the lanes' largest keys, then
+// the lowest expert holding it (a ballot per slot: the first slot with a
+// match, its lowest lane), whose key becomes 0: the larger key first, the
+// lower index among equal keys.  A round that finds no key left (only
+// logits whose key is 0, the all-ones NaN, remain: outside the contract)
+// yields the sentinel -1, never an expert past the row.  The loads are
+// unconditional, the index clamped into the row, so they all go out at
 // once.
 template <int PER_LANE>
 __device__ inline void topk_load(const float* __restrict__ l, int n_experts, float (&lv)[PER_LANE]) {
@@ -516,28 +517,29 @@ __device__ inline void topk_pick_loaded(float (&lv)[PER_LANE], int n_experts, in
   // under the select below, where it would wait for each load in turn)
 #pragma unroll
   for (int j = 0; j < PER_LANE; ++j) asm volatile("" : "+v"(lv[j]));
-  uint64_t c[PER_LANE];
+  uint32_t k[PER_LANE];
 #pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) {
-    const int e = lane + 64 * j;
-    const uint32_t k = e < n_experts ? logit_key(lv[j]) : 0u;
-    c[j] = ((uint64_t)k << 32) | (uint32_t)~e;
-  }
+  for (int j = 0; j < PER_LANE; ++j) k[j] = lane + 64 * j < n_experts ? logit_key(lv[j]) : 0u;
   uint32_t my_k = 0;
   int id = 0;
   for (int s = 0; s < top_k; ++s) {
-    uint64_t lc = c[0];
+    uint32_t lm = k[0];
 #pragma unroll
-    for (int j = 1; j < PER_LANE; ++j) lc = c[j] > lc ? c[j] : lc;
-    const uint64_t bc = wave_max_u64(lc);
-    const int be = (int)~(uint32_t)bc;
-    const uint32_t bk = (uint32_t)(bc >> 32);
+    for (int j = 1; j < PER_LANE; ++j) lm = max(lm, k[j]);
+    const uint32_t bk = wave_max_u32(lm);
+    int be = -1;
+#pragma unroll
+    for (int j = PER_LANE - 1; j >= 0; --j) {
+      const uint64_t m = __ballot(k[j] == bk);
+      if (m != 0ull) be = 64 * j + (__ffsll((unsigned long long)m) - 1);
+    }
+    if (bk == 0u) be = -1;
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j)
-      if (lane == (be & 63) && j == (be >> 6)) c[j] &= 0xFFFFFFFFull;
+      if (lane + 64 * j == be) k[j] = 0u;
     if (lane == s) {
       my_k = bk;
-      id = bk != 0u ? be : -1;
+      id = be;
     }
   }
   *my_id = id;
