@@ -27,7 +27,7 @@ namespace moe {
 constexpr int kDRWaves = 8;
 constexpr int kDRThreads = kDRWaves * 64;
 constexpr int kDRGroup = 16;  // K chunks of a wave's weight registers (16 KiB)
-constexpr int kDRAhead = 6;   // chunks a wave keeps in flight ahead of its math
+constexpr int kDRAhead = kDownRowsHead;  // chunks a wave keeps in flight ahead of its math
 
 struct DownRowsArgs {
   const uint8_t* dn;  // routed expert 0 blob

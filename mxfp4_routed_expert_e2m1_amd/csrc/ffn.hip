@@ -555,7 +555,17 @@ static int step_launch(const moe_layer_t* L, int stages, const float* x, int64_t
   if (rows == 1 && stream_supported(g.kc_total, g.rg_total)) {
     // one launch quantises, routes and runs gate/up; then the down stage
     if (stages & MOE_STAGE_GATE_UP) {
-      const StepIn in{x, logits, q, qs, ids, w, counts, offsets, sorted};
+      StepIn in{x, logits, q, qs, ids, w, counts, offsets, sorted};
+      if ((stages & MOE_STAGE_DOWN) && down_rows_supported(L, rows)) {
+        const PackedDims pd(L->d_model, L->d_ff);
+        in.dn = (const uint8_t*)L->down;
+        in.dn_stride = L->down_stride;
+        in.dn_shared = (const uint8_t*)L->shared_down;
+        in.dn_nib_bytes = pd.nib_bytes;
+        in.dn_kc = (int)pd.kc;
+        in.dn_sc = (int)pd.sc;
+        in.dn_rg = (int)pd.rg;
+      }
       launch_stream_step1(g, in, s);
     }
     if (!(stages & MOE_STAGE_DOWN)) return launch_status();

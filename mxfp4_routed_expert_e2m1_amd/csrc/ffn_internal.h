@@ -86,6 +86,15 @@ struct StepIn {
   int32_t* counts;      // out [n_experts]
   int32_t* offsets;     // out [n_experts + 1]
   int32_t* sorted;      // out [top_k]
+  // The down matrix the one-row down-by-rows launch reads next (dn null:
+  // none).  The workgroups holding one item fewer read its head chunks (the
+  // first kDownRowsHead chunks of every row group of every tile) toward the
+  // caches after their item.
+  const uint8_t* dn;
+  int64_t dn_stride;
+  const uint8_t* dn_shared;
+  int64_t dn_nib_bytes;
+  int dn_kc, dn_sc, dn_rg;
 };
 // needs stream_supported(kc_total, rg_total) for the gate/up matrix
 void launch_stream_step1(const ProjArgs& a, const StepIn& in, hipStream_t s);
@@ -99,6 +108,7 @@ void launch_combine(const float* P, const int32_t* ids, const float* w, int rows
 // of LDS; a decode step has at most min(E, 256) + 16 + 1 <= kMaxDecodeTiles
 // tiles).
 constexpr int kDownRowsMaxLds = 150 * 1024;
+constexpr int kDownRowsHead = 6;  // chunks a wave issues before its first math
 constexpr int kMaxDecodeTiles = 288;
 bool down_rows_supported(const moe_layer_t* L, int rows);
 int down_rows_run(const moe_layer_t* L, int rows, const int32_t* ids, const float* w,

@@ -40,6 +40,12 @@ constexpr int kSKPW = 4;  // K chunks of a wave per item
 #define STREAM_AHEAD 2
 #endif
 constexpr int kSAhead = STREAM_AHEAD;
+// Chunks per row group of the down matrix that the one-row step's early
+// finishers read ahead for the down launch.
+#ifndef DOWN_PREFETCH_CHUNKS
+#define DOWN_PREFETCH_CHUNKS kDownRowsHead
+#endif
+constexpr int kDownPrefetch = DOWN_PREFETCH_CHUNKS;
 static_assert(kSAhead >= 1 && kSAhead <= kSKPW, "prefetch distance");
 
 // F1 (gate/up only): a one-row step straight from the layer input; see the
@@ -459,6 +465,54 @@ __device__ inline void stream_body(const ProjArgs& p, const StepIn& in) {
   }
   if (in_sv_n) step(std::false_type{}, cur, sv_n, sv);
   else step(std::false_type{}, cur, sv, sv_n);
+
+  if constexpr (F1) {
+    // With grid < n_items < 2 grid, workgroups from n_items - grid on hold
+    // one item fewer and finish early.  They read the down launch's head
+    // chunks toward the caches: reader r takes row groups r, r + R, ... (R
+    // readers; at most 4 each), wave w tile w, the first kDownPrefetch
+    // chunks and their scale bytes, two row groups at a time.  With R and
+    // n_items - grid multiples of 8, a row group is read on the XCD of the
+    // down workgroup that owns it (workgroup i runs on XCD i % 8).  The
+    // values are only waited for.
+    const int grid = (int)gridDim.x, first1 = n_items - grid, R = grid - first1;
+    const int n_tiles = uniform(s_ntiles);
+    if (in.dn != nullptr && first1 > 0 && R > 0 && (int)blockIdx.x >= first1 &&
+        in.dn_rg <= 4 * R && wave < n_tiles) {
+      const int ex = uniform(s_tiles[wave].x);
+      const uint8_t* blob = ex == p.n_experts ? in.dn_shared : in.dn + (int64_t)ex * in.dn_stride;
+      const __amdgpu_buffer_rsrc_t r =
+          buf_rsrc(blob, (uint32_t)(in.dn_nib_bytes + (int64_t)in.dn_rg * in.dn_sc * 256));
+      const int rd = (int)blockIdx.x - first1;
+#pragma unroll
+      for (int i0 = 0; i0 < 4; i0 += 2) {  // two row groups at a time
+        u32x4 v[2][kDownPrefetch];
+        constexpr int NS = (kDownPrefetch + 3) / 4;  // scale rows (4 chunks each)
+        uint32_t sv2[2][NS];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int rg = min(rd + (i0 + i) * R, in.dn_rg - 1);  // (a repeat past the end)
+#pragma unroll
+          for (int kk = 0; kk < kDownPrefetch; ++kk) {
+            const int kc = min(kk, in.dn_kc - 1);
+            v[i][kk] = buf_load16(r, (uint32_t)lane * 16u,
+                                  (uint32_t)(rg * in.dn_kc + chunk_slot(kc, in.dn_kc)) * 1024u);
+          }
+#pragma unroll
+          for (int j = 0; j < NS; ++j)
+            sv2[i][j] = buf_load4(r, (uint32_t)lane * 4u,
+                                  (uint32_t)(in.dn_nib_bytes + ((int64_t)rg * in.dn_sc + min(j, in.dn_sc - 1)) * 256));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+          for (int kk = 0; kk < kDownPrefetch; ++kk) asm volatile("" ::"v"(v[i][kk]));
+#pragma unroll
+          for (int j = 0; j < NS; ++j) asm volatile("" ::"v"(sv2[i][j]));
+        }
+      }
+    }
+  }
 }
 
 template <int PASS, int W>
