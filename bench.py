@@ -58,14 +58,14 @@ GEMM_SIMDS = 1024
 # (hash below, over the device code in csrc/): after any change to it the
 # benchmark reports traffic as null.
 TRAFFIC_DOC = "profiles/hbm_traffic_counters.md (moe_counters under rocprofv3 --pmc, offline)"
-TRAFFIC_SRC = "11680c44e0644344"
+TRAFFIC_SRC = "5fb566e52a374d56"
 TRAFFIC = {  # (workload, rows[, variant]): (read bytes, written bytes)
-    ("decode", 1): (2 * 30840.2 * 1024, 48.6 * 1024),
-    ("decode-batch", 16): (2 * 349811.5 * 1024, 676.2 * 1024),
-    ("decode-batch", 16, "hot"): (2 * 171099.0 * 1024, 672.6 * 1024),
-    ("prefill", 4096): (2 * 1277571.8 * 1024, 93847.8 * 1024),
-    ("prefill", 512): (2 * 1167151.3 * 1024, 12222.8 * 1024),
-    ("matvec", 5): (2 * 15409.4 * 1024, 280.0 * 1024),
+    ("decode", 1): (2 * 36676.4 * 1024, 48.6 * 1024),
+    ("decode-batch", 16): (2 * 349812.3 * 1024, 675.5 * 1024),
+    ("decode-batch", 16, "hot"): (2 * 171103.4 * 1024, 672.7 * 1024),
+    ("prefill", 4096): (2 * 1277591.8 * 1024, 93724.5 * 1024),
+    ("prefill", 512): (2 * 1167079.6 * 1024, 12216.2 * 1024),
+    ("matvec", 5): (2 * 15414.7 * 1024, 280.0 * 1024),
 }
 
 
